@@ -1,0 +1,214 @@
+"""Python binding of the W4A8 block-32 linear library (libw4a8.so, gfx950).
+
+Argument marshalling only: every step of the computation runs in the HIP
+kernels behind the C ABI declared in include/w4a8.h.  PyTorch provides device
+memory and the current stream; there is no CPU fallback, and every function
+raises if the library is not built or a call fails.
+
+Stage-aware layout of the layer (ML Drift explainer on tech.dede.sh, section
+"Stage-aware optimization for large language models"): `linear` runs the
+decode GEMV (activations quantised inside the kernel) for few token rows and
+the int8-MFMA prefill GEMM for many.
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+import re
+
+import torch
+
+__all__ = [
+    "PATH_AUTO", "PATH_GEMV", "PATH_GEMM", "W4A8Error", "library_path", "load_library",
+    "declared_functions", "init", "pack_weights", "linear", "linear_argmax",
+    "quantize_act", "block_sums", "gemv_max_m",
+]
+
+PATH_AUTO, PATH_GEMV, PATH_GEMM = 0, 1, 2
+W4A8_OK, W4A8_EINVAL, W4A8_EUNSUPPORTED, W4A8_EHIP, W4A8_ENOINIT = 0, -1, -2, -3, -4
+
+_HERE = os.path.dirname(os.path.abspath(__file__))
+_HEADER = os.path.join(os.path.dirname(_HERE), "include", "w4a8.h")
+_lib = None
+
+
+class W4A8Error(RuntimeError):
+    def __init__(self, fn: str, code: int, message: str):
+        super().__init__(f"{fn} returned {code}: {message}")
+        self.code = code
+
+
+def library_path() -> str:
+    return os.path.join(_HERE, "libw4a8.so")
+
+
+def declared_functions() -> list[str]:
+    """Names of the entry points declared in include/w4a8.h."""
+    with open(_HEADER) as f:
+        text = f.read()
+    return re.findall(r"W4A8_API\s+[\w\s\*]+?\b(w4a8_\w+)\s*\(", text)
+
+
+def load_library() -> ctypes.CDLL:
+    global _lib
+    if _lib is not None:
+        return _lib
+    path = library_path()
+    if not os.path.exists(path):
+        raise ImportError(f"{path} is not built; run `python -m bit_block_quantized_w4a8_amd.build`")
+    lib = ctypes.CDLL(path)
+    p, i64, i32 = ctypes.c_void_p, ctypes.c_int64, ctypes.c_int
+    sig = {
+        "w4a8_init": ([i32], i32),
+        "w4a8_pack_weights": ([p, p, i64, i64, p, p, p], i32),
+        "w4a8_linear": ([p, p, p, i64, i64, i64, p, p], i32),
+        "w4a8_linear_path": ([p, p, p, i64, i64, i64, p, i32, p], i32),
+        "w4a8_linear_argmax": ([p, p, p, i64, i64, i64, p, p, p], i32),
+        "w4a8_quantize_act": ([p, i64, i64, p, p, p], i32),
+        "w4a8_block_sums": ([p, p, i64, i64, i64, p, i32, p], i32),
+        "w4a8_gemv_max_m": ([], i32),
+        "w4a8_last_error": ([], ctypes.c_char_p),
+    }
+    for name, (args, res) in sig.items():
+        fn = getattr(lib, name)
+        fn.argtypes = args
+        fn.restype = res
+    _lib = lib
+    return lib
+
+
+def _check(fn: str, code: int):
+    if code != W4A8_OK:
+        msg = load_library().w4a8_last_error().decode(errors="replace")
+        raise W4A8Error(fn, code, msg)
+
+
+def _stream(t: torch.Tensor) -> int:
+    return torch.cuda.current_stream(t.device).cuda_stream
+
+
+def _need(t: torch.Tensor, name: str, dtype: torch.dtype, ndim: int):
+    if not isinstance(t, torch.Tensor) or not t.is_cuda:
+        raise TypeError(f"{name} must be a CUDA tensor")
+    if t.dtype != dtype:
+        raise TypeError(f"{name} must be {dtype}, got {t.dtype}")
+    if t.dim() != ndim or not t.is_contiguous():
+        raise ValueError(f"{name} must be a contiguous {ndim}-d tensor, got shape {tuple(t.shape)}")
+
+
+_initialised: set[int] = set()
+
+
+def init(device: int | None = None) -> None:
+    """Select the device and let the library allocate its scratch (idempotent)."""
+    dev = torch.cuda.current_device() if device is None else int(device)
+    if dev in _initialised:
+        return
+    _check("w4a8_init", load_library().w4a8_init(dev))
+    torch.cuda.set_device(dev)
+    _initialised.add(dev)
+
+
+def _ready(t: torch.Tensor):
+    init(t.device.index if t.device.index is not None else torch.cuda.current_device())
+
+
+def pack_weights(q: torch.Tensor, s: torch.Tensor):
+    """int8 weights [N][K] in [-8, 7] + fp16 scales [N][K/32] -> (packed uint8 [K/32][N][16], fp16 [K/32][N])."""
+    _need(q, "q", torch.int8, 2)
+    _need(s, "s", torch.float16, 2)
+    n, k = q.shape
+    if s.shape != (n, k // 32):
+        raise ValueError(f"scales must be [{n}][{k // 32}], got {tuple(s.shape)}")
+    _ready(q)
+    packed = torch.empty((k // 32, n, 16), dtype=torch.uint8, device=q.device)
+    w_scales = torch.empty((k // 32, n), dtype=torch.float16, device=q.device)
+    _check("w4a8_pack_weights", load_library().w4a8_pack_weights(
+        q.data_ptr(), s.data_ptr(), k, n, packed.data_ptr(), w_scales.data_ptr(), _stream(q)))
+    return packed, w_scales
+
+
+def _weights_shape(packed: torch.Tensor, w_scales: torch.Tensor):
+    _need(packed, "packed_w", torch.uint8, 3)
+    _need(w_scales, "w_scales", torch.float16, 2)
+    nb, n, width = packed.shape
+    if width != 16 or w_scales.shape != (nb, n):
+        raise ValueError("packed_w must be [K/32][N][16] and w_scales [K/32][N]")
+    return nb * 32, n
+
+
+def linear(x: torch.Tensor, packed: torch.Tensor, w_scales: torch.Tensor, path: int = PATH_AUTO,
+           out: torch.Tensor | None = None) -> torch.Tensor:
+    """fp16 activations [M][K] -> fp32 [M][N] through the W4A8 block-32 linear layer."""
+    _need(x, "x", torch.float16, 2)
+    k, n = _weights_shape(packed, w_scales)
+    m = x.shape[0]
+    if x.shape[1] != k:
+        raise ValueError(f"x has K = {x.shape[1]}, weights have K = {k}")
+    if out is None:
+        out = torch.empty((m, n), dtype=torch.float32, device=x.device)
+    else:
+        _need(out, "out", torch.float32, 2)
+        if out.shape != (m, n):
+            raise ValueError("out has the wrong shape")
+    _ready(x)
+    _check("w4a8_linear_path", load_library().w4a8_linear_path(
+        x.data_ptr(), packed.data_ptr(), w_scales.data_ptr(), m, k, n, out.data_ptr(), path,
+        _stream(x)))
+    return out
+
+
+def linear_argmax(x: torch.Tensor, packed: torch.Tensor, w_scales: torch.Tensor,
+                  logits: torch.Tensor | bool | None = None, argmax: torch.Tensor | None = None):
+    """Linear layer + fused argmax per row.  Returns argmax int32 [M], or (argmax, logits)
+    when `logits` is True or a preallocated fp32 [M][N] tensor."""
+    _need(x, "x", torch.float16, 2)
+    k, n = _weights_shape(packed, w_scales)
+    m = x.shape[0]
+    if x.shape[1] != k:
+        raise ValueError(f"x has K = {x.shape[1]}, weights have K = {k}")
+    want_logits = logits is not None and logits is not False
+    if logits is True:
+        logits = torch.empty((m, n), dtype=torch.float32, device=x.device)
+    elif want_logits:
+        _need(logits, "logits", torch.float32, 2)
+    if argmax is None:
+        argmax = torch.empty((m,), dtype=torch.int32, device=x.device)
+    else:
+        _need(argmax, "argmax", torch.int32, 1)
+    _ready(x)
+    _check("w4a8_linear_argmax", load_library().w4a8_linear_argmax(
+        x.data_ptr(), packed.data_ptr(), w_scales.data_ptr(), m, k, n,
+        logits.data_ptr() if want_logits else None, argmax.data_ptr(), _stream(x)))
+    return (argmax, logits) if want_logits else argmax
+
+
+def quantize_act(x: torch.Tensor):
+    """The in-kernel activation quantiser on its own: (qx int8 [M][K], sx fp32 [M][K/32])."""
+    _need(x, "x", torch.float16, 2)
+    m, k = x.shape
+    qx = torch.empty((m, k), dtype=torch.int8, device=x.device)
+    sx = torch.empty((m, k // 32), dtype=torch.float32, device=x.device)
+    _ready(x)
+    _check("w4a8_quantize_act", load_library().w4a8_quantize_act(
+        x.data_ptr(), m, k, qx.data_ptr(), sx.data_ptr(), _stream(x)))
+    return qx, sx
+
+
+def block_sums(x: torch.Tensor, packed: torch.Tensor, path: int = PATH_AUTO) -> torch.Tensor:
+    """Unscaled integer block sums int32 [M][N][K/32] as the chosen kernel forms them."""
+    _need(x, "x", torch.float16, 2)
+    _need(packed, "packed_w", torch.uint8, 3)
+    nb, n, _ = packed.shape
+    m, k = x.shape
+    if k != nb * 32:
+        raise ValueError("x and packed_w disagree on K")
+    sums = torch.empty((m, n, nb), dtype=torch.int32, device=x.device)
+    _ready(x)
+    _check("w4a8_block_sums", load_library().w4a8_block_sums(
+        x.data_ptr(), packed.data_ptr(), m, k, n, sums.data_ptr(), path, _stream(x)))
+    return sums
+
+
+def gemv_max_m() -> int:
+    return int(load_library().w4a8_gemv_max_m())

@@ -1,0 +1,266 @@
+// C ABI of the W4A8 block-32 library: argument validation, per-device scratch,
+// stage dispatch (decode GEMV or prefill GEMM) and error reporting.
+#include <cstdarg>
+#include <cstdio>
+#include <cstdlib>
+#include <cstring>
+#include <mutex>
+
+#include "kernels.hpp"
+
+namespace w4a8 {
+
+namespace {
+
+thread_local char g_error[512] = "";
+
+constexpr int kMaxDevices = 64;
+constexpr size_t kInitialWork = 32u << 20;
+
+struct DeviceState {
+  bool ready = false;
+  Scratch sc;
+};
+DeviceState g_dev[kMaxDevices];
+bool g_any_ready = false;
+std::mutex g_mutex;
+
+int g_gemv_max_m = -1;
+
+int current_state(DeviceState** out) {
+  if (!g_any_ready) {
+    set_error("w4a8_init has not been called");
+    return W4A8_ENOINIT;
+  }
+  int dev = -1;
+  W4A8_HIP(hipGetDevice(&dev));
+  if (dev < 0 || dev >= kMaxDevices || !g_dev[dev].ready) {
+    set_error("w4a8_init has not been called for device %d", dev);
+    return W4A8_ENOINIT;
+  }
+  *out = &g_dev[dev];
+  return W4A8_OK;
+}
+
+bool aligned(const void* p, size_t a) { return (reinterpret_cast<uintptr_t>(p) % a) == 0; }
+
+int check_shape(int64_t M, int64_t K, int64_t N, int64_t max_m) {
+  if (M < 1 || M > max_m) {
+    set_error("M = %lld out of range [1, %lld]", static_cast<long long>(M), static_cast<long long>(max_m));
+    return W4A8_EINVAL;
+  }
+  if (K < kBlock || K % kBlock != 0 || K >= (int64_t{1} << 31)) {
+    set_error("K = %lld must be a positive multiple of 32 below 2^31", static_cast<long long>(K));
+    return W4A8_EINVAL;
+  }
+  if (N < 64 || N % 64 != 0 || N / 64 >= kMaxTickets - 1) {
+    set_error("N = %lld must be a positive multiple of 64 below %lld", static_cast<long long>(N),
+              static_cast<long long>(int64_t{64} * (kMaxTickets - 1)));
+    return W4A8_EINVAL;
+  }
+  if (K / 2 * N >= (int64_t{1} << 40)) {
+    set_error("packed weights of %lld x %lld exceed 2^40 bytes", static_cast<long long>(K),
+              static_cast<long long>(N));
+    return W4A8_EINVAL;
+  }
+  return W4A8_OK;
+}
+
+#define W4A8_REQUIRE(cond, ...)   \
+  do {                            \
+    if (!(cond)) {                \
+      set_error(__VA_ARGS__);     \
+      return W4A8_EINVAL;         \
+    }                             \
+  } while (0)
+
+int check_linear_args(const uint16_t* x, const uint8_t* pw, const uint16_t* ws, int64_t M, int64_t K,
+                      int64_t N, int64_t max_m) {
+  W4A8_REQUIRE(x && pw && ws, "null input pointer");
+  int rc = check_shape(M, K, N, max_m);
+  if (rc != W4A8_OK) return rc;
+  W4A8_REQUIRE(aligned(x, 8), "x must be 8-byte aligned");
+  W4A8_REQUIRE(aligned(pw, 16), "packed_w must be 16-byte aligned");
+  W4A8_REQUIRE(aligned(ws, 8), "w_scales must be 8-byte aligned");
+  return W4A8_OK;
+}
+
+}  // namespace
+
+void set_error(const char* fmt, ...) {
+  va_list ap;
+  va_start(ap, fmt);
+  vsnprintf(g_error, sizeof(g_error), fmt, ap);
+  va_end(ap);
+}
+
+int hip_fail(hipError_t e, const char* what) {
+  set_error("%s failed: %s", what, hipGetErrorString(e));
+  return W4A8_EHIP;
+}
+
+int scratch_for(size_t work_bytes, Scratch** out) {
+  DeviceState* st = nullptr;
+  int rc = current_state(&st);
+  if (rc != W4A8_OK) return rc;
+  Scratch& sc = st->sc;
+  if (work_bytes > sc.work_bytes) {
+    std::lock_guard<std::mutex> lock(g_mutex);
+    if (work_bytes > sc.work_bytes) {
+      // Kernels already queued may still read the old buffer.
+      W4A8_HIP(hipDeviceSynchronize());
+      if (sc.work) W4A8_HIP(hipFree(sc.work));
+      sc.work = nullptr;
+      sc.work_bytes = 0;
+      const size_t bytes = (work_bytes + (1u << 20) - 1) & ~static_cast<size_t>((1u << 20) - 1);
+      W4A8_HIP(hipMalloc(&sc.work, bytes));
+      sc.work_bytes = bytes;
+    }
+  }
+  *out = &sc;
+  return W4A8_OK;
+}
+
+int gemv_max_m() {
+  if (g_gemv_max_m < 0) {
+    int v = 4;
+    if (const char* e = std::getenv("W4A8_GEMV_MAX_M")) {
+      const int u = std::atoi(e);
+      if (u >= 0 && u <= 64) v = u;
+    }
+    g_gemv_max_m = v;
+  }
+  return g_gemv_max_m;
+}
+
+}  // namespace w4a8
+
+using namespace w4a8;
+
+extern "C" {
+
+int w4a8_init(int device) {
+  int count = 0;
+  W4A8_HIP(hipGetDeviceCount(&count));
+  W4A8_REQUIRE(device >= 0 && device < count && device < kMaxDevices, "device %d not present", device);
+  W4A8_HIP(hipSetDevice(device));
+  std::lock_guard<std::mutex> lock(g_mutex);
+  DeviceState& st = g_dev[device];
+  if (st.ready) return W4A8_OK;
+  hipDeviceProp_t prop;
+  W4A8_HIP(hipGetDeviceProperties(&prop, device));
+  if (std::strncmp(prop.gcnArchName, "gfx950", 6) != 0) {
+    set_error("device %d is %s; this library is built for gfx950 only", device, prop.gcnArchName);
+    return W4A8_EUNSUPPORTED;
+  }
+  Scratch& sc = st.sc;
+  sc.bytes = kMaxTickets * sizeof(uint32_t) + kMaxArgmaxRows * sizeof(unsigned long long);
+  W4A8_HIP(hipMalloc(&sc.base, sc.bytes));
+  W4A8_HIP(hipMemset(sc.base, 0, sc.bytes));
+  sc.slots = static_cast<unsigned long long*>(sc.base);
+  sc.tickets = reinterpret_cast<uint32_t*>(static_cast<char*>(sc.base) +
+                                           kMaxArgmaxRows * sizeof(unsigned long long));
+  W4A8_HIP(hipMalloc(&sc.work, kInitialWork));
+  sc.work_bytes = kInitialWork;
+  W4A8_HIP(hipDeviceSynchronize());
+  st.ready = true;
+  g_any_ready = true;
+  return W4A8_OK;
+}
+
+int w4a8_pack_weights(const int8_t* q, const uint16_t* s, int64_t K, int64_t N, uint8_t* packed_w,
+                      uint16_t* w_scales, hipStream_t stream) {
+  W4A8_REQUIRE(q && s && packed_w && w_scales, "null pointer");
+  int rc = check_shape(1, K, N, 1);
+  if (rc != W4A8_OK) return rc;
+  W4A8_REQUIRE(aligned(packed_w, 16), "packed_w must be 16-byte aligned");
+  W4A8_REQUIRE(aligned(s, 2) && aligned(w_scales, 2), "scales must be 2-byte aligned");
+  DeviceState* st = nullptr;
+  rc = current_state(&st);
+  if (rc != W4A8_OK) return rc;
+  return launch_pack(q, s, static_cast<int>(K), static_cast<int>(N), packed_w, w_scales, stream);
+}
+
+int w4a8_linear_path(const uint16_t* x, const uint8_t* packed_w, const uint16_t* w_scales, int64_t M,
+                     int64_t K, int64_t N, float* out, int path, hipStream_t stream) {
+  int rc = check_linear_args(x, packed_w, w_scales, M, K, N, int64_t{1} << 20);
+  if (rc != W4A8_OK) return rc;
+  W4A8_REQUIRE(out, "null output pointer");
+  W4A8_REQUIRE(aligned(out, 16), "out must be 16-byte aligned");
+  W4A8_REQUIRE(path == W4A8_PATH_AUTO || path == W4A8_PATH_GEMV || path == W4A8_PATH_GEMM,
+               "unknown path %d", path);
+  DeviceState* st = nullptr;
+  rc = current_state(&st);
+  if (rc != W4A8_OK) return rc;
+  if (path == W4A8_PATH_AUTO) path = M <= gemv_max_m() ? W4A8_PATH_GEMV : W4A8_PATH_GEMM;
+  if (path == W4A8_PATH_GEMV) {
+    GemvArgs a{x, packed_w, w_scales, static_cast<int>(M), static_cast<int>(K), static_cast<int>(N),
+               out, nullptr, nullptr, nullptr};
+    return launch_gemv(a, 0, stream);
+  }
+  GemmArgs a{x, packed_w, w_scales, static_cast<int>(M), static_cast<int>(K), static_cast<int>(N), out,
+             nullptr};
+  return launch_gemm(a, 0, stream);
+}
+
+int w4a8_linear(const uint16_t* x, const uint8_t* packed_w, const uint16_t* w_scales, int64_t M,
+                int64_t K, int64_t N, float* out, hipStream_t stream) {
+  return w4a8_linear_path(x, packed_w, w_scales, M, K, N, out, W4A8_PATH_AUTO, stream);
+}
+
+int w4a8_linear_argmax(const uint16_t* x, const uint8_t* packed_w, const uint16_t* w_scales, int64_t M,
+                       int64_t K, int64_t N, float* logits, int32_t* argmax, hipStream_t stream) {
+  int rc = check_linear_args(x, packed_w, w_scales, M, K, N, kMaxArgmaxRows);
+  if (rc != W4A8_OK) return rc;
+  W4A8_REQUIRE(argmax, "null argmax pointer");
+  W4A8_REQUIRE(aligned(argmax, 4), "argmax must be 4-byte aligned");
+  W4A8_REQUIRE(!logits || aligned(logits, 16), "logits must be 16-byte aligned");
+  DeviceState* st = nullptr;
+  rc = current_state(&st);
+  if (rc != W4A8_OK) return rc;
+  GemvArgs a{x, packed_w, w_scales, static_cast<int>(M), static_cast<int>(K), static_cast<int>(N),
+             nullptr, nullptr, logits, argmax};
+  return launch_gemv(a, 2, stream);
+}
+
+int w4a8_quantize_act(const uint16_t* x, int64_t M, int64_t K, int8_t* qx, float* sx,
+                      hipStream_t stream) {
+  W4A8_REQUIRE(x && qx && sx, "null pointer");
+  int rc = check_shape(M, K, 64, int64_t{1} << 24);
+  if (rc != W4A8_OK) return rc;
+  W4A8_REQUIRE(M * K < (int64_t{1} << 34), "M * K too large");
+  W4A8_REQUIRE(aligned(x, 8) && aligned(qx, 4) && aligned(sx, 4), "misaligned pointer");
+  DeviceState* st = nullptr;
+  rc = current_state(&st);
+  if (rc != W4A8_OK) return rc;
+  return launch_quantize_export(x, static_cast<int>(M), static_cast<int>(K), qx, sx, stream);
+}
+
+int w4a8_block_sums(const uint16_t* x, const uint8_t* packed_w, int64_t M, int64_t K, int64_t N,
+                    int32_t* sums, int path, hipStream_t stream) {
+  // The block-sum kernels read no scales; the packed weights stand in for them here.
+  int rc = check_linear_args(x, packed_w, reinterpret_cast<const uint16_t*>(packed_w), M, K, N,
+                             int64_t{1} << 16);
+  if (rc != W4A8_OK) return rc;
+  W4A8_REQUIRE(sums && aligned(sums, 16), "sums must be a 16-byte aligned pointer");
+  W4A8_REQUIRE(path == W4A8_PATH_AUTO || path == W4A8_PATH_GEMV || path == W4A8_PATH_GEMM,
+               "unknown path %d", path);
+  DeviceState* st = nullptr;
+  rc = current_state(&st);
+  if (rc != W4A8_OK) return rc;
+  if (path == W4A8_PATH_AUTO) path = M <= gemv_max_m() ? W4A8_PATH_GEMV : W4A8_PATH_GEMM;
+  if (path == W4A8_PATH_GEMV) {
+    GemvArgs a{x, packed_w, nullptr, static_cast<int>(M), static_cast<int>(K), static_cast<int>(N),
+               nullptr, sums, nullptr, nullptr};
+    return launch_gemv(a, 1, stream);
+  }
+  GemmArgs a{x, packed_w, nullptr, static_cast<int>(M), static_cast<int>(K), static_cast<int>(N),
+             nullptr, sums};
+  return launch_gemm(a, 1, stream);
+}
+
+int w4a8_gemv_max_m(void) { return gemv_max_m(); }
+
+const char* w4a8_last_error(void) { return g_error; }
+
+}  // extern "C"

@@ -1,0 +1,119 @@
+// Weight packer and activation quantiser kernels (gfx950).
+#include "kernels.hpp"
+
+namespace w4a8 {
+
+// ------------------------------------------------------------------ packer
+// One thread per (block b, column n): reads the 32 int4 values of column n in
+// block b and writes the 16-byte group packed_w[b][n][0..15] (byte j: element
+// 32b+j in the low nibble, element 32b+16+j in the high nibble) and the scale
+// w_scales[b][n] = s[n][b].  Off the timed path: weights are packed once.
+__global__ __launch_bounds__(256) void pack_kernel(const int8_t* __restrict__ q,
+                                                   const uint16_t* __restrict__ s, int K, int N,
+                                                   uint8_t* __restrict__ packed,
+                                                   uint16_t* __restrict__ w_scales) {
+  const int nb = K / kBlock;
+  const int64_t total = static_cast<int64_t>(nb) * N;
+  const int64_t t = static_cast<int64_t>(blockIdx.x) * blockDim.x + threadIdx.x;
+  if (t >= total) return;
+  const int b = static_cast<int>(t / N);
+  const int n = static_cast<int>(t % N);
+  const int8_t* src = q + static_cast<int64_t>(n) * K + static_cast<int64_t>(b) * kBlock;
+  uint32_t words[4];
+#pragma unroll
+  for (int d = 0; d < 4; ++d) {
+    uint32_t w = 0;
+#pragma unroll
+    for (int e = 0; e < 4; ++e) {
+      const int j = 4 * d + e;
+      const uint32_t lo = static_cast<uint32_t>(src[j]) & 0xFu;
+      const uint32_t hi = static_cast<uint32_t>(src[j + 16]) & 0xFu;
+      w |= (lo | (hi << 4)) << (8 * e);
+    }
+    words[d] = w;
+  }
+  *reinterpret_cast<uint4*>(packed + t * kPackedBytes) = make_uint4(words[0], words[1], words[2], words[3]);
+  w_scales[t] = s[static_cast<int64_t>(n) * nb + b];
+}
+
+int launch_pack(const int8_t* q, const uint16_t* s, int K, int N, uint8_t* packed,
+                uint16_t* w_scales, hipStream_t stream) {
+  const int64_t total = static_cast<int64_t>(K / kBlock) * N;
+  const int64_t grid = (total + 255) / 256;
+  hipLaunchKernelGGL(pack_kernel, dim3(static_cast<unsigned>(grid)), dim3(256), 0, stream, q, s, K, N,
+                     packed, w_scales);
+  W4A8_HIP(hipGetLastError());
+  return W4A8_OK;
+}
+
+// -------------------------------------------------------- quantiser export
+// Thread t quantises elements 4g .. 4g+3 of block b of row m, with 8
+// consecutive threads per block (K/4 is a multiple of 8, so the groups of 8
+// are lane-aligned and whole groups are in or out of range together).
+__global__ __launch_bounds__(256) void quantize_export_kernel(const uint16_t* __restrict__ x, int M,
+                                                              int K, int8_t* __restrict__ qx,
+                                                              float* __restrict__ sx) {
+  const int64_t per_row = K / 4;
+  const int64_t t = static_cast<int64_t>(blockIdx.x) * blockDim.x + threadIdx.x;
+  if (t >= per_row * M) return;
+  const int64_t m = t / per_row;
+  const int64_t e = t % per_row;  // dword index within the row
+  float v[4];
+  unpack_half4(*reinterpret_cast<const uint2*>(x + m * K + 4 * e), v);
+  float scale;
+  const uint32_t codes = quantize4_group8(v[0], v[1], v[2], v[3], &scale);
+  *reinterpret_cast<uint32_t*>(qx + m * K + 4 * e) = codes;
+  if ((e & 7) == 0) sx[m * (K / kBlock) + e / 8] = scale;
+}
+
+int launch_quantize_export(const uint16_t* x, int M, int K, int8_t* qx, float* sx,
+                           hipStream_t stream) {
+  const int64_t total = static_cast<int64_t>(M) * (K / 4);
+  const int64_t grid = (total + 255) / 256;
+  hipLaunchKernelGGL(quantize_export_kernel, dim3(static_cast<unsigned>(grid)), dim3(256), 0, stream,
+                     x, M, K, qx, sx);
+  W4A8_HIP(hipGetLastError());
+  return W4A8_OK;
+}
+
+// ------------------------------------------------------ GEMM pre-pass
+// Quantises x [M][K] into the staging layout read by the MFMA GEMM:
+//   qxs [K/32][M_pad][32] int8: the 32 codes of (block b, row m), ordered so that
+//       lane half h of an MFMA operand reads bytes 16h .. 16h+15 and finds
+//       elements 8h .. 8h+7 followed by 16+8h .. 16+8h+7 (the order in which
+//       the weight nibbles unpack, see gemm.hip);
+//   sxs [K/32][M_pad] fp32 block scales.
+// Rows M .. M_pad-1 are written as zeros (codes and scales).
+// Group lane g holds elements 4g .. 4g+3, which land in dword (g with bits 1 and
+// 2 swapped): 0,1,4,5,2,3,6,7.
+__global__ __launch_bounds__(256) void quantize_stage_kernel(const uint16_t* __restrict__ x, int M,
+                                                             int M_pad, int K,
+                                                             uint8_t* __restrict__ qxs,
+                                                             float* __restrict__ sxs) {
+  const int64_t per_row = K / 4;
+  const int64_t t = static_cast<int64_t>(blockIdx.x) * blockDim.x + threadIdx.x;
+  if (t >= per_row * M_pad) return;
+  const int64_t m = t / per_row;
+  const int64_t e = t % per_row;
+  const int64_t b = e / 8;
+  const int g = static_cast<int>(e & 7);
+  float v[4] = {0.f, 0.f, 0.f, 0.f};
+  if (m < M) unpack_half4(*reinterpret_cast<const uint2*>(x + m * K + 4 * e), v);
+  float scale;
+  const uint32_t codes = quantize4_group8(v[0], v[1], v[2], v[3], &scale);
+  const int d = (g & 1) | ((g & 2) << 1) | ((g & 4) >> 1);
+  *reinterpret_cast<uint32_t*>(qxs + (b * M_pad + m) * kBlock + 4 * d) = codes;
+  if (g == 0) sxs[b * M_pad + m] = scale;
+}
+
+int launch_quantize_stage(const uint16_t* x, int M, int M_pad, int K, uint8_t* qxs, float* sxs,
+                          hipStream_t stream) {
+  const int64_t total = static_cast<int64_t>(M_pad) * (K / 4);
+  const int64_t grid = (total + 255) / 256;
+  hipLaunchKernelGGL(quantize_stage_kernel, dim3(static_cast<unsigned>(grid)), dim3(256), 0, stream,
+                     x, M, M_pad, K, qxs, sxs);
+  W4A8_HIP(hipGetLastError());
+  return W4A8_OK;
+}
+
+}  // namespace w4a8

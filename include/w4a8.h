@@ -1,0 +1,139 @@
+/*
+ * w4a8.h -- C ABI of the W4A8 block-32 linear layer for AMD Instinct MI355X (gfx950).
+ *
+ * The operation (ML Drift pages: explainer on tech.dede.sh, section
+ * "Stage-aware optimization for large language models"; x-techcon article,
+ * section on moving less data for large models): an LLM linear layer whose
+ * weights are 4-bit in blocks of 32 and whose activations the kernel
+ * quantises itself, with one kernel for the decode stage (few tokens,
+ * memory-bound) and another for the prefill stage (hundreds of tokens,
+ * compute-bound).  The numeric scheme pinned by this library:
+ *
+ *   weights      qw in [-8, 7] (int4, symmetric), one fp16 scale sw[n][b] per
+ *                output column n and block b of 32 consecutive inputs;
+ *   activations  per token row m and block b: sx[m][b] = fp32(max|x| / 127),
+ *                qx = clamp(round_half_even(fp32(x / sx)), -127, 127);
+ *                an all-zero block gives sx = 0, qx = 0;
+ *   output       out[m][n] = sum_b sx[m][b] * sw[n][b] * I[m][n][b],
+ *                I[m][n][b] = sum_{j<32} qx[m][32b+j] * qw[n][32b+j]  (exact int32).
+ *
+ * Conventions for every entry point:
+ *   - tensor pointers are HIP device pointers to row-major, contiguous data;
+ *     fp16 tensors are passed as uint16_t bit patterns;
+ *   - the caller owns every tensor; the library owns only the scratch memory it
+ *     allocates in w4a8_init (per device) and grows when a larger problem
+ *     arrives (growth synchronises the device, so warm up before timing);
+ *   - calls are asynchronous on `stream` (0 = the null stream); none
+ *     synchronises and none returns results on the host, except as noted;
+ *   - calls that share a device share its scratch and its argmax slots:
+ *     issue them on one stream, or serialise them yourself;
+ *   - outputs must not alias inputs;
+ *   - arguments are validated before any HIP call, so a rejected call has no
+ *     effect; no C++ exception crosses this boundary.
+ *
+ * Shape limits: M >= 1, K >= 32 with K % 32 == 0, N >= 64 with N % 64 == 0,
+ * all three below 2^31, and K * N / 2 bytes of packed weights below 2^40.
+ * Inputs must be finite (NaN and Inf activations give unspecified results).
+ */
+#ifndef W4A8_H
+#define W4A8_H
+
+#include <stdint.h>
+#include <hip/hip_runtime_api.h>
+
+#if defined(__GNUC__)
+#define W4A8_API __attribute__((visibility("default")))
+#else
+#define W4A8_API
+#endif
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+/* Status codes: 0 on success, negative on failure. */
+#define W4A8_OK            0
+#define W4A8_EINVAL       -1  /* null pointer, bad shape, misaligned pointer, bad path/option */
+#define W4A8_EUNSUPPORTED -2  /* the device is not gfx950 */
+#define W4A8_EHIP         -3  /* a HIP runtime call or kernel launch failed; see w4a8_last_error() */
+#define W4A8_ENOINIT      -4  /* w4a8_init has not succeeded on the current device */
+
+/* Kernel selection for w4a8_linear_path / w4a8_block_sums. */
+#define W4A8_PATH_AUTO 0  /* decode GEMV for M <= w4a8_gemv_max_m(), prefill MFMA GEMM above */
+#define W4A8_PATH_GEMV 1  /* force the decode GEMV (any M; slow for large M) */
+#define W4A8_PATH_GEMM 2  /* force the quantise pre-pass + MFMA GEMM (any M) */
+
+/*
+ * Select `device`, check that it is gfx950 and allocate the library's scratch
+ * (quantised-activation staging, split-K partials, completion tickets, argmax
+ * slots).  Idempotent per device.  Returns W4A8_EUNSUPPORTED on other GPUs.
+ */
+W4A8_API int w4a8_init(int device);
+
+/*
+ * Pack int4 weights into the K-block-major layout read by every kernel
+ * (the pages fix 4-bit weights in blocks of 32; the layout is this library's).
+ *   q         int8  [N][K], values in [-8, 7] (out-of-range values are masked to 4 bits)
+ *   s         fp16  [N][K/32] weight scales
+ *   packed_w  uint8 [K/32][N][16], 16-byte aligned: byte j of (block b, column n)
+ *             = (q[n][32b+j] & 0xF) | (q[n][32b+16+j] & 0xF) << 4
+ *   w_scales  fp16  [K/32][N]: w_scales[b][n] = s[n][b]
+ */
+W4A8_API int w4a8_pack_weights(const int8_t* q, const uint16_t* s, int64_t K, int64_t N,
+                      uint8_t* packed_w, uint16_t* w_scales, hipStream_t stream);
+
+/*
+ * out = W4A8 linear of x (see the header comment), fp32 [M][N], 16-byte aligned.
+ *   x         fp16 [M][K], 8-byte aligned
+ *   packed_w, w_scales as produced by w4a8_pack_weights (16- and 8-byte aligned)
+ * Stage choice: M <= w4a8_gemv_max_m() runs the decode GEMV, which quantises
+ * the activations inside the kernel; larger M runs a quantise pre-pass into
+ * library scratch followed by the int8-MFMA prefill GEMM.
+ */
+W4A8_API int w4a8_linear(const uint16_t* x, const uint8_t* packed_w, const uint16_t* w_scales,
+                int64_t M, int64_t K, int64_t N, float* out, hipStream_t stream);
+
+/* w4a8_linear with an explicit kernel choice (W4A8_PATH_*), for tests and tuning. */
+W4A8_API int w4a8_linear_path(const uint16_t* x, const uint8_t* packed_w, const uint16_t* w_scales,
+                     int64_t M, int64_t K, int64_t N, float* out, int path,
+                     hipStream_t stream);
+
+/*
+ * Linear layer followed by argmax over each output row (the pages' benchmark
+ * samples with argmax).  argmax[m] = lowest n with out[m][n] maximal, -0.0 and
+ * +0.0 compare equal.  `logits` (fp32 [M][N], 16-byte aligned) may be NULL, in
+ * which case the logits are never written to memory.  argmax is int32 [M].
+ * M must not exceed 64.  Runs the decode GEMV for any M.
+ */
+W4A8_API int w4a8_linear_argmax(const uint16_t* x, const uint8_t* packed_w, const uint16_t* w_scales,
+                       int64_t M, int64_t K, int64_t N, float* logits, int32_t* argmax,
+                       hipStream_t stream);
+
+/*
+ * Verification export: the in-kernel activation quantiser run on its own.
+ *   x 8-byte aligned; qx int8 [M][K] and sx fp32 [M][K/32], 4-byte aligned
+ *   (the same device function the GEMV and the GEMM pre-pass use)
+ */
+W4A8_API int w4a8_quantize_act(const uint16_t* x, int64_t M, int64_t K, int8_t* qx, float* sx,
+                      hipStream_t stream);
+
+/*
+ * Verification export: the unscaled integer block sums I[m][n][b] as the chosen
+ * kernel forms them (same quantiser, unpacking and integer arithmetic as
+ * w4a8_linear_path with that path), int32 [M][N][K/32], 16-byte aligned.
+ * M must not exceed 65536.  The weight scales are not needed for this export.
+ */
+W4A8_API int w4a8_block_sums(const uint16_t* x, const uint8_t* packed_w, int64_t M, int64_t K,
+                    int64_t N, int32_t* sums, int path, hipStream_t stream);
+
+/* Largest M that W4A8_PATH_AUTO sends to the decode GEMV. */
+W4A8_API int w4a8_gemv_max_m(void);
+
+/* Message of the last failure on the calling thread ("" if none). */
+W4A8_API const char* w4a8_last_error(void);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* W4A8_H */

@@ -1,0 +1,68 @@
+"""The C ABI library on a machine without a GPU: it loads, exports every declared
+entry point, and rejects invalid arguments before touching the device."""
+import ctypes
+
+import pytest
+
+import bit_block_quantized_w4a8_amd as w4
+
+
+@pytest.fixture(scope="module")
+def lib():
+    return w4.load_library()
+
+
+def test_exports_every_declared_symbol(lib):
+    names = w4.declared_functions()
+    assert len(names) == 9, names
+    for name in names:
+        assert hasattr(lib, name), name
+
+
+def test_gemv_threshold(lib):
+    assert 1 <= lib.w4a8_gemv_max_m() <= 64
+
+
+ALIGNED = 1 << 20       # fake, suitably aligned device addresses: never dereferenced
+P = ctypes.c_void_p
+
+
+def _linear(lib, x=ALIGNED, pw=ALIGNED, ws=ALIGNED, m=1, k=64, n=128, out=ALIGNED, path=0):
+    return lib.w4a8_linear_path(P(x), P(pw), P(ws), m, k, n, P(out), path, None)
+
+
+@pytest.mark.parametrize("kw", [
+    dict(x=0), dict(pw=0), dict(ws=0), dict(out=0),
+    dict(m=0), dict(m=-3), dict(k=0), dict(k=48), dict(k=16), dict(n=0), dict(n=96), dict(n=32),
+    dict(x=ALIGNED + 2), dict(pw=ALIGNED + 8), dict(ws=ALIGNED + 2), dict(out=ALIGNED + 4),
+    dict(path=3), dict(path=-1),
+])
+def test_linear_rejects_bad_arguments(lib, kw):
+    assert _linear(lib, **kw) == w4.W4A8_EINVAL
+    assert lib.w4a8_last_error()
+
+
+def test_valid_arguments_need_init(lib):
+    assert _linear(lib) == w4.W4A8_ENOINIT
+    assert b"w4a8_init" in lib.w4a8_last_error()
+
+
+def test_other_entry_points_validate(lib):
+    assert lib.w4a8_linear(P(0), P(ALIGNED), P(ALIGNED), 1, 64, 128, P(ALIGNED), None) == w4.W4A8_EINVAL
+    assert lib.w4a8_linear_argmax(P(ALIGNED), P(ALIGNED), P(ALIGNED), 65, 64, 128, P(0), P(ALIGNED), None) == w4.W4A8_EINVAL
+    assert lib.w4a8_linear_argmax(P(ALIGNED), P(ALIGNED), P(ALIGNED), 1, 64, 128, P(0), P(0), None) == w4.W4A8_EINVAL
+    assert lib.w4a8_linear_argmax(P(ALIGNED), P(ALIGNED), P(ALIGNED), 1, 64, 128, P(ALIGNED + 4), P(ALIGNED), None) == w4.W4A8_EINVAL
+    assert lib.w4a8_linear_argmax(P(ALIGNED), P(ALIGNED), P(ALIGNED), 1, 64, 128, P(0), P(ALIGNED), None) == w4.W4A8_ENOINIT
+    assert lib.w4a8_quantize_act(P(ALIGNED), 2, 40, P(ALIGNED), P(ALIGNED), None) == w4.W4A8_EINVAL
+    assert lib.w4a8_quantize_act(P(ALIGNED), 2, 64, P(0), P(ALIGNED), None) == w4.W4A8_EINVAL
+    assert lib.w4a8_block_sums(P(ALIGNED), P(ALIGNED), 1, 64, 128, P(ALIGNED + 4), 0, None) == w4.W4A8_EINVAL
+    assert lib.w4a8_block_sums(P(ALIGNED), P(ALIGNED), 1, 64, 128, P(ALIGNED), 7, None) == w4.W4A8_EINVAL
+    assert lib.w4a8_pack_weights(P(ALIGNED), P(ALIGNED), 64, 100, P(ALIGNED), P(ALIGNED), None) == w4.W4A8_EINVAL
+    assert lib.w4a8_pack_weights(P(ALIGNED), P(ALIGNED), 64, 128, P(ALIGNED + 1), P(ALIGNED), None) == w4.W4A8_EINVAL
+
+
+def test_python_binding_rejects_cpu_tensors():
+    import torch
+    with pytest.raises(TypeError):
+        w4.linear(torch.zeros(1, 32, dtype=torch.float16), torch.zeros(1, 64, 16, dtype=torch.uint8),
+                  torch.zeros(1, 64, dtype=torch.float16))
