@@ -1,0 +1,267 @@
+"""Benchmark of the W4A8 block-32 linear layer on one MI355X.
+
+Prints ONE JSON line.  The headline `value` is the decode stage: the four
+projections of one synthetic transformer layer of hidden size 2048 at M = 1
+token (qkv 2048x2560, o 2048x2048, gate_up 2048x16384, down 8192x2048), each a
+w4a8_linear call whose weights are read from HBM (a rotation over 32 weight
+replicas, 1.08 GB, defeats the 256 MB last-level cache).  value = algorithmic
+bytes of one layer / time of one layer, in GB/s; a step is one such layer.
+
+Also reported, each on its own keys: the prefill stage (the same projections at
+M = 512 with outlier channels, int8 TOPS against the int8 MFMA peak), the
+decode-batch sweep on K = 4096, N = 14336 at M in {1, 4, 8, 16} for both
+kernels, the roofline of the dominant kernel (the gate_up GEMV) and the CPU
+oracle timed on the host.
+
+Timing: launches are queued behind a GPU sleep so the device runs them back to
+back, and two HIP events (torch.cuda.Event, recorded on the stream every
+kernel is launched on) bracket each timed batch: the K steps of the layer, and
+for every projection a batch of 4K launches of that projection alone, whose
+average is the per-launch duration used for the roofline.
+"""
+from __future__ import annotations
+
+import argparse
+import json
+import os
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+if ROOT not in sys.path:
+    sys.path.insert(0, ROOT)
+
+METRIC = "decode GEMV HBM GB/s (% of peak) + prefill M=512 int8 TOPS; synthetic tok/s"
+HBM_PEAK_GBS = 8000.0          # MI355X HBM3E
+INT8_PEAK_TOPS = 5000.0        # MI355X dense int8 MFMA (5.0 POP/s)
+REPLICA_BYTES_MIN = 1 << 30    # weight rotation size for cold-cache timing
+
+
+def algorithmic_bytes(m, k, n):
+    """Packed int4 weights + fp16 scales + fp16 activations + fp32 outputs, each moved once."""
+    return k * n // 2 + (k // 32) * n * 2 + m * k * 2 + m * n * 4
+
+
+def parse():
+    ap = argparse.ArgumentParser(description=__doc__.split("\n")[0])
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=50)
+    ap.add_argument("--warmup", type=int, default=10)
+    ap.add_argument("--skip-prefill", action="store_true")
+    ap.add_argument("--skip-wide", action="store_true")
+    ap.add_argument("--skip-cpu", action="store_true")
+    ap.add_argument("--cpu-seconds", type=float, default=10.0, help="CPU oracle sample budget")
+    return ap.parse_args()
+
+
+class Timer:
+    """Queues work behind a GPU sleep, then measures it with events on the current stream."""
+
+    def __init__(self, torch):
+        self.torch = torch
+        ev = [torch.cuda.Event(enable_timing=True) for _ in range(2)]
+        torch.cuda.synchronize()
+        torch.cuda._sleep(1000)
+        ev[0].record()
+        torch.cuda._sleep(1_000_000)
+        ev[1].record()
+        torch.cuda.synchronize()
+        self.cycles_per_ms = 1_000_000 / max(ev[0].elapsed_time(ev[1]), 1e-3)
+
+    def sleep_ms(self, ms):
+        self.torch.cuda._sleep(int(self.cycles_per_ms * ms))
+
+    def event(self):
+        e = self.torch.cuda.Event(enable_timing=True)
+        e.record()
+        return e
+
+
+def replicas(w4, torch, weights, total_bytes):
+    """Copies of each projection's packed weights so a rotation spans >= total_bytes."""
+    r = max(1, -(-REPLICA_BYTES_MIN // total_bytes))
+    out = {}
+    for name, (packed, ws) in weights.items():
+        out[name] = [(packed, ws)] + [(packed.clone(), ws.clone()) for _ in range(r - 1)]
+    torch.cuda.synchronize()
+    return out, r
+
+
+def upload(w4, torch, inputs):
+    dev = torch.device("cuda:0")
+    weights, xs = {}, {}
+    for name, (x, qw, sw) in inputs.items():
+        weights[name] = w4.pack_weights(torch.from_numpy(qw).to(dev), torch.from_numpy(sw).to(dev))
+        xs[name] = torch.from_numpy(x).to(dev)
+    torch.cuda.synchronize()
+    return weights, xs
+
+
+def back_to_back(torch, timer, launch, count):
+    """Average time of `count` launches queued back to back (ms per launch)."""
+    torch.cuda.synchronize()
+    timer.sleep_ms(5 + 0.05 * count)      # enough for the host to queue every launch
+    t0 = timer.event()
+    for i in range(count):
+        launch(i)
+    t1 = timer.event()
+    torch.cuda.synchronize()
+    return t0.elapsed_time(t1) / count
+
+
+def bench_decode(w4, torch, synth, timer, steps, warmup):
+    inputs = synth.workload_inputs("decode")
+    shapes = {p: (x.shape[0], x.shape[1], qw.shape[0]) for p, (x, qw, _) in inputs.items()}
+    weights, xs = upload(w4, torch, inputs)
+    layer_bytes = sum(algorithmic_bytes(*s) for s in shapes.values())
+    reps, r = replicas(w4, torch, weights, layer_bytes)
+    outs = {p: torch.empty((m, n), dtype=torch.float32, device="cuda:0") for p, (m, k, n) in shapes.items()}
+    names = list(shapes)
+
+    def one(p, i):
+        packed, ws = reps[p][i % r]
+        w4.linear(xs[p], packed, ws, out=outs[p])
+
+    def step(i):
+        for p in names:
+            one(p, i)
+
+    for i in range(warmup):
+        step(i)
+    ms_per_step = back_to_back(torch, timer, lambda i: step(warmup + i), steps)
+    per = {}
+    for p in names:
+        us = 1000.0 * back_to_back(torch, timer, lambda i, p=p: one(p, i), 4 * steps)
+        b = algorithmic_bytes(*shapes[p])
+        per[p] = {"M": shapes[p][0], "K": shapes[p][1], "N": shapes[p][2], "bytes": b,
+                  "us": round(us, 3), "GB_s": round(b / us / 1e3, 1),
+                  "frac_hbm": round(b / us / 1e3 / HBM_PEAK_GBS, 4)}
+    return {"layer_bytes": layer_bytes, "ms_per_step": ms_per_step, "replicas": r,
+            "rotation_bytes": r * layer_bytes, "per_projection": per}
+
+
+def bench_prefill(w4, torch, synth, timer, iters):
+    inputs = synth.workload_inputs("prefill")
+    weights, xs = upload(w4, torch, inputs)
+    per, tot_ops, tot_us = {}, 0, 0.0
+    for p, (x, qw, _) in inputs.items():
+        m, k = x.shape
+        n = qw.shape[0]
+        packed, ws = weights[p]
+        out = torch.empty((m, n), dtype=torch.float32, device="cuda:0")
+        for _ in range(3):
+            w4.linear(xs[p], packed, ws, out=out)
+        us = 1000.0 * back_to_back(torch, timer, lambda i: w4.linear(xs[p], packed, ws, out=out), iters)
+        ops = 2 * m * k * n
+        per[p] = {"M": m, "K": k, "N": n, "us": round(us, 2), "TOPS": round(ops / us / 1e6, 1),
+                  "frac_int8_peak": round(ops / us / 1e6 / INT8_PEAK_TOPS, 4)}
+        tot_ops += ops
+        tot_us += us
+    tops = tot_ops / tot_us / 1e6
+    return {"TOPS": round(tops, 1), "frac_int8_peak": round(tops / INT8_PEAK_TOPS, 4),
+            "layer_us": round(tot_us, 2), "prefill_tokens_per_s_per_layer": round(512 / tot_us * 1e6, 1),
+            "note": "per call: activation-quantisation pre-pass + GEMM, weights warm",
+            "per_projection": per}
+
+
+def bench_wide(w4, torch, synth, timer, iters):
+    res = {}
+    _, qw, sw = synth.workload_inputs("wide", 1)["wide"]
+    k, n = qw.shape[1], qw.shape[0]
+    dev = torch.device("cuda:0")
+    packed, ws = w4.pack_weights(torch.from_numpy(qw).to(dev), torch.from_numpy(sw).to(dev))
+    reps, r = replicas(w4, torch, {"w": (packed, ws)}, algorithmic_bytes(1, k, n))
+    reps = reps["w"]
+    for m in synth.WORKLOADS["wide"]["M"]:
+        x = torch.from_numpy(synth.workload_inputs("wide", m)["wide"][0]).to(dev)
+        out = torch.empty((m, n), dtype=torch.float32, device=dev)
+        row = {}
+        for path, name in ((w4.PATH_GEMV, "gemv"), (w4.PATH_GEMM, "gemm")):
+            for i in range(3):
+                w4.linear(x, *reps[i % r], path=path, out=out)
+            us = 1000.0 * back_to_back(torch, timer, lambda i: w4.linear(x, *reps[i % r], path=path, out=out), iters)
+            b = algorithmic_bytes(m, k, n)
+            row[name] = {"us": round(us, 2), "GB_s": round(b / us / 1e3, 1)}
+        row["auto"] = "gemv" if m <= w4.gemv_max_m() else "gemm"
+        res[f"M={m}"] = row
+    return {"K": k, "N": n, "replicas": r, "results": res}
+
+
+def cpu_baseline(synth, budget_s):
+    """The numpy oracle on the decode layer (all four projections, M = 1), repeated to fill the budget."""
+    import oracle
+    from threadpoolctl import threadpool_info
+
+    inputs = synth.workload_inputs("decode")
+    layer_bytes = sum(algorithmic_bytes(x.shape[0], x.shape[1], qw.shape[0]) for x, qw, _ in inputs.values())
+    passes, t0 = 0, time.perf_counter()
+    while True:
+        for x, qw, sw in inputs.values():
+            oracle.linear(x, qw, sw)
+        passes += 1
+        el = time.perf_counter() - t0
+        if el >= budget_s:
+            break
+    threads = max([i.get("num_threads", 1) for i in threadpool_info()] + [1])
+    return {"value": round(passes * layer_bytes / el / 1e9, 4), "unit": "GB/s", "cores": threads,
+            "kind": "oracle",
+            "sample": f"{passes} passes of the decode layer (4 projections, M=1, {layer_bytes} B) in {el:.1f} s"}
+
+
+def main():
+    args = parse()
+    if args.gpus != 1:
+        print(f"bench.py measures one GPU; --gpus {args.gpus} is not supported by this build "
+              "(the path shards by output columns with no exchange, see DESIGN.md)", file=sys.stderr)
+        sys.exit(2)
+    import torch
+
+    import bit_block_quantized_w4a8_amd as w4
+    import synth
+
+    torch.cuda.set_device(0)
+    w4.init(0)
+    timer = Timer(torch)
+    dec = bench_decode(w4, torch, synth, timer, args.steps, args.warmup)
+    print(f"[bench] decode done: {dec['ms_per_step'] * 1e3:.2f} us per layer", file=sys.stderr, flush=True)
+    pre = None if args.skip_prefill else bench_prefill(w4, torch, synth, timer, max(10, args.steps // 2))
+    if pre:
+        print(f"[bench] prefill done: {pre['TOPS']} TOPS", file=sys.stderr, flush=True)
+    wide = None if args.skip_wide else bench_wide(w4, torch, synth, timer, max(10, args.steps // 2))
+    if wide:
+        print("[bench] decode-batch sweep done", file=sys.stderr, flush=True)
+    cpu = None if args.skip_cpu else cpu_baseline(synth, args.cpu_seconds)
+
+    value = dec["layer_bytes"] / (dec["ms_per_step"] * 1e-3) / 1e9
+    gu = dec["per_projection"]["gate_up"]
+    line = {
+        "metric": METRIC,
+        "value": round(value, 1),
+        "unit": "GB/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": round(dec["ms_per_step"], 5),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "int8",
+        "data": "synthetic (seeded int4 weights, fp16 N(0,1) activations)",
+        "config": {"workload": "decode layer, M=1: qkv 2048x2560, o 2048x2048, gate_up 2048x16384, "
+                               "down 8192x2048; weights cold (rotation over replicas)",
+                   "M": 1, "hidden": 2048, "replicas": dec["replicas"],
+                   "rotation_bytes": dec["rotation_bytes"], "frac_hbm_peak": round(value / HBM_PEAK_GBS, 4)},
+        "roofline": {"bound": "hbm", "kernel": "gemv_kernel<1,0,8> (gate_up 2048x16384, M=1)",
+                     "achieved": gu["GB_s"], "peak": HBM_PEAK_GBS, "unit": "GB/s",
+                     "frac": round(gu["GB_s"] / HBM_PEAK_GBS, 4), "traffic": None,
+                     "bytes_per_launch": gu["bytes"], "us_per_launch": gu["us"]},
+        "cpu_baseline": cpu,
+        "decode_per_projection": dec["per_projection"],
+        "prefill": pre,
+        "decode_batch_sweep": wide,
+    }
+    print(json.dumps(line), flush=True)
+
+
+if __name__ == "__main__":
+    main()

@@ -21,7 +21,6 @@ HIPCC_FLAGS = [
     "-O3",
     "-std=c++17",
     "-fPIC",
-    "-shared",
     "-fvisibility=hidden",
     # packed fp32 VALU instructions are kept out of every kernel
     "-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops",
@@ -36,16 +35,35 @@ def hipcc() -> str:
     return path
 
 
-def build(verbose: bool = False) -> str:
-    sources = sorted(glob.glob(os.path.join(CSRC, "*.hip")))
-    tmp = LIB + ".tmp"
-    cmd = [hipcc(), *HIPCC_FLAGS, "-I", os.path.join(ROOT, "include"), "-o", tmp, *sources]
+def _compile(src: str, obj: str, verbose: bool) -> None:
+    cmd = [hipcc(), *HIPCC_FLAGS, "-c", "-I", os.path.join(ROOT, "include"), "-o", obj, src]
     if verbose:
         print(" ".join(cmd), flush=True)
     res = subprocess.run(cmd, capture_output=True, text=True)
     if res.returncode != 0:
         sys.stderr.write(res.stdout + res.stderr)
-        raise RuntimeError(f"hipcc failed with exit code {res.returncode}")
+        raise RuntimeError(f"hipcc failed on {os.path.basename(src)} with exit code {res.returncode}")
+
+
+def build(verbose: bool = False) -> str:
+    """Compile every source to an object (in parallel), then link libw4a8.so."""
+    from concurrent.futures import ThreadPoolExecutor
+
+    sources = sorted(glob.glob(os.path.join(CSRC, "*.hip")))
+    objdir = os.path.join(PKG, "_build")
+    os.makedirs(objdir, exist_ok=True)
+    objs = [os.path.join(objdir, os.path.basename(s) + ".o") for s in sources]
+    workers = max(1, min(len(sources), os.cpu_count() or 1))
+    with ThreadPoolExecutor(max_workers=workers) as pool:
+        list(pool.map(lambda so: _compile(so[0], so[1], verbose), zip(sources, objs)))
+    tmp = LIB + ".tmp"
+    cmd = [hipcc(), *HIPCC_FLAGS, "-shared", "-o", tmp, *objs]
+    if verbose:
+        print(" ".join(cmd), flush=True)
+    res = subprocess.run(cmd, capture_output=True, text=True)
+    if res.returncode != 0:
+        sys.stderr.write(res.stdout + res.stderr)
+        raise RuntimeError(f"hipcc link failed with exit code {res.returncode}")
     os.replace(tmp, LIB)
     return LIB
 

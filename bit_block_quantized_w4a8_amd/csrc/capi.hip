@@ -79,7 +79,7 @@ int check_linear_args(const uint16_t* x, const uint8_t* pw, const uint16_t* ws, 
   W4A8_REQUIRE(x && pw && ws, "null input pointer");
   int rc = check_shape(M, K, N, max_m);
   if (rc != W4A8_OK) return rc;
-  W4A8_REQUIRE(aligned(x, 8), "x must be 8-byte aligned");
+  W4A8_REQUIRE(aligned(x, 16), "x must be 16-byte aligned");
   W4A8_REQUIRE(aligned(pw, 16), "packed_w must be 16-byte aligned");
   W4A8_REQUIRE(aligned(ws, 8), "w_scales must be 8-byte aligned");
   return W4A8_OK;
@@ -229,7 +229,7 @@ int w4a8_quantize_act(const uint16_t* x, int64_t M, int64_t K, int8_t* qx, float
   int rc = check_shape(M, K, 64, int64_t{1} << 24);
   if (rc != W4A8_OK) return rc;
   W4A8_REQUIRE(M * K < (int64_t{1} << 34), "M * K too large");
-  W4A8_REQUIRE(aligned(x, 8) && aligned(qx, 4) && aligned(sx, 4), "misaligned pointer");
+  W4A8_REQUIRE(aligned(x, 16) && aligned(qx, 8) && aligned(sx, 4), "misaligned pointer");
   DeviceState* st = nullptr;
   rc = current_state(&st);
   if (rc != W4A8_OK) return rc;

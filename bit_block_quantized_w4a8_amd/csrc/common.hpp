@@ -47,37 +47,70 @@ __device__ __forceinline__ float half_bits_to_float(uint32_t h) {
   return static_cast<float>(__builtin_bit_cast(_Float16, static_cast<unsigned short>(h)));
 }
 
-// Quantise one 32-element activation block held by 8 consecutive lanes, four
-// consecutive elements per lane (lane % 8 = g holds elements 4g .. 4g+3).
-// Returns the four int8 codes packed little-endian into one dword and writes
+// Quantise one 32-element activation block held by an aligned quad of lanes,
+// eight consecutive elements per lane (lane % 4 = g holds elements 8g .. 8g+7).
+// Returns the eight int8 codes packed little-endian into two dwords and writes
 // the block scale sx = fp32(amax / 127) to *sx_out (0 for an all-zero block).
-// amax is exact (max of exact fp16 -> fp32 widenings, in any order); x / sx is
-// the IEEE division and rintf rounds half to even, so the codes do not depend
-// on the lane or reduction order.
-__device__ __forceinline__ uint32_t quantize4_group8(float x0, float x1, float x2, float x3,
-                                                     float* sx_out) {
-  float a = fmaxf(fmaxf(fabsf(x0), fabsf(x1)), fmaxf(fabsf(x2), fabsf(x3)));
-  a = fmaxf(a, __shfl_xor(a, 1));
-  a = fmaxf(a, __shfl_xor(a, 2));
-  a = fmaxf(a, __shfl_xor(a, 4));
-  const float sx = a / 127.0f;
-  *sx_out = sx;
-  if (!(a > 0.0f)) return 0u;
-  const float lo = -127.0f, hi = 127.0f;
-  const int q0 = static_cast<int>(fminf(fmaxf(__builtin_rintf(x0 / sx), lo), hi));
-  const int q1 = static_cast<int>(fminf(fmaxf(__builtin_rintf(x1 / sx), lo), hi));
-  const int q2 = static_cast<int>(fminf(fmaxf(__builtin_rintf(x2 / sx), lo), hi));
-  const int q3 = static_cast<int>(fminf(fmaxf(__builtin_rintf(x3 / sx), lo), hi));
-  return (static_cast<uint32_t>(q0) & 0xFFu) | ((static_cast<uint32_t>(q1) & 0xFFu) << 8) |
-         ((static_cast<uint32_t>(q2) & 0xFFu) << 16) | (static_cast<uint32_t>(q3) << 24);
+//
+// The codes equal round_half_even(fp32(x / sx)) exactly.  amax is exact (a max
+// of exact fp16 -> fp32 widenings, in any order) and sx is the IEEE division.
+// Each code is first estimated as y = x * rcp(sx): v_rcp_f32 is accurate to
+// 1 ulp, so |y - x/sx| <= |x/sx| * (2^-23 + 2^-24) < 2.5e-5 and the IEEE
+// quotient is within 7.6e-6 of x/sx, since |x/sx| <= 127.5.  Where y is further
+// than kTieWindow = 2^-12 from the nearest k + 1/2, both round to the same
+// integer; otherwise the code is recomputed from the IEEE division.  The
+// recomputation is rare (about 2 * 2^-12 of random inputs), so most elements
+// cost a multiply, a rounding and a compare instead of a division.
+constexpr float kTieWindow = 1.0f / 4096.0f;
+
+// Max over the 4 lanes of an aligned quad (DPP quad permutes, no LDS traffic).
+__device__ __forceinline__ float quad_max(float a) {
+  a = fmaxf(a, __int_as_float(__builtin_amdgcn_mov_dpp(__float_as_int(a), 0xB1, 0xF, 0xF, true)));  // lane ^ 1
+  a = fmaxf(a, __int_as_float(__builtin_amdgcn_mov_dpp(__float_as_int(a), 0x4E, 0xF, 0xF, true)));  // lane ^ 2
+  return a;
 }
 
-// The four fp16 values of an 8-byte load, widened to fp32 (exact).
-__device__ __forceinline__ void unpack_half4(uint2 v, float* x) {
-  x[0] = half_bits_to_float(v.x & 0xFFFFu);
-  x[1] = half_bits_to_float(v.x >> 16);
-  x[2] = half_bits_to_float(v.y & 0xFFFFu);
-  x[3] = half_bits_to_float(v.y >> 16);
+__device__ __forceinline__ uint2 quantize8_group4(const float* x, float* sx_out) {
+  float a = 0.0f;
+#pragma unroll
+  for (int i = 0; i < 8; ++i) a = fmaxf(a, fabsf(x[i]));
+  a = quad_max(a);
+  const float sx = a / 127.0f;
+  *sx_out = sx;
+  if (!(a > 0.0f)) return make_uint2(0u, 0u);
+  const float r = __builtin_amdgcn_rcpf(sx);
+  float q[8];
+  bool near_tie = false;
+#pragma unroll
+  for (int i = 0; i < 8; ++i) {
+    const float y = x[i] * r;
+    q[i] = __builtin_rintf(y);
+    near_tie |= fabsf(y - q[i]) >= 0.5f - kTieWindow;
+  }
+  if (near_tie) {
+#pragma unroll
+    for (int i = 0; i < 8; ++i) {
+      const float y = x[i] * r;
+      if (fabsf(y - q[i]) >= 0.5f - kTieWindow) q[i] = __builtin_rintf(x[i] / sx);
+    }
+  }
+  uint32_t packed[2] = {0u, 0u};
+#pragma unroll
+  for (int i = 0; i < 8; ++i) {
+    const float c = fminf(fmaxf(q[i], -127.0f), 127.0f);
+    packed[i >> 2] |= (static_cast<uint32_t>(static_cast<int>(c)) & 0xFFu) << (8 * (i & 3));
+  }
+  return make_uint2(packed[0], packed[1]);
+}
+
+// The eight fp16 values of a 16-byte load, widened to fp32 (exact).
+__device__ __forceinline__ void unpack_half8(uint4 v, float* x) {
+  const uint32_t w[4] = {v.x, v.y, v.z, v.w};
+#pragma unroll
+  for (int i = 0; i < 4; ++i) {
+    x[2 * i] = half_bits_to_float(w[i] & 0xFFFFu);
+    x[2 * i + 1] = half_bits_to_float(w[i] >> 16);
+  }
 }
 
 // int4 nibbles -> int8 bytes holding 16 * value (two's complement nibble moved

@@ -38,6 +38,53 @@ namespace {
 typedef int v4i __attribute__((ext_vector_type(4)));
 typedef int v16i __attribute__((ext_vector_type(16)));
 
+// Per-block operands of one wave, loaded one block ahead of their use.
+template <int TN, int TM>
+struct Operands {
+  uint2 a[TN];      // 8 packed weight bytes of this lane's column and half
+  uint2 s[TN][4];   // 16 fp16 weight scales of this lane's 16 result rows
+  v4i b[TM];        // 16 staged activation codes
+  float sx[TM];     // activation block scale of this lane's token
+};
+
+// Loads are unconditional, with column indices clamped into range (results of
+// out-of-range columns are never stored): the compiler can then count the
+// loads in flight and wait only for the current block, not for the prefetch.
+template <int TN, int TM, int MODE>
+__device__ __forceinline__ void load_operands(Operands<TN, TM>& o, const uint8_t* __restrict__ pw,
+                                              const uint16_t* __restrict__ ws,
+                                              const uint8_t* __restrict__ qxs,
+                                              const float* __restrict__ sxs, int b, int N, int M_pad,
+                                              int n_base, int m_base, int h, int l32) {
+#pragma unroll
+  for (int i = 0; i < TN; ++i) {
+    const int n = min(n_base + 32 * i + l32, N - 1);
+    o.a[i] = *reinterpret_cast<const uint2*>(pw + (static_cast<int64_t>(b) * N + n) * kPackedBytes + 8 * h);
+    if (MODE != 1) {
+#pragma unroll
+      for (int q = 0; q < 4; ++q) {
+        const int nq = min(n_base + 32 * i + 8 * q + 4 * h, N - 4);
+        o.s[i][q] = *reinterpret_cast<const uint2*>(ws + static_cast<int64_t>(b) * N + nq);
+      }
+    }
+  }
+#pragma unroll
+  for (int j = 0; j < TM; ++j) {
+    const int64_t row = static_cast<int64_t>(b) * M_pad + m_base + 32 * j + l32;
+    o.b[j] = *reinterpret_cast<const v4i*>(qxs + row * kBlock + 16 * h);
+    o.sx[j] = sxs[row];
+  }
+}
+
+__device__ __forceinline__ void store_agent(float* p, float v) {
+  __hip_atomic_store(reinterpret_cast<uint32_t*>(p), __float_as_uint(v), __ATOMIC_RELAXED,
+                     __HIP_MEMORY_SCOPE_AGENT);
+}
+__device__ __forceinline__ float load_agent(const float* p) {
+  return __uint_as_float(__hip_atomic_load(reinterpret_cast<uint32_t*>(const_cast<float*>(p)),
+                                           __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT));
+}
+
 template <int TN, int TM, int WAVES_M, int MODE>
 __global__ __launch_bounds__(256) void gemm_kernel(
     const uint8_t* __restrict__ pw, const uint16_t* __restrict__ ws, const uint8_t* __restrict__ qxs,
@@ -81,47 +128,23 @@ __global__ __launch_bounds__(256) void gemm_kernel(
 #pragma unroll
       for (int r = 0; r < 16; ++r) acc[i][j][r] = 0.0f;
 
-  for (int b = b_begin; b < b_end; ++b) {
-    uint2 araw[TN];
-    uint2 sraw[TN][4];
-    v4i bfrag[TM];
-    float sxv[TM];
-#pragma unroll
-    for (int i = 0; i < TN; ++i) {
-      const int n = n_base + 32 * i + l32;
-      araw[i] = n < N ? *reinterpret_cast<const uint2*>(pw + (static_cast<int64_t>(b) * N + n) * kPackedBytes + 8 * h)
-                      : make_uint2(0u, 0u);
-#pragma unroll
-      for (int q = 0; q < 4; ++q) {
-        const int nq = n_base + 32 * i + 8 * q + 4 * h;
-        sraw[i][q] = (MODE != 1 && nq < N) ? *reinterpret_cast<const uint2*>(ws + static_cast<int64_t>(b) * N + nq)
-                            : make_uint2(0u, 0u);
-      }
-    }
-#pragma unroll
-    for (int j = 0; j < TM; ++j) {
-      const int m = m_base + 32 * j + l32;
-      const int64_t row = static_cast<int64_t>(b) * M_pad + m;
-      bfrag[j] = *reinterpret_cast<const v4i*>(qxs + row * kBlock + 16 * h);
-      sxv[j] = sxs[row];
-    }
-
+  // Two operand buffers in ping-pong: while one block is multiplied and
+  // scaled, the loads of the next block are in flight.
+  auto step = [&](const Operands<TN, TM>& cur, int b) {
     v4i afrag[TN];
 #pragma unroll
     for (int i = 0; i < TN; ++i) {
-      afrag[i][0] = static_cast<int>(low_nibbles_x16(araw[i].x));
-      afrag[i][1] = static_cast<int>(low_nibbles_x16(araw[i].y));
-      afrag[i][2] = static_cast<int>(high_nibbles_x16(araw[i].x));
-      afrag[i][3] = static_cast<int>(high_nibbles_x16(araw[i].y));
+      afrag[i][0] = static_cast<int>(low_nibbles_x16(cur.a[i].x));
+      afrag[i][1] = static_cast<int>(low_nibbles_x16(cur.a[i].y));
+      afrag[i][2] = static_cast<int>(high_nibbles_x16(cur.a[i].x));
+      afrag[i][3] = static_cast<int>(high_nibbles_x16(cur.a[i].y));
     }
-
     v16i d[TN][TM];
 #pragma unroll
     for (int i = 0; i < TN; ++i)
 #pragma unroll
       for (int j = 0; j < TM; ++j)
-        d[i][j] = __builtin_amdgcn_mfma_i32_32x32x32_i8(afrag[i], bfrag[j], magic, 0, 0, 0);
-
+        d[i][j] = __builtin_amdgcn_mfma_i32_32x32x32_i8(afrag[i], cur.b[j], magic, 0, 0, 0);
     if (MODE == 1) {
 #pragma unroll
       for (int i = 0; i < TN; ++i)
@@ -135,13 +158,12 @@ __global__ __launch_bounds__(256) void gemm_kernel(
               sums[(static_cast<int64_t>(m) * N + n) * nb + b] = (d[i][j][r] - kMagicBits) >> 4;
           }
         }
-      continue;
+      return;
     }
-
     float sxq[TM], cx[TM];
 #pragma unroll
     for (int j = 0; j < TM; ++j) {
-      sxq[j] = __uint_as_float(__float_as_uint(sxv[j]) & 0xFFFFFFFCu) * 0.0625f;
+      sxq[j] = __uint_as_float(__float_as_uint(cur.sx[j]) & 0xFFFFFFFCu) * 0.0625f;
       cx[j] = sxq[j] * -kMagic;
     }
 #pragma unroll
@@ -150,16 +172,38 @@ __global__ __launch_bounds__(256) void gemm_kernel(
       for (int j = 0; j < TM; ++j)
 #pragma unroll
         for (int r = 0; r < 16; ++r) {
-          const uint32_t word = (r & 2) ? sraw[i][r / 4].y : sraw[i][r / 4].x;
+          const uint32_t word = (r & 2) ? cur.s[i][r / 4].y : cur.s[i][r / 4].x;
           const float sw = half_bits_to_float((r & 1) ? (word >> 16) : (word & 0xFFFFu));
           const float t = fmaf(__int_as_float(d[i][j][r]), sxq[j], cx[j]);
           acc[i][j][r] = fmaf(t, sw, acc[i][j][r]);
         }
+  };
+
+  if (b_begin < b_end) {
+    const int last = b_end - 1;
+    Operands<TN, TM> buf0, buf1;
+    load_operands<TN, TM, MODE>(buf0, pw, ws, qxs, sxs, b_begin, N, M_pad, n_base, m_base, h, l32);
+    // sched_barrier keeps each prefetch issued before the step that hides it
+    // (left alone, the scheduler sinks the loads below the arithmetic).
+    for (int b = b_begin; b < b_end; b += 2) {
+      load_operands<TN, TM, MODE>(buf1, pw, ws, qxs, sxs, min(b + 1, last), N, M_pad, n_base, m_base, h, l32);
+      __builtin_amdgcn_sched_barrier(0);
+      step(buf0, b);
+      __builtin_amdgcn_sched_barrier(0);
+      load_operands<TN, TM, MODE>(buf0, pw, ws, qxs, sxs, min(b + 2, last), N, M_pad, n_base, m_base, h, l32);
+      __builtin_amdgcn_sched_barrier(0);
+      if (b + 1 < b_end) step(buf1, b + 1);
+      __builtin_amdgcn_sched_barrier(0);
+    }
   }
 
   if (MODE == 1) return;
 
   if (ksplit > 1) {
+    // Partial tiles meet in library scratch.  Every access to it and to the
+    // ticket is a device-scope atomic, so no cache-wide fence is needed; the
+    // explicit wait makes each lane's partial stores complete before the
+    // workgroup takes its ticket.
     __shared__ int last_flag;
 #pragma unroll
     for (int i = 0; i < TN; ++i)
@@ -167,38 +211,33 @@ __global__ __launch_bounds__(256) void gemm_kernel(
       for (int j = 0; j < TM; ++j) {
         const int m = m_base + 32 * j + l32;
 #pragma unroll
-        for (int q = 0; q < 4; ++q) {
-          const int n = n_base + 32 * i + 8 * q + 4 * h;
-          if (m < M && n < N)
-            *reinterpret_cast<float4*>(partials + (static_cast<int64_t>(split) * M + m) * N + n) =
-                make_float4(acc[i][j][4 * q], acc[i][j][4 * q + 1], acc[i][j][4 * q + 2], acc[i][j][4 * q + 3]);
+        for (int r = 0; r < 16; ++r) {
+          const int n = n_base + 32 * i + 8 * (r / 4) + 4 * h + (r % 4);
+          if (m < M && n < N) store_agent(partials + (static_cast<int64_t>(split) * M + m) * N + n, acc[i][j][r]);
         }
       }
-    __threadfence();
+    __builtin_amdgcn_s_waitcnt(0);
     __syncthreads();
-    if (threadIdx.x == 0) last_flag = (atomicAdd(&tickets[1 + id], 1u) == static_cast<uint32_t>(ksplit - 1));
+    if (threadIdx.x == 0)
+      last_flag = __hip_atomic_fetch_add(&tickets[1 + id], 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) ==
+                  static_cast<uint32_t>(ksplit - 1);
     __syncthreads();
     if (!last_flag) return;
-    __threadfence();
 #pragma unroll
     for (int i = 0; i < TN; ++i)
 #pragma unroll
       for (int j = 0; j < TM; ++j) {
         const int m = m_base + 32 * j + l32;
 #pragma unroll
-        for (int q = 0; q < 4; ++q) {
-          const int n = n_base + 32 * i + 8 * q + 4 * h;
-          float4 s = make_float4(0.f, 0.f, 0.f, 0.f);
+        for (int r = 0; r < 16; ++r) {
+          const int n = n_base + 32 * i + 8 * (r / 4) + 4 * h + (r % 4);
+          float t = 0.0f;
           if (m < M && n < N)
-            for (int sp = 0; sp < ksplit; ++sp) {
-              const float4 p = *reinterpret_cast<const float4*>(partials + (static_cast<int64_t>(sp) * M + m) * N + n);
-              s.x += p.x; s.y += p.y; s.z += p.z; s.w += p.w;
-            }
-          acc[i][j][4 * q] = s.x; acc[i][j][4 * q + 1] = s.y;
-          acc[i][j][4 * q + 2] = s.z; acc[i][j][4 * q + 3] = s.w;
+            for (int sp = 0; sp < ksplit; ++sp) t += load_agent(partials + (static_cast<int64_t>(sp) * M + m) * N + n);
+          acc[i][j][r] = t;
         }
       }
-    if (threadIdx.x == 0) atomicExch(&tickets[1 + id], 0u);
+    if (threadIdx.x == 0) __hip_atomic_store(&tickets[1 + id], 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
   }
 
 #pragma unroll
@@ -223,21 +262,38 @@ struct Plan {
   int ksplit, bps;
 };
 
-Plan plan_gemm(int M, int K, int N) {
+Plan make_plan(int tn, int tm, int waves_m, int M, int N) {
   Plan p{};
-  if (M <= 32) { p.tn = 1; p.tm = 1; p.waves_m = 1; }
-  else if (M <= 64) { p.tn = 2; p.tm = 1; p.waves_m = 2; }
-  else { p.tn = 2; p.tm = 2; p.waves_m = 2; }
-  p.wg_n = 32 * p.tn * (4 / p.waves_m);
-  p.wg_m = 32 * p.tm * p.waves_m;
+  p.tn = tn;
+  p.tm = tm;
+  p.waves_m = waves_m;
+  p.wg_n = 32 * tn * (4 / waves_m);
+  p.wg_m = 32 * tm * waves_m;
   p.tiles_n = (N + p.wg_n - 1) / p.wg_n;
   p.tiles_m = (M + p.wg_m - 1) / p.wg_m;
   p.m_pad = p.tiles_m * p.wg_m;
+  return p;
+}
+
+// Largest tile that still yields a full wave of workgroups; split K only when
+// even the smallest tile leaves CUs idle (split partials cost HBM traffic).
+Plan plan_gemm(int M, int K, int N) {
+  constexpr int kFull = 256;
+  Plan p;
+  if (M <= 32) {
+    p = make_plan(1, 1, 1, M, N);
+  } else if (M <= 64) {
+    p = make_plan(2, 1, 2, M, N);
+    if (p.tiles_n * p.tiles_m < kFull) p = make_plan(1, 1, 2, M, N);
+  } else {
+    p = make_plan(2, 2, 2, M, N);
+    if (p.tiles_n * p.tiles_m < kFull) p = make_plan(1, 2, 2, M, N);
+    if (p.tiles_n * p.tiles_m < kFull) p = make_plan(1, 1, 2, M, N);
+  }
   const int nb = K / kBlock;
   const int tiles = p.tiles_n * p.tiles_m;
-  constexpr int kTargetGroups = 512;
   constexpr int kMinBlocksPerSplit = 8;
-  int ks = (kTargetGroups + tiles - 1) / tiles;
+  int ks = (kFull + tiles - 1) / tiles;
   const int ks_max = nb / kMinBlocksPerSplit;
   if (ks > ks_max) ks = ks_max;
   if (ks < 1) ks = 1;
@@ -279,12 +335,16 @@ int launch_gemm(const GemmArgs& a, int mode, hipStream_t stream) {
                      partials, sc->tickets)
   if (mode == 1) {
     if (p.waves_m == 1) W4A8_GEMM_LAUNCH(1, 1, 1, 1);
-    else if (p.tm == 1) W4A8_GEMM_LAUNCH(2, 1, 2, 1);
-    else W4A8_GEMM_LAUNCH(2, 2, 2, 1);
+    else if (p.tn == 2 && p.tm == 2) W4A8_GEMM_LAUNCH(2, 2, 2, 1);
+    else if (p.tn == 2) W4A8_GEMM_LAUNCH(2, 1, 2, 1);
+    else if (p.tm == 2) W4A8_GEMM_LAUNCH(1, 2, 2, 1);
+    else W4A8_GEMM_LAUNCH(1, 1, 2, 1);
   } else {
     if (p.waves_m == 1) W4A8_GEMM_LAUNCH(1, 1, 1, 0);
-    else if (p.tm == 1) W4A8_GEMM_LAUNCH(2, 1, 2, 0);
-    else W4A8_GEMM_LAUNCH(2, 2, 2, 0);
+    else if (p.tn == 2 && p.tm == 2) W4A8_GEMM_LAUNCH(2, 2, 2, 0);
+    else if (p.tn == 2) W4A8_GEMM_LAUNCH(2, 1, 2, 0);
+    else if (p.tm == 2) W4A8_GEMM_LAUNCH(1, 2, 2, 0);
+    else W4A8_GEMM_LAUNCH(1, 1, 2, 0);
   }
 #undef W4A8_GEMM_LAUNCH
   W4A8_HIP(hipGetLastError());

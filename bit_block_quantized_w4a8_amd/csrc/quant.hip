@@ -47,28 +47,28 @@ int launch_pack(const int8_t* q, const uint16_t* s, int K, int N, uint8_t* packe
 }
 
 // -------------------------------------------------------- quantiser export
-// Thread t quantises elements 4g .. 4g+3 of block b of row m, with 8
-// consecutive threads per block (K/4 is a multiple of 8, so the groups of 8
-// are lane-aligned and whole groups are in or out of range together).
+// Thread t quantises elements 8g .. 8g+7 of block b of row m, with 4
+// consecutive threads per block (K/8 is a multiple of 4, so the groups of 4 are
+// lane-aligned and whole groups are in or out of range together).
 __global__ __launch_bounds__(256) void quantize_export_kernel(const uint16_t* __restrict__ x, int M,
                                                               int K, int8_t* __restrict__ qx,
                                                               float* __restrict__ sx) {
-  const int64_t per_row = K / 4;
+  const int64_t per_row = K / 8;
   const int64_t t = static_cast<int64_t>(blockIdx.x) * blockDim.x + threadIdx.x;
   if (t >= per_row * M) return;
   const int64_t m = t / per_row;
-  const int64_t e = t % per_row;  // dword index within the row
-  float v[4];
-  unpack_half4(*reinterpret_cast<const uint2*>(x + m * K + 4 * e), v);
+  const int64_t e = t % per_row;  // 8-element group index within the row
+  float v[8];
+  unpack_half8(*reinterpret_cast<const uint4*>(x + m * K + 8 * e), v);
   float scale;
-  const uint32_t codes = quantize4_group8(v[0], v[1], v[2], v[3], &scale);
-  *reinterpret_cast<uint32_t*>(qx + m * K + 4 * e) = codes;
-  if ((e & 7) == 0) sx[m * (K / kBlock) + e / 8] = scale;
+  const uint2 codes = quantize8_group4(v, &scale);
+  *reinterpret_cast<uint2*>(qx + m * K + 8 * e) = codes;
+  if ((e & 3) == 0) sx[m * (K / kBlock) + e / 4] = scale;
 }
 
 int launch_quantize_export(const uint16_t* x, int M, int K, int8_t* qx, float* sx,
                            hipStream_t stream) {
-  const int64_t total = static_cast<int64_t>(M) * (K / 4);
+  const int64_t total = static_cast<int64_t>(M) * (K / 8);
   const int64_t grid = (total + 255) / 256;
   hipLaunchKernelGGL(quantize_export_kernel, dim3(static_cast<unsigned>(grid)), dim3(256), 0, stream,
                      x, M, K, qx, sx);
@@ -84,31 +84,30 @@ int launch_quantize_export(const uint16_t* x, int M, int K, int8_t* qx, float* s
 //       the weight nibbles unpack, see gemm.hip);
 //   sxs [K/32][M_pad] fp32 block scales.
 // Rows M .. M_pad-1 are written as zeros (codes and scales).
-// Group lane g holds elements 4g .. 4g+3, which land in dword (g with bits 1 and
-// 2 swapped): 0,1,4,5,2,3,6,7.
+// Group lane g holds elements 8g .. 8g+7, which land at byte 8 * (0, 2, 1, 3)[g].
 __global__ __launch_bounds__(256) void quantize_stage_kernel(const uint16_t* __restrict__ x, int M,
                                                              int M_pad, int K,
                                                              uint8_t* __restrict__ qxs,
                                                              float* __restrict__ sxs) {
-  const int64_t per_row = K / 4;
+  const int64_t per_row = K / 8;
   const int64_t t = static_cast<int64_t>(blockIdx.x) * blockDim.x + threadIdx.x;
   if (t >= per_row * M_pad) return;
   const int64_t m = t / per_row;
   const int64_t e = t % per_row;
-  const int64_t b = e / 8;
-  const int g = static_cast<int>(e & 7);
-  float v[4] = {0.f, 0.f, 0.f, 0.f};
-  if (m < M) unpack_half4(*reinterpret_cast<const uint2*>(x + m * K + 4 * e), v);
+  const int64_t b = e / 4;
+  const int g = static_cast<int>(e & 3);
+  float v[8] = {0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f};
+  if (m < M) unpack_half8(*reinterpret_cast<const uint4*>(x + m * K + 8 * e), v);
   float scale;
-  const uint32_t codes = quantize4_group8(v[0], v[1], v[2], v[3], &scale);
-  const int d = (g & 1) | ((g & 2) << 1) | ((g & 4) >> 1);
-  *reinterpret_cast<uint32_t*>(qxs + (b * M_pad + m) * kBlock + 4 * d) = codes;
+  const uint2 codes = quantize8_group4(v, &scale);
+  const int off = 8 * (((g & 1) << 1) | (g >> 1));
+  *reinterpret_cast<uint2*>(qxs + (b * M_pad + m) * kBlock + off) = codes;
   if (g == 0) sxs[b * M_pad + m] = scale;
 }
 
 int launch_quantize_stage(const uint16_t* x, int M, int M_pad, int K, uint8_t* qxs, float* sxs,
                           hipStream_t stream) {
-  const int64_t total = static_cast<int64_t>(M_pad) * (K / 4);
+  const int64_t total = static_cast<int64_t>(M_pad) * (K / 8);
   const int64_t grid = (total + 255) / 256;
   hipLaunchKernelGGL(quantize_stage_kernel, dim3(static_cast<unsigned>(grid)), dim3(256), 0, stream,
                      x, M, M_pad, K, qxs, sxs);

@@ -84,7 +84,7 @@ W4A8_API int w4a8_pack_weights(const int8_t* q, const uint16_t* s, int64_t K, in
 
 /*
  * out = W4A8 linear of x (see the header comment), fp32 [M][N], 16-byte aligned.
- *   x         fp16 [M][K], 8-byte aligned
+ *   x         fp16 [M][K], 16-byte aligned
  *   packed_w, w_scales as produced by w4a8_pack_weights (16- and 8-byte aligned)
  * Stage choice: M <= w4a8_gemv_max_m() runs the decode GEMV, which quantises
  * the activations inside the kernel; larger M runs a quantise pre-pass into
@@ -111,7 +111,7 @@ W4A8_API int w4a8_linear_argmax(const uint16_t* x, const uint8_t* packed_w, cons
 
 /*
  * Verification export: the in-kernel activation quantiser run on its own.
- *   x 8-byte aligned; qx int8 [M][K] and sx fp32 [M][K/32], 4-byte aligned
+ *   x 16-byte aligned; qx int8 [M][K] 8-byte and sx fp32 [M][K/32] 4-byte aligned
  *   (the same device function the GEMV and the GEMM pre-pass use)
  */
 W4A8_API int w4a8_quantize_act(const uint16_t* x, int64_t M, int64_t K, int8_t* qx, float* sx,
