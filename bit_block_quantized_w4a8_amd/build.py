@@ -24,6 +24,9 @@ HIPCC_FLAGS = [
     "-fvisibility=hidden",
     # packed fp32 VALU instructions are kept out of every kernel
     "-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops",
+    # MFMA results in ordinary VGPRs: the fp32 epilogue reads every element,
+    # and results left in AGPRs would cost one extra copy instruction each
+    "-mllvm", "-amdgpu-mfma-vgpr-form=1",
     "-Wno-unused-command-line-argument",
 ]
 

@@ -81,7 +81,7 @@ int check_linear_args(const uint16_t* x, const uint8_t* pw, const uint16_t* ws, 
   if (rc != W4A8_OK) return rc;
   W4A8_REQUIRE(aligned(x, 16), "x must be 16-byte aligned");
   W4A8_REQUIRE(aligned(pw, 16), "packed_w must be 16-byte aligned");
-  W4A8_REQUIRE(aligned(ws, 8), "w_scales must be 8-byte aligned");
+  W4A8_REQUIRE(aligned(ws, 16), "w_scales must be 16-byte aligned");
   return W4A8_OK;
 }
 

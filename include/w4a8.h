@@ -85,7 +85,7 @@ W4A8_API int w4a8_pack_weights(const int8_t* q, const uint16_t* s, int64_t K, in
 /*
  * out = W4A8 linear of x (see the header comment), fp32 [M][N], 16-byte aligned.
  *   x         fp16 [M][K], 16-byte aligned
- *   packed_w, w_scales as produced by w4a8_pack_weights (16- and 8-byte aligned)
+ *   packed_w, w_scales as produced by w4a8_pack_weights, both 16-byte aligned
  * Stage choice: M <= w4a8_gemv_max_m() runs the decode GEMV, which quantises
  * the activations inside the kernel; larger M runs a quantise pre-pass into
  * library scratch followed by the int8-MFMA prefill GEMM.

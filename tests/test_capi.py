@@ -34,7 +34,8 @@ def _linear(lib, x=ALIGNED, pw=ALIGNED, ws=ALIGNED, m=1, k=64, n=128, out=ALIGNE
 @pytest.mark.parametrize("kw", [
     dict(x=0), dict(pw=0), dict(ws=0), dict(out=0),
     dict(m=0), dict(m=-3), dict(k=0), dict(k=48), dict(k=16), dict(n=0), dict(n=96), dict(n=32),
-    dict(x=ALIGNED + 2), dict(x=ALIGNED + 8), dict(pw=ALIGNED + 8), dict(ws=ALIGNED + 2), dict(out=ALIGNED + 4),
+    dict(x=ALIGNED + 2), dict(x=ALIGNED + 8), dict(pw=ALIGNED + 8), dict(ws=ALIGNED + 2), dict(ws=ALIGNED + 8),
+    dict(out=ALIGNED + 4),
     dict(path=3), dict(path=-1),
 ])
 def test_linear_rejects_bad_arguments(lib, kw):
