@@ -10,8 +10,10 @@ bytes of one layer / time of one layer, in GB/s; a step is one such layer.
 Also reported, each on its own keys: the prefill stage (the same projections at
 M = 512 with outlier channels, int8 TOPS against the int8 MFMA peak), the
 decode-batch sweep on K = 4096, N = 14336 at M in {1, 4, 8, 16} for both
-kernels, the roofline of the dominant kernel (the gate_up GEMV) and the CPU
-oracle timed on the host.
+kernels, the end-to-end token loop (26 layers + a 262144-entry LM head with
+the fused argmax, 512-token prefill, 128 decode steps with a host sync every
+token; stream-ordered and replayed from a HIP graph), the roofline of the
+dominant kernel (the gate_up GEMV) and the CPU oracle timed on the host.
 
 Timing: launches are queued behind a GPU sleep so the device runs them back to
 back, and two HIP events (torch.cuda.Event, recorded on the stream every
@@ -50,6 +52,8 @@ def parse():
     ap.add_argument("--skip-prefill", action="store_true")
     ap.add_argument("--skip-wide", action="store_true")
     ap.add_argument("--skip-cpu", action="store_true")
+    ap.add_argument("--skip-e2e", action="store_true")
+    ap.add_argument("--decode-steps", type=int, default=128)
     ap.add_argument("--cpu-seconds", type=float, default=10.0, help="CPU oracle sample budget")
     return ap.parse_args()
 
@@ -187,6 +191,106 @@ def bench_wide(w4, torch, synth, timer, iters):
     return {"K": k, "N": n, "replicas": r, "results": res}
 
 
+E2E_EPS = 1e-6
+E2E_SCALE = 0.01
+
+
+def bench_e2e(w4, torch, synth, timer, decode_steps):
+    """The pages' LLM benchmark setup on synthetic weights: 26 decoder layers of the decode
+    projections + a 2048 -> 262144 LM head, 512-token prefill, then `decode_steps` tokens, each
+    ending in the fused argmax whose index is read back on the host (sync every token)."""
+    dev = torch.device("cuda:0")
+    n_layers = synth.N_LAYERS_E2E
+    layers = []
+    for layer in range(n_layers):
+        hw = synth.e2e_layer_weights(layer)
+        layers.append({p: w4.Weights.pack(torch.from_numpy(qw).to(dev), torch.from_numpy(sw).to(dev))
+                       for p, (qw, sw) in hw.items()})
+        del hw
+    qh, sh = synth.e2e_head_weights()
+    head = w4.Weights.pack(torch.from_numpy(qh).to(dev), torch.from_numpy(sh).to(dev))
+    del qh, sh
+    torch.cuda.synchronize()
+    h = synth.LM_HEAD_SHAPE[0]
+    token_bytes = sum(algorithmic_bytes(1, k, n) for k, n in synth.LAYER_SHAPES.values()) * n_layers \
+        + algorithmic_bytes(1, *synth.LM_HEAD_SHAPE)
+
+    def run_layers(x, ws):
+        for lw in layers:
+            w4.decoder_layer(x, lw["qkv"], lw["o"], lw["gate_up"], lw["down"], E2E_SCALE, E2E_EPS, ws)
+
+    # Prefill: 512 rows through the GEMM path of every layer.
+    x_pre = torch.from_numpy(synth.e2e_prompt()).to(dev).float()
+    ws_pre = torch.empty(w4.decoder_layer_workspace(x_pre.shape[0], h, layers[0]["qkv"], layers[0]["gate_up"]),
+                         dtype=torch.uint8, device=dev)
+    run_layers(x_pre.clone(), ws_pre)                      # warm-up (grows library scratch)
+    torch.cuda.synchronize()
+    t0 = timer.event()
+    run_layers(x_pre, ws_pre)
+    t1 = timer.event()
+    torch.cuda.synchronize()
+    prefill_ms = t0.elapsed_time(t1)
+
+    # Decode: the last prefill row seeds the residual stream.
+    x = x_pre[-1:].clone()
+    ws = torch.empty(w4.decoder_layer_workspace(1, h, layers[0]["qkv"], layers[0]["gate_up"]),
+                     dtype=torch.uint8, device=dev)
+    hbuf = torch.empty((1, h), dtype=torch.float16, device=dev)
+    am = torch.empty((1,), dtype=torch.int32, device=dev)
+
+    def token():
+        run_layers(x, ws)
+        w4.residual_norm_cast(x, eps=E2E_EPS, y=hbuf)
+        w4.linear_argmax(hbuf, head.packed, head.w_scales, argmax=am)
+
+    x_start = x.clone()
+    token()
+    torch.cuda.synchronize()
+
+    def decode(step_fn):
+        x.copy_(x_start)
+        ids = []
+        torch.cuda.synchronize()
+        t_start = time.perf_counter()
+        for _ in range(decode_steps):
+            step_fn()
+            ids.append(int(am.item()))                     # host sync every token
+        return time.perf_counter() - t_start, ids
+
+    stream_s, ids_stream = decode(token)
+
+    graph = torch.cuda.CUDAGraph()
+    side = torch.cuda.Stream()
+    side.wait_stream(torch.cuda.current_stream())
+    with torch.cuda.stream(side):
+        token()                                            # warm-up on the capture stream
+    torch.cuda.current_stream().wait_stream(side)
+    torch.cuda.synchronize()
+    with torch.cuda.graph(graph):
+        token()
+    graph_s, ids_graph = decode(graph.replay)
+
+    tok_s_stream = decode_steps / stream_s
+    tok_s_graph = decode_steps / graph_s
+    ceiling = HBM_PEAK_GBS * 1e9 / token_bytes
+    return {
+        "layers": n_layers, "hidden": h, "vocab": synth.LM_HEAD_SHAPE[1],
+        "prefill_tokens": int(x_pre.shape[0]), "prefill_ms": round(prefill_ms, 3),
+        "prefill_tokens_per_s": round(x_pre.shape[0] / prefill_ms * 1e3, 1),
+        "decode_steps": decode_steps,
+        "decode_tok_s_stream": round(tok_s_stream, 1),
+        "decode_tok_s_graph": round(tok_s_graph, 1),
+        "decode_ms_per_token_graph": round(graph_s / decode_steps * 1e3, 4),
+        "weight_bytes_per_token": token_bytes,
+        "decode_hbm_GB_s_graph": round(token_bytes * tok_s_graph / 1e9, 1),
+        "frac_of_hbm_token_ceiling": round(tok_s_graph / ceiling, 4),
+        "hbm_token_ceiling_tok_s": round(ceiling, 1),
+        "graph_ids_match_stream": ids_graph == ids_stream,
+        "first_ids": ids_stream[:8],
+        "note": "sync every token: the argmax index is copied to the host after each step",
+    }
+
+
 def cpu_baseline(synth, budget_s):
     """The numpy oracle on the decode layer (all four projections, M = 1), repeated to fill the budget."""
     import oracle
@@ -230,6 +334,9 @@ def main():
     wide = None if args.skip_wide else bench_wide(w4, torch, synth, timer, max(10, args.steps // 2))
     if wide:
         print("[bench] decode-batch sweep done", file=sys.stderr, flush=True)
+    e2e = None if args.skip_e2e else bench_e2e(w4, torch, synth, timer, args.decode_steps)
+    if e2e:
+        print(f"[bench] end-to-end done: {e2e['decode_tok_s_graph']} tok/s", file=sys.stderr, flush=True)
     cpu = None if args.skip_cpu else cpu_baseline(synth, args.cpu_seconds)
 
     value = dec["layer_bytes"] / (dec["ms_per_step"] * 1e-3) / 1e9
@@ -259,6 +366,7 @@ def main():
         "decode_per_projection": dec["per_projection"],
         "prefill": pre,
         "decode_batch_sweep": wide,
+        "end_to_end": e2e,
     }
     print(json.dumps(line), flush=True)
 

@@ -21,7 +21,8 @@ import torch
 __all__ = [
     "PATH_AUTO", "PATH_GEMV", "PATH_GEMM", "W4A8Error", "library_path", "load_library",
     "declared_functions", "init", "pack_weights", "linear", "linear_argmax",
-    "quantize_act", "block_sums", "gemv_max_m",
+    "quantize_act", "block_sums", "gemv_max_m", "Weights", "residual_norm_cast",
+    "decoder_layer_workspace", "decoder_layer",
 ]
 
 PATH_AUTO, PATH_GEMV, PATH_GEMM = 0, 1, 2
@@ -30,6 +31,12 @@ W4A8_OK, W4A8_EINVAL, W4A8_EUNSUPPORTED, W4A8_EHIP, W4A8_ENOINIT = 0, -1, -2, -3
 _HERE = os.path.dirname(os.path.abspath(__file__))
 _HEADER = os.path.join(os.path.dirname(_HERE), "include", "w4a8.h")
 _lib = None
+
+
+class _CWeights(ctypes.Structure):
+    """C struct w4a8_weights."""
+    _fields_ = [("packed_w", ctypes.c_void_p), ("w_scales", ctypes.c_void_p),
+                ("K", ctypes.c_int64), ("N", ctypes.c_int64)]
 
 
 class W4A8Error(RuntimeError):
@@ -67,6 +74,12 @@ def load_library() -> ctypes.CDLL:
         "w4a8_quantize_act": ([p, i64, i64, p, p, p], i32),
         "w4a8_block_sums": ([p, p, i64, i64, i64, p, i32, p], i32),
         "w4a8_gemv_max_m": ([], i32),
+        "w4a8_residual_norm_cast": ([p, p, i64, ctypes.c_float, ctypes.c_float, i64, i64, p, p], i32),
+        "w4a8_decoder_layer_workspace": ([i64, i64, ctypes.POINTER(_CWeights), ctypes.POINTER(_CWeights),
+                                          ctypes.POINTER(ctypes.c_size_t)], i32),
+        "w4a8_decoder_layer": ([p, i64, i64, ctypes.POINTER(_CWeights), ctypes.POINTER(_CWeights),
+                                ctypes.POINTER(_CWeights), ctypes.POINTER(_CWeights), ctypes.c_float,
+                                ctypes.c_float, p, ctypes.c_size_t, p], i32),
         "w4a8_last_error": ([], ctypes.c_char_p),
     }
     for name, (args, res) in sig.items():
@@ -212,3 +225,60 @@ def block_sums(x: torch.Tensor, packed: torch.Tensor, path: int = PATH_AUTO) -> 
 
 def gemv_max_m() -> int:
     return int(load_library().w4a8_gemv_max_m())
+
+
+class Weights:
+    """A packed weight matrix (device tensors) and its C descriptor."""
+
+    def __init__(self, packed: torch.Tensor, w_scales: torch.Tensor):
+        k, n = _weights_shape(packed, w_scales)
+        self.packed, self.w_scales, self.K, self.N = packed, w_scales, k, n
+        self.c = _CWeights(packed.data_ptr(), w_scales.data_ptr(), k, n)
+
+    @classmethod
+    def pack(cls, q: torch.Tensor, s: torch.Tensor) -> "Weights":
+        return cls(*pack_weights(q, s))
+
+
+def residual_norm_cast(x: torch.Tensor, d: torch.Tensor | None = None, alpha: float = 0.0,
+                       eps: float = 1e-6, y: torch.Tensor | None = None, want_y: bool = True):
+    """x (fp32 [M][H], in place) += alpha * d[:, :H] if d is given; returns fp16(x / rms(x)) or None."""
+    _need(x, "x", torch.float32, 2)
+    m, h = x.shape
+    ld = 0
+    if d is not None:
+        _need(d, "d", torch.float32, 2)
+        if d.shape[0] != m or d.shape[1] < h:
+            raise ValueError("d must be [M][>= H]")
+        ld = d.shape[1]
+    if want_y and y is None:
+        y = torch.empty((m, h), dtype=torch.float16, device=x.device)
+    elif y is not None:
+        _need(y, "y", torch.float16, 2)
+    _ready(x)
+    _check("w4a8_residual_norm_cast", load_library().w4a8_residual_norm_cast(
+        x.data_ptr(), d.data_ptr() if d is not None else None, ld, alpha, eps, m, h,
+        y.data_ptr() if want_y else None, _stream(x)))
+    return y if want_y else None
+
+
+def decoder_layer_workspace(m: int, h: int, qkv: Weights, gate_up: Weights) -> int:
+    nbytes = ctypes.c_size_t(0)
+    _check("w4a8_decoder_layer_workspace", load_library().w4a8_decoder_layer_workspace(
+        m, h, ctypes.byref(qkv.c), ctypes.byref(gate_up.c), ctypes.byref(nbytes)))
+    return int(nbytes.value)
+
+
+def decoder_layer(x: torch.Tensor, qkv: Weights, o: Weights, gate_up: Weights, down: Weights,
+                  residual_scale: float, eps: float, workspace: torch.Tensor) -> torch.Tensor:
+    """One synthetic decoder layer in place on the fp32 residual stream x [M][H]."""
+    _need(x, "x", torch.float32, 2)
+    if not workspace.is_cuda or not workspace.is_contiguous():
+        raise ValueError("workspace must be a contiguous CUDA tensor")
+    m, h = x.shape
+    _ready(x)
+    _check("w4a8_decoder_layer", load_library().w4a8_decoder_layer(
+        x.data_ptr(), m, h, ctypes.byref(qkv.c), ctypes.byref(o.c), ctypes.byref(gate_up.c),
+        ctypes.byref(down.c), residual_scale, eps, workspace.data_ptr(),
+        workspace.numel() * workspace.element_size(), _stream(x)))
+    return x

@@ -259,6 +259,88 @@ int w4a8_block_sums(const uint16_t* x, const uint8_t* packed_w, int64_t M, int64
   return launch_gemm(a, 1, stream);
 }
 
+int w4a8_residual_norm_cast(float* x, const float* d, int64_t ld_d, float alpha, float eps, int64_t M,
+                            int64_t H, uint16_t* y, hipStream_t stream) {
+  W4A8_REQUIRE(x, "null x");
+  W4A8_REQUIRE(M >= 1 && M <= (int64_t{1} << 20) && H >= 1 && H < (int64_t{1} << 24), "bad shape M=%lld H=%lld",
+               static_cast<long long>(M), static_cast<long long>(H));
+  W4A8_REQUIRE(!d || ld_d >= H, "ld_d must be at least H");
+  W4A8_REQUIRE(eps >= 0.0f, "eps must be non-negative");
+  DeviceState* st = nullptr;
+  int rc = current_state(&st);
+  if (rc != W4A8_OK) return rc;
+  return launch_residual_norm_cast(x, d, ld_d, alpha, eps, static_cast<int>(M), static_cast<int>(H), y, stream);
+}
+
+namespace {
+int check_weights(const w4a8_weights* w, const char* name) {
+  W4A8_REQUIRE(w && w->packed_w && w->w_scales, "%s: null weights", name);
+  W4A8_REQUIRE(aligned(w->packed_w, 16) && aligned(w->w_scales, 16), "%s: weights must be 16-byte aligned", name);
+  return check_shape(1, w->K, w->N, 1);
+}
+}  // namespace
+
+int w4a8_decoder_layer_workspace(int64_t M, int64_t H, const w4a8_weights* qkv, const w4a8_weights* gate_up,
+                                 size_t* bytes) {
+  W4A8_REQUIRE(bytes && qkv && gate_up, "null pointer");
+  W4A8_REQUIRE(M >= 1 && M <= 65536 && H >= 64 && H % 64 == 0 && H < (int64_t{1} << 24), "bad shape");
+  W4A8_REQUIRE(qkv->N >= H && qkv->N < (int64_t{1} << 30) && gate_up->N >= 128 && gate_up->N < (int64_t{1} << 30),
+               "bad weight shapes");
+  *bytes = layer_workspace(static_cast<int>(M), static_cast<int>(H), static_cast<int>(qkv->N),
+                           static_cast<int>(gate_up->N)).bytes;
+  return W4A8_OK;
+}
+
+int w4a8_decoder_layer(float* x, int64_t M, int64_t H, const w4a8_weights* qkv, const w4a8_weights* o,
+                       const w4a8_weights* gate_up, const w4a8_weights* down, float residual_scale, float eps,
+                       void* workspace, size_t workspace_bytes, hipStream_t stream) {
+  W4A8_REQUIRE(x && aligned(x, 16), "x must be a 16-byte aligned pointer");
+  W4A8_REQUIRE(M >= 1 && M <= 65536 && H >= 64 && H % 64 == 0 && H < (int64_t{1} << 24), "bad shape M=%lld H=%lld",
+               static_cast<long long>(M), static_cast<long long>(H));
+  int rc;
+  if ((rc = check_weights(qkv, "qkv")) != W4A8_OK || (rc = check_weights(o, "o")) != W4A8_OK ||
+      (rc = check_weights(gate_up, "gate_up")) != W4A8_OK || (rc = check_weights(down, "down")) != W4A8_OK)
+    return rc;
+  W4A8_REQUIRE(qkv->K == H && qkv->N >= H, "qkv must be H x N with N >= H");
+  W4A8_REQUIRE(o->K == H && o->N == H, "o must be H x H");
+  W4A8_REQUIRE(gate_up->K == H && gate_up->N % 128 == 0 && down->K == gate_up->N / 2 && down->N == H,
+               "gate_up must be H x 2F and down F x H");
+  W4A8_REQUIRE(gate_up->N < (int64_t{1} << 30) && qkv->N < (int64_t{1} << 30), "weights too wide");
+  const LayerWorkspace w = layer_workspace(static_cast<int>(M), static_cast<int>(H), static_cast<int>(qkv->N),
+                                           static_cast<int>(gate_up->N));
+  W4A8_REQUIRE(workspace && aligned(workspace, 256) && workspace_bytes >= w.bytes,
+               "workspace must be 256-byte aligned and hold %zu bytes", w.bytes);
+  DeviceState* st = nullptr;
+  rc = current_state(&st);
+  if (rc != W4A8_OK) return rc;
+
+  char* base = static_cast<char*>(workspace);
+  float* q = reinterpret_cast<float*>(base + w.q);
+  uint16_t* a = reinterpret_cast<uint16_t*>(base + w.a);
+  float* ob = reinterpret_cast<float*>(base + w.o);
+  uint16_t* n = reinterpret_cast<uint16_t*>(base + w.n);
+  float* g = reinterpret_cast<float*>(base + w.g);
+  uint16_t* u = reinterpret_cast<uint16_t*>(base + w.u);
+  float* d = reinterpret_cast<float*>(base + w.d);
+  const int Mi = static_cast<int>(M), Hi = static_cast<int>(H);
+  const int F = static_cast<int>(gate_up->N / 2);
+#define W4A8_STEP(call)              \
+  do {                              \
+    if ((rc = (call)) != W4A8_OK) return rc; \
+  } while (0)
+  W4A8_STEP(launch_residual_norm_cast(x, nullptr, 0, 0.0f, eps, Mi, Hi, n, stream));
+  W4A8_STEP(w4a8_linear(n, qkv->packed_w, qkv->w_scales, M, H, qkv->N, q, stream));
+  W4A8_STEP(launch_cast_rows(q, qkv->N, Mi, Hi, a, stream));
+  W4A8_STEP(w4a8_linear(a, o->packed_w, o->w_scales, M, H, H, ob, stream));
+  W4A8_STEP(launch_residual_norm_cast(x, ob, H, residual_scale, eps, Mi, Hi, n, stream));
+  W4A8_STEP(w4a8_linear(n, gate_up->packed_w, gate_up->w_scales, M, H, gate_up->N, g, stream));
+  W4A8_STEP(launch_gated_cast(g, Mi, F, u, stream));
+  W4A8_STEP(w4a8_linear(u, down->packed_w, down->w_scales, M, F, H, d, stream));
+  W4A8_STEP(launch_residual_norm_cast(x, d, H, residual_scale, eps, Mi, Hi, nullptr, stream));
+#undef W4A8_STEP
+  return W4A8_OK;
+}
+
 int w4a8_gemv_max_m(void) { return gemv_max_m(); }
 
 const char* w4a8_last_error(void) { return g_error; }

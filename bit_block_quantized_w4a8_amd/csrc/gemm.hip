@@ -357,10 +357,11 @@ Plan plan_gemm(int M, int K, int N) {
     if (p.tiles_n * p.tiles_m < kFull) p = make_plan(1, 1, 2, M, N);  // 64 x 64
   }
   // Fewer than two tiles per CU leave too few waves to hide latency: split K
-  // towards four workgroups per CU, keeping at least 16 blocks per split.
+  // towards four workgroups per CU, keeping at least 64 blocks per split (the
+  // partial tiles cost HBM traffic that short splits do not amortise).
   const int nb = K / kBlock;
   const int tiles = p.tiles_n * p.tiles_m;
-  constexpr int kMinBlocksPerSplit = 16;
+  constexpr int kMinBlocksPerSplit = 64;
   constexpr int kTargetGroups = 1024;
   int ks = tiles < 2 * kFull ? (kTargetGroups + tiles - 1) / tiles : 1;
   const int ks_max = nb / kMinBlocksPerSplit;

@@ -44,4 +44,16 @@ size_t gemm_scratch_bytes(int M, int K, int N);
 
 int gemv_max_m();
 
+// Glue of the synthetic decoder layer (layer.hip).
+int launch_residual_norm_cast(float* x, const float* d, int64_t ld_d, float alpha, float eps, int M, int H,
+                              uint16_t* y, hipStream_t stream);
+int launch_cast_rows(const float* src, int64_t ld, int M, int H, uint16_t* dst, hipStream_t stream);
+int launch_gated_cast(const float* g, int M, int F, uint16_t* u, hipStream_t stream);
+
+// Byte offsets of a decoder layer's temporaries inside the caller's workspace.
+struct LayerWorkspace {
+  size_t q, a, o, n, g, u, d, bytes;
+};
+LayerWorkspace layer_workspace(int M, int H, int n_qkv, int n_gu);
+
 }  // namespace w4a8

@@ -1,0 +1,129 @@
+// Synthetic decoder layer around the W4A8 linear: glue kernels and the
+// stream-ordered layer chain.
+//
+// The pages' LLM benchmark runs prefill 512 / decode 128 with argmax sampling
+// and a sync every token (ML Drift explainer on tech.dede.sh, section
+// "Stage-aware optimization for large language models"), and they fuse
+// residual and element-wise work into a normalisation operator (sciencestack
+// summary of the ML Drift paper, Figure 4).  The layer wiring here is this
+// library's stand-in for a transformer layer without attention:
+//
+//   n1 = fp16(x / rms(x));  q = L(n1; Wqkv);  a = fp16(q[:, :H])
+//   o  = L(a; Wo);          x = x + s*o;      n2 = fp16(x / rms(x))
+//   g  = L(n2; Wgu);        u = fp16(g[:, :F] * g[:, F:])
+//   d  = L(u; Wdown);       x = x + s*d
+//
+// with rms(x) = sqrt(mean(x^2) + eps) per row, x an fp32 residual stream and s
+// the residual scale.  The query slice stands in for the attention output.
+#include "kernels.hpp"
+
+namespace w4a8 {
+
+namespace {
+
+constexpr int kGlueThreads = 256;
+
+__device__ __forceinline__ uint16_t float_to_half_bits(float v) {
+  return __builtin_bit_cast(unsigned short, static_cast<_Float16>(v));
+}
+
+// Fixed-order workgroup sum: wave shuffles, then the 4 wave totals in order.
+__device__ __forceinline__ float block_sum(float v, float* red) {
+#pragma unroll
+  for (int off = 32; off >= 1; off >>= 1) v += __shfl_xor(v, off);
+  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+  if (lane == 0) red[wave] = v;
+  __syncthreads();
+  const float t = ((red[0] + red[1]) + red[2]) + red[3];
+  __syncthreads();
+  return t;
+}
+
+// One workgroup per row: optionally x += alpha * d (one fma per element, so
+// x' = RN(x + alpha*d)), then y = fp16(x' * (1 / sqrt(mean(x'^2) + eps))).
+__global__ __launch_bounds__(kGlueThreads) void residual_norm_cast_kernel(
+    float* __restrict__ x, const float* __restrict__ d, int64_t ld_d, float alpha, float eps, int H,
+    uint16_t* __restrict__ y) {
+  __shared__ float red[4];
+  const int64_t m = blockIdx.x;
+  float* xr = x + m * H;
+  float ss = 0.0f;
+  for (int h = threadIdx.x; h < H; h += kGlueThreads) {
+    float v = xr[h];
+    if (d) {
+      v = fmaf(alpha, d[m * ld_d + h], v);
+      xr[h] = v;
+    }
+    ss = fmaf(v, v, ss);
+  }
+  const float inv = 1.0f / sqrtf(block_sum(ss, red) / static_cast<float>(H) + eps);
+  if (y)
+    for (int h = threadIdx.x; h < H; h += kGlueThreads) y[m * H + h] = float_to_half_bits(xr[h] * inv);
+}
+
+// dst[m][h] = fp16(src[m * ld + h]) for h < H.
+__global__ __launch_bounds__(kGlueThreads) void cast_rows_kernel(const float* __restrict__ src, int64_t ld,
+                                                                 int H, uint16_t* __restrict__ dst) {
+  const int64_t m = blockIdx.y;
+  const int h = blockIdx.x * kGlueThreads + threadIdx.x;
+  if (h < H) dst[m * H + h] = float_to_half_bits(src[m * ld + h]);
+}
+
+// u[m][f] = fp16(fp32(g[m][f] * g[m][F + f])) for f < F (rows of g hold 2F values).
+__global__ __launch_bounds__(kGlueThreads) void gated_cast_kernel(const float* __restrict__ g, int F,
+                                                                  uint16_t* __restrict__ u) {
+  const int64_t m = blockIdx.y;
+  const int f = blockIdx.x * kGlueThreads + threadIdx.x;
+  if (f < F) {
+    const float* row = g + m * 2 * static_cast<int64_t>(F);
+    u[m * F + f] = float_to_half_bits(row[f] * row[F + f]);
+  }
+}
+
+size_t align256(size_t v) { return (v + 255) & ~static_cast<size_t>(255); }
+
+}  // namespace
+
+int launch_residual_norm_cast(float* x, const float* d, int64_t ld_d, float alpha, float eps, int M, int H,
+                              uint16_t* y, hipStream_t stream) {
+  hipLaunchKernelGGL(residual_norm_cast_kernel, dim3(M), dim3(kGlueThreads), 0, stream, x, d, ld_d, alpha,
+                     eps, H, y);
+  W4A8_HIP(hipGetLastError());
+  return W4A8_OK;
+}
+
+int launch_cast_rows(const float* src, int64_t ld, int M, int H, uint16_t* dst, hipStream_t stream) {
+  hipLaunchKernelGGL(cast_rows_kernel, dim3((H + kGlueThreads - 1) / kGlueThreads, M), dim3(kGlueThreads), 0,
+                     stream, src, ld, H, dst);
+  W4A8_HIP(hipGetLastError());
+  return W4A8_OK;
+}
+
+int launch_gated_cast(const float* g, int M, int F, uint16_t* u, hipStream_t stream) {
+  hipLaunchKernelGGL(gated_cast_kernel, dim3((F + kGlueThreads - 1) / kGlueThreads, M), dim3(kGlueThreads), 0,
+                     stream, g, F, u);
+  W4A8_HIP(hipGetLastError());
+  return W4A8_OK;
+}
+
+// Workspace carve-up of one decoder layer: q, a, o, n, g, u, d.
+LayerWorkspace layer_workspace(int M, int H, int n_qkv, int n_gu) {
+  LayerWorkspace w{};
+  size_t off = 0;
+  auto take = [&](size_t bytes) {
+    const size_t at = off;
+    off += align256(bytes);
+    return at;
+  };
+  w.q = take(static_cast<size_t>(M) * n_qkv * 4);
+  w.a = take(static_cast<size_t>(M) * H * 2);
+  w.o = take(static_cast<size_t>(M) * H * 4);
+  w.n = take(static_cast<size_t>(M) * H * 2);
+  w.g = take(static_cast<size_t>(M) * n_gu * 4);
+  w.u = take(static_cast<size_t>(M) * (n_gu / 2) * 2);
+  w.d = take(static_cast<size_t>(M) * H * 4);
+  w.bytes = off;
+  return w;
+}
+
+}  // namespace w4a8

@@ -126,6 +126,53 @@ W4A8_API int w4a8_quantize_act(const uint16_t* x, int64_t M, int64_t K, int8_t* 
 W4A8_API int w4a8_block_sums(const uint16_t* x, const uint8_t* packed_w, int64_t M, int64_t K,
                     int64_t N, int32_t* sums, int path, hipStream_t stream);
 
+/* ------------------------------------------------------------------------
+ * Synthetic decoder layer around the linear (the pages' LLM benchmark runs
+ * prefill 512 / decode 128 with argmax sampling and a sync every token: ML
+ * Drift explainer on tech.dede.sh, section "Stage-aware optimization for large
+ * language models").  Layer wiring, with x an fp32 residual stream [M][H],
+ * rms(x) = sqrt(mean(x^2) + eps) per row and s the residual scale:
+ *   n1 = fp16(x / rms(x)); q = L(n1; qkv); a = fp16(q[:, :H]); o = L(a; o)
+ *   x += s*o; n2 = fp16(x / rms(x)); g = L(n2; gate_up)
+ *   u = fp16(g[:, :F] * g[:, F:]) with F = gate_up.N / 2; d = L(u; down); x += s*d
+ * Every L is w4a8_linear (decode GEMV or prefill GEMM by M).
+ * ------------------------------------------------------------------------ */
+
+/* One packed weight matrix as produced by w4a8_pack_weights (device pointers). */
+typedef struct w4a8_weights {
+  const uint8_t* packed_w;   /* uint8 [K/32][N][16], 16-byte aligned */
+  const uint16_t* w_scales;  /* fp16  [K/32][N], 16-byte aligned */
+  int64_t K;
+  int64_t N;
+} w4a8_weights;
+
+/*
+ * Per row m of x (fp32 [M][H]): if d is not NULL, x[m][h] = RN(x[m][h] + alpha *
+ * d[m * ld_d + h]) (one fused multiply-add); then, if y is not NULL,
+ * y[m][h] = fp16(x[m][h] * (1 / sqrt(mean_h x[m][h]^2 + eps))) (fp32 arithmetic).
+ * H >= 1; y fp16 [M][H].
+ */
+W4A8_API int w4a8_residual_norm_cast(float* x, const float* d, int64_t ld_d, float alpha, float eps,
+                                     int64_t M, int64_t H, uint16_t* y, hipStream_t stream);
+
+/* Bytes of caller-owned workspace that w4a8_decoder_layer needs for these shapes. */
+W4A8_API int w4a8_decoder_layer_workspace(int64_t M, int64_t H, const w4a8_weights* qkv,
+                                          const w4a8_weights* gate_up, size_t* bytes);
+
+/*
+ * One decoder layer (wiring above), in place on x (fp32 [M][H], 16-byte aligned).
+ * Shapes: qkv.K = H <= qkv.N; o.K = o.N = H; gate_up.K = H; gate_up.N = 2 * down.K;
+ * down.N = H; H % 64 == 0.  workspace: device memory of at least
+ * w4a8_decoder_layer_workspace bytes, 256-byte aligned, owned by the caller and
+ * not touched by other calls in flight.  Allocates nothing (the linears use the
+ * library scratch as w4a8_linear does), so a warmed-up call can be captured in
+ * a HIP graph.  M must not exceed 65536.
+ */
+W4A8_API int w4a8_decoder_layer(float* x, int64_t M, int64_t H, const w4a8_weights* qkv,
+                                const w4a8_weights* o, const w4a8_weights* gate_up,
+                                const w4a8_weights* down, float residual_scale, float eps,
+                                void* workspace, size_t workspace_bytes, hipStream_t stream);
+
 /* Largest M that W4A8_PATH_AUTO sends to the decode GEMV. */
 W4A8_API int w4a8_gemv_max_m(void);
 

@@ -160,3 +160,65 @@ def argmax_first(logits: np.ndarray) -> np.ndarray:
     v = np.asarray(logits)
     assert np.all(np.isfinite(v))
     return np.argmax(v, axis=-1)
+
+
+# ---------------------------------------------------------------------------
+# Synthetic decoder layer around the linear, for the end-to-end workload (the
+# pages' benchmark: prefill 512 / decode 128, argmax sampling, sync every
+# token -- ML Drift explainer on tech.dede.sh, section "Stage-aware
+# optimization for large language models").  The wiring is this
+# implementation's stand-in for a transformer layer without attention; x is an
+# fp32 residual stream, every linear output is an fp32 tensor:
+#   n1 = fp16(x / rms(x)); q = L(n1; qkv); a = fp16(q[:, :H]); o = L(a; o)
+#   x = x + s*o; n2 = fp16(x / rms(x)); g = L(n2; gate_up)
+#   u = fp16(g[:, :F] * g[:, F:]); d = L(u; down); x = x + s*d
+# ---------------------------------------------------------------------------
+
+def rms_norm_fp16(x32: np.ndarray, eps: float) -> np.ndarray:
+    """fp16(x / sqrt(mean(x^2) + eps)) per row, in fp64 before the one rounding to fp16.
+
+    Pinned by constant rows (closed form), exact power-of-two invariance with
+    eps = 0, and the unit mean square of the result.
+    """
+    xd = np.asarray(x32, dtype=np.float32).astype(np.float64)
+    ms = np.mean(xd * xd, axis=1, keepdims=True)
+    return (xd / np.sqrt(ms + eps)).astype(np.float16)
+
+
+def residual_add(x32: np.ndarray, d32: np.ndarray, alpha: float) -> np.ndarray:
+    """fp32(x + alpha * d) with alpha taken as fp32 and one rounding (an fma).
+
+    Exact in fp64 before the rounding (fp32 x fp32 products and their sums with
+    fp32 values fit in 53 bits here).  Pinned against exact rational arithmetic.
+    """
+    a = np.float64(np.float32(alpha))
+    return (np.asarray(x32, np.float32).astype(np.float64) +
+            a * np.asarray(d32, np.float32).astype(np.float64)).astype(np.float32)
+
+
+def gated_fp16(g32: np.ndarray) -> np.ndarray:
+    """fp16(fp32(g[:, :F] * g[:, F:])) with F = half the row; pinned by a hand example."""
+    g = np.asarray(g32, dtype=np.float32)
+    f = g.shape[1] // 2
+    return (g[:, :f] * g[:, f:]).astype(np.float32).astype(np.float16)
+
+
+def linear_fp32(x16, qw, sw16) -> np.ndarray:
+    """The linear's output as the fp32 tensor it is stored in."""
+    return linear(x16, qw, sw16).astype(np.float32)
+
+
+def decoder_layer(x32: np.ndarray, w: dict, residual_scale: float, eps: float) -> np.ndarray:
+    """One layer of the wiring above; w maps qkv/o/gate_up/down to (qw int8 [N][K], sw fp16)."""
+    x = np.asarray(x32, dtype=np.float32).copy()
+    h = x.shape[1]
+    n1 = rms_norm_fp16(x, eps)
+    q = linear_fp32(n1, *w["qkv"])
+    a = q[:, :h].astype(np.float16)
+    o = linear_fp32(a, *w["o"])
+    x = residual_add(x, o, residual_scale)
+    n2 = rms_norm_fp16(x, eps)
+    g = linear_fp32(n2, *w["gate_up"])
+    u = gated_fp16(g)
+    d = linear_fp32(u, *w["down"])
+    return residual_add(x, d, residual_scale)

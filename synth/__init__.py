@@ -110,3 +110,30 @@ def workload_inputs(name: str, m: int | None = None):
         x = activations(rng(w["seed"], base + 4 + mm), mm, k, ch)
         out[proj] = (x, qw, sw)
     return out
+
+
+def e2e_layer_weights(layer: int) -> dict:
+    """int4 weights and fp16 scales of decoder layer `layer` of the end-to-end workload:
+    {proj: (qw int8 [N][K], sw fp16 [N][K/32])}; tensor ids 64*layer + 2p (+1 for scales)."""
+    seed = WORKLOADS["e2e"]["seed"]
+    out = {}
+    for p, (proj, (k, n)) in enumerate(LAYER_SHAPES.items()):
+        base = 64 * layer + 2 * p
+        out[proj] = (int4_values(rng(seed, base), n, k), weight_scales(rng(seed, base + 1), n, k))
+    return out
+
+
+def e2e_head_weights():
+    """The 2048 -> 262144 LM head of the end-to-end workload (tensor ids 1_000_000, +1)."""
+    seed = WORKLOADS["e2e"]["seed"]
+    k, n = LM_HEAD_SHAPE
+    return int4_values(rng(seed, 1_000_000), n, k), weight_scales(rng(seed, 1_000_001), n, k)
+
+
+def e2e_prompt() -> np.ndarray:
+    """The 512 prefill rows of the end-to-end workload: fp16 N(0,1) with outlier channels
+    (tensor ids 2_000_000 for the activations, 2_000_001 for the channels)."""
+    seed = WORKLOADS["e2e"]["seed"]
+    k = LM_HEAD_SHAPE[0]
+    ch = outlier_channels(rng(seed, 2_000_001), k)
+    return activations(rng(seed, 2_000_000), PREFILL_TOKENS, k, ch)
