@@ -37,6 +37,29 @@ METRIC = "decode GEMV HBM GB/s (% of peak) + prefill M=512 int8 TOPS; synthetic 
 HBM_PEAK_GBS = 8000.0          # MI355X HBM3E
 INT8_PEAK_TOPS = 5000.0        # MI355X dense int8 MFMA (5.0 POP/s)
 REPLICA_BYTES_MIN = 1 << 30    # weight rotation size for cold-cache timing
+TRAFFIC_FILE = os.path.join("profiles", "gemv_gate_up_hbm_traffic.json")
+COPY_BYTES = 256 << 20         # calibration copy for the HBM byte counters
+GEMV_SOURCES = ["gemv_kernel.hpp", "gemv.hip", "common.hpp"]
+
+
+def gemv_source_hash():
+    import hashlib
+    h = hashlib.sha256()
+    for name in GEMV_SOURCES:
+        with open(os.path.join(ROOT, "bit_block_quantized_w4a8_amd", "csrc", name), "rb") as f:
+            h.update(f.read())
+    return h.hexdigest()[:16]
+
+
+def measured_traffic():
+    """HBM bytes per gate_up GEMV launch from the committed counter summary, or None when the
+    GEMV sources changed since the counters were taken."""
+    path = os.path.join(ROOT, TRAFFIC_FILE)
+    if not os.path.exists(path):
+        return None
+    with open(path) as f:
+        t = json.load(f)
+    return t["bytes_per_launch"] if t.get("source_hash") == gemv_source_hash() else None
 
 
 def algorithmic_bytes(m, k, n):
@@ -54,6 +77,10 @@ def parse():
     ap.add_argument("--skip-cpu", action="store_true")
     ap.add_argument("--skip-e2e", action="store_true")
     ap.add_argument("--decode-steps", type=int, default=128)
+    ap.add_argument("--profile-gemv", action="store_true",
+                    help="only run the gate_up GEMV (cold weights) and a 256 MiB copy, for counter runs")
+    ap.add_argument("--summarize-traffic", nargs=2, metavar=("FETCH_CSV", "WRITE_CSV"),
+                    help="turn two rocprofv3 --pmc counter_collection.csv files into " + TRAFFIC_FILE)
     ap.add_argument("--cpu-seconds", type=float, default=10.0, help="CPU oracle sample budget")
     return ap.parse_args()
 
@@ -291,6 +318,71 @@ def bench_e2e(w4, torch, synth, timer, decode_steps):
     }
 
 
+def profile_gemv(w4, torch, synth, launches=40):
+    """Cold-weight launches of the decode gate_up GEMV, then three 256 MiB device copies."""
+    x, qw, sw = synth.workload_inputs("decode")["gate_up"]
+    dev = torch.device("cuda:0")
+    packed, ws = w4.pack_weights(torch.from_numpy(qw).to(dev), torch.from_numpy(sw).to(dev))
+    reps, r = replicas(w4, torch, {"g": (packed, ws)}, algorithmic_bytes(1, qw.shape[1], qw.shape[0]))
+    xd = torch.from_numpy(x).to(dev)
+    out = torch.empty((1, qw.shape[0]), dtype=torch.float32, device=dev)
+    for i in range(launches):
+        w4.linear(xd, *reps["g"][i % r], out=out)
+    src = torch.empty(COPY_BYTES, dtype=torch.uint8, device=dev)
+    dst = torch.empty_like(src)
+    for _ in range(3):
+        dst.copy_(src)
+    torch.cuda.synchronize()
+    print(json.dumps({"profile_gemv": launches, "copies": 3, "copy_bytes": COPY_BYTES}), flush=True)
+
+
+def summarize_traffic(fetch_csv, write_csv):
+    """Median KiB per dispatch of FETCH_SIZE / WRITE_SIZE for the GEMV, scaled by the copy's."""
+    import csv
+    import statistics
+
+    def per_kernel(path, counter):
+        vals = {"gemv": [], "copy": []}
+        with open(path) as f:
+            for row in csv.DictReader(f):
+                if row.get("Counter_Name") != counter:
+                    continue
+                name = row["Kernel_Name"]
+                key = "gemv" if "gemv_kernel" in name else "copy" if "copy" in name.lower() else None
+                if key:
+                    vals[key].append(float(row["Counter_Value"]))
+        # the calibration copies are the three largest copy dispatches (the weight-replica
+        # clones of the same run are copies too, but smaller)
+        vals["copy"] = sorted(vals["copy"])[-3:]
+        return {k: statistics.median(v) for k, v in vals.items() if v}
+
+    fetch = per_kernel(fetch_csv, "FETCH_SIZE")
+    write = per_kernel(write_csv, "WRITE_SIZE")
+    expect_kib = COPY_BYTES / 1024
+    f_factor = fetch["copy"] / expect_kib       # counter KiB per real KiB read
+    w_factor = write["copy"] / expect_kib
+    gemv_bytes = (fetch["gemv"] / f_factor + write["gemv"] / w_factor) * 1024
+    out = {
+        "kernel": "gemv_kernel<1,0,32,8> (decode gate_up 2048x16384, M=1, cold weights)",
+        "fetch_kib_per_launch": fetch["gemv"], "write_kib_per_launch": write["gemv"],
+        "copy_fetch_kib": fetch["copy"], "copy_write_kib": write["copy"], "copy_bytes": COPY_BYTES,
+        "fetch_scale": round(f_factor, 4), "write_scale": round(w_factor, 4),
+        "bytes_per_launch": round(gemv_bytes), "algorithmic_bytes_per_launch": algorithmic_bytes(1, 2048, 16384),
+        "source_hash": gemv_source_hash(),
+        "commands": [
+            "cd /tmp && export TMPDIR=/tmp && rocprofv3 --pmc FETCH_SIZE --output-format csv "
+            "-d /root/repo/gpurun_out/pmc_fetch -o f -- python3 /root/repo/bench.py --profile-gemv",
+            "cd /tmp && export TMPDIR=/tmp && rocprofv3 --pmc WRITE_SIZE --output-format csv "
+            "-d /root/repo/gpurun_out/pmc_write -o w -- python3 /root/repo/bench.py --profile-gemv",
+            "python bench.py --summarize-traffic gpurun_out/pmc_fetch/f_counter_collection.csv "
+            "gpurun_out/pmc_write/w_counter_collection.csv",
+        ],
+    }
+    with open(os.path.join(ROOT, TRAFFIC_FILE), "w") as f:
+        json.dump(out, f, indent=1)
+    print(json.dumps(out))
+
+
 def cpu_baseline(synth, budget_s):
     """The numpy oracle on the decode layer (all four projections, M = 1), repeated to fill the budget."""
     import oracle
@@ -314,6 +406,9 @@ def cpu_baseline(synth, budget_s):
 
 def main():
     args = parse()
+    if args.summarize_traffic:
+        summarize_traffic(*args.summarize_traffic)
+        return
     if args.gpus != 1:
         print(f"bench.py measures one GPU; --gpus {args.gpus} is not supported by this build "
               "(the path shards by output columns with no exchange, see DESIGN.md)", file=sys.stderr)
@@ -325,6 +420,9 @@ def main():
 
     torch.cuda.set_device(0)
     w4.init(0)
+    if args.profile_gemv:
+        profile_gemv(w4, torch, synth)
+        return
     timer = Timer(torch)
     dec = bench_decode(w4, torch, synth, timer, args.steps, args.warmup)
     print(f"[bench] decode done: {dec['ms_per_step'] * 1e3:.2f} us per layer", file=sys.stderr, flush=True)
@@ -360,7 +458,7 @@ def main():
                    "rotation_bytes": dec["rotation_bytes"], "frac_hbm_peak": round(value / HBM_PEAK_GBS, 4)},
         "roofline": {"bound": "hbm", "kernel": "gemv_kernel<1,0,8> (gate_up 2048x16384, M=1)",
                      "achieved": gu["GB_s"], "peak": HBM_PEAK_GBS, "unit": "GB/s",
-                     "frac": round(gu["GB_s"] / HBM_PEAK_GBS, 4), "traffic": None,
+                     "frac": round(gu["GB_s"] / HBM_PEAK_GBS, 4), "traffic": measured_traffic(),
                      "bytes_per_launch": gu["bytes"], "us_per_launch": gu["us"]},
         "cpu_baseline": cpu,
         "decode_per_projection": dec["per_projection"],

@@ -66,7 +66,13 @@ __global__ __launch_bounds__(kThreads) void gemv_kernel(
   const int tid = threadIdx.x;
   const int c = tid % C;
   const int slot = tid / C;
-  const int n = blockIdx.x * C + c;
+  // Neighbouring column tiles share 128-byte lines of the weight scales (a
+  // tile reads 2C bytes of them per block).  Workgroups are dealt round-robin
+  // over the 8 XCDs, each with its own L2, so consecutive tiles are mapped to
+  // the same XCD: otherwise every XCD would fetch the shared lines again.
+  const int tiles = gridDim.x;
+  const int tile = (tiles & 7) == 0 ? (blockIdx.x & 7) * (tiles >> 3) + (blockIdx.x >> 3) : blockIdx.x;
+  const int n = tile * C + c;
   const int nb = K / kBlock;
 
   float acc[MR];
