@@ -23,13 +23,23 @@
 // slot s of lane half h of B (checked on gfx950), so the product is the block's
 // full 32-element dot product.
 //
-// Data movement: a workgroup stages each K block's operands through LDS (two
-// stages): its packed weights [BN][16 B], weight scales [BN] fp16, activation
-// scales [BM] fp32 and staged activation codes [BM][32 B], contiguous in
-// global memory per block, are fetched by every thread as exactly two 16-byte
-// loads, kDepth blocks ahead through a register ring, and written to LDS one
-// step before use.  Waves read their MFMA fragments and scales from LDS, so no
-// operand is fetched from global memory twice by one workgroup.
+// Data movement: per K block, a workgroup needs its packed weights [BN][16 B],
+// weight scales [BN] fp16, activation scales [BM] fp32 and staged activation
+// codes [BM][32 B]; each is one contiguous run in global memory per block.
+// They are copied straight into LDS with global_load_lds_dwordx4 (no register
+// round trip): chunk c of a stage is 16 bytes, and 64-chunk group g is one
+// DMA instruction of wave g % NW (NW waves), whose lane i lands at chunk
+// 64g + i.  A ring of NS LDS stages is filled NS - 1 steps ahead; each wave
+// waits on its own DMA count (s_waitcnt vmcnt) and a workgroup barrier then
+// publishes the stage.  The staged activation codes are laid out so that a
+// wave's 64 B-fragment reads hit 64 consecutive 16-byte slots (no LDS bank
+// conflicts).
+//
+// K split inside the workgroup: the waves form a WN x WM x WK grid; the
+// WK waves of one (n, m) position take interleaved K blocks (a step stages WK
+// consecutive blocks) and add their accumulators through LDS at the end, in
+// a fixed order.  Shapes with few output tiles thus still give every SIMD
+// several waves to switch between.
 //
 // Epilogue per element and block, with the accumulator started at the bits of
 // 1.5 * 2^23 so that D = 1.5 * 2^23 + 16 * I as an fp32 number:
@@ -45,59 +55,65 @@ namespace {
 
 typedef int v4i __attribute__((ext_vector_type(4)));
 typedef int v16i __attribute__((ext_vector_type(16)));
+// Plain vector types for LDS reads: every read then keeps the alias
+// information that lets the compiler tell it apart from DMA into another stage.
+typedef unsigned v2u __attribute__((ext_vector_type(2)));
 
-constexpr int kThreads = 256;
-constexpr int kDepth = 4;  // K blocks in flight per thread (the ring below has four slots)
 
-// Byte layout of one LDS stage (one K block of one workgroup tile).
-template <int BN, int BM>
+// Byte layout of one LDS stage: WK K blocks of one workgroup tile.
+template <int BN, int BM, int WK, int NW>
 struct Stage {
   static constexpr int kA = 0;              // packed weights [BN][16]
   static constexpr int kSW = BN * 16;       // weight scales fp16 [BN]
   static constexpr int kSX = kSW + BN * 2;  // activation scales fp32 [BM]
-  static constexpr int kB = kSX + BM * 4;   // staged activation codes [BM][32]
-  static constexpr int kBytes = kB + BM * 32;
-  static constexpr int kChunks = kBytes / 16;
-  static_assert(kChunks <= 2 * kThreads, "at most two 16-byte chunks per thread");
+  static constexpr int kB = kSX + BM * 4;   // staged codes [BM/32][2][32][16]
+  static constexpr int kBlockBytes = kB + BM * 32;
+  static constexpr int kBlockChunks = kBlockBytes / 16;
+  static constexpr int kChunks = WK * kBlockChunks;
+  static constexpr int kGroups = (kChunks + 63) / 64;   // DMA instructions per stage
+  static constexpr int kMaxLoads = (kGroups + NW - 1) / NW;  // per wave
+  static constexpr int kBytes = kGroups * 64 * 16;      // padded to whole groups
+  static_assert(kBlockBytes % 16 == 0, "16-byte chunks");
+  static_assert(2 * kMaxLoads <= 63, "vmcnt range");
 };
 
-// Global address of 16-byte chunk c of the stage for block 0, and its stride
-// per block.  Column indices are clamped into range (the data of columns past
-// N is loaded but never stored), so every thread issues its loads
-// unconditionally and the compiler can count them.
-template <int BN, int BM>
-__device__ __forceinline__ void chunk_address(int c, const uint8_t* pw, const uint16_t* ws,
-                                              const uint8_t* qxs, const float* sxs, int N, int M_pad,
-                                              int n0, int m0, const uint8_t** base, int64_t* stride) {
-  const uint8_t* pa = pw + static_cast<int64_t>(min(n0 + c, N - 1)) * kPackedBytes;
-  const int cs = c - BN;
-  const uint8_t* psw = reinterpret_cast<const uint8_t*>(ws + min(n0 + 8 * cs, N - 8));
-  const int cx = cs - BN / 8;
-  const uint8_t* psx = reinterpret_cast<const uint8_t*>(sxs + m0 + 4 * cx);
-  const int cb = min(cx - BM / 4, 2 * BM - 1);
-  const uint8_t* pb = qxs + static_cast<int64_t>(m0 + (cb >> 1)) * kBlock + 16 * (cb & 1);
-  if (c < BN) {
-    *base = pa;
-    *stride = static_cast<int64_t>(N) * kPackedBytes;
-  } else if (cs < BN / 8) {
-    *base = psw;
-    *stride = static_cast<int64_t>(N) * 2;
-  } else if (cx < BM / 4) {
-    *base = psx;
-    *stride = static_cast<int64_t>(M_pad) * 4;
-  } else {
-    *base = pb;
-    *stride = static_cast<int64_t>(M_pad) * kBlock;
-  }
+// s_waitcnt vmcnt(n) (gfx9 encoding), leaving the other counters alone.
+template <int N>
+__device__ __forceinline__ void wait_vmcnt() {
+  static_assert(N >= 0 && N < 64, "vmcnt range");
+  __builtin_amdgcn_s_waitcnt((N & 15) | ((N >> 4) << 14) | 0x0F70);
 }
 
-// Workgroup barrier that orders LDS accesses only.  __syncthreads() also
-// orders global memory, which makes every wave wait for all of its loads in
-// flight, draining the operand prefetch at each K block.
-__device__ __forceinline__ void lds_barrier() {
-  __builtin_amdgcn_fence(__ATOMIC_RELEASE, "workgroup", "local");
+// One 16-byte-per-lane DMA from global memory into LDS: lane i's bytes land
+// at lds_dst + 16 i (lds_dst is wave-uniform; the hardware takes it from M0
+// when the instruction issues).  Issued as inline assembly so that the
+// compiler's wait-count pass, which cannot always tell DMA into one stage
+// from reads of another and then drains every DMA before a read, keeps out:
+// the kernel waits for its DMAs itself (vmcnt), and the memory clobber keeps
+// LDS accesses in program order around it.  M0 is restored afterwards, and
+// an SALU write of M0 needs one wait state before an LDS DMA reads it.
+__device__ __forceinline__ void dma16(const void* src, const void* lds_dst) {
+  const uint32_t lds = static_cast<uint32_t>(reinterpret_cast<uintptr_t>(lds_dst));
+  uint32_t saved;
+  asm volatile(
+      "s_mov_b32 %[sv], m0\n\t"
+      "s_mov_b32 m0, %[lds]\n\t"
+      "s_nop 0\n\t"
+      "global_load_lds_dwordx4 %[src], off\n\t"
+      "s_mov_b32 m0, %[sv]"
+      : [sv] "=&s"(saved)
+      : [src] "v"(src), [lds] "s"(lds)
+      : "memory");
+}
+
+// Workgroup barrier that orders nothing in hardware: each wave has already
+// waited for its own DMA into the stage (vmcnt) and has consumed every LDS
+// read of the previous step before it arrives.  The empty asm statements
+// keep the compiler from moving LDS accesses across it.
+__device__ __forceinline__ void stage_barrier() {
+  asm volatile("" ::: "memory");
   __builtin_amdgcn_s_barrier();
-  __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "workgroup", "local");
+  asm volatile("" ::: "memory");
 }
 
 __device__ __forceinline__ void store_agent(float* p, float v) {
@@ -109,25 +125,68 @@ __device__ __forceinline__ float load_agent(const float* p) {
                                            __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT));
 }
 
-template <int TN, int TM, int WAVES_M, int MODE>
-__global__ __launch_bounds__(kThreads) void gemm_kernel(
+// Source of one lane's DMA chunk: global address of its bytes in K block 0
+// of the region, the region's stride per K block, and which of the step's
+// WK blocks it belongs to.  Columns are clamped into range, so every lane of
+// every DMA instruction reads valid memory.
+template <int BN, int BM, int WK, int NW>
+__device__ __forceinline__ void chunk_source(int c, const uint8_t* pw, const uint16_t* ws, const uint8_t* qxs,
+                                             const float* sxs, int N, int M_pad, int n0, int m0,
+                                             const uint8_t** base, uint32_t* stride, int* kk) {
+  using St = Stage<BN, BM, WK, NW>;
+  c = min(c, St::kChunks - 1);  // padding lanes repeat the last chunk into the pad
+  *kk = c / St::kBlockChunks;
+  const int cc = c - *kk * St::kBlockChunks;
+  if (cc < BN) {
+    *base = pw + static_cast<int64_t>(min(n0 + cc, N - 1)) * kPackedBytes;
+    *stride = static_cast<uint32_t>(N) * kPackedBytes;
+  } else if (cc < BN + BN / 8) {
+    *base = reinterpret_cast<const uint8_t*>(ws + min(n0 + 8 * (cc - BN), N - 8));
+    *stride = static_cast<uint32_t>(N) * 2;
+  } else if (cc < BN + BN / 8 + BM / 4) {
+    *base = reinterpret_cast<const uint8_t*>(sxs + m0 + 4 * (cc - BN - BN / 8));
+    *stride = static_cast<uint32_t>(M_pad) * 4;
+  } else {
+    *base = qxs + static_cast<int64_t>(m0) * kBlock + 16 * (cc - BN - BN / 8 - BM / 4);
+    *stride = static_cast<uint32_t>(M_pad) * kBlock;
+  }
+}
+
+template <int TN, int TM, int WN, int WM, int WK, int MODE, int NS>
+__global__ __launch_bounds__(64 * WN * WM * WK) __attribute__((amdgpu_waves_per_eu(MODE == 0 && WK == 1 ? 4 : 1)))
+void gemm_kernel(
     const uint8_t* __restrict__ pw, const uint16_t* __restrict__ ws, const uint8_t* __restrict__ qxs,
     const float* __restrict__ sxs, int M, int M_pad, int K, int N, int tiles_n, int tiles_m, int bps,
     float* __restrict__ out, int32_t* __restrict__ sums, float* __restrict__ partials,
     uint32_t* __restrict__ tickets) {
-  constexpr int WAVES_N = 4 / WAVES_M;
-  constexpr int BN = 32 * TN * WAVES_N;
-  constexpr int BM = 32 * TM * WAVES_M;
-  using St = Stage<BN, BM>;
-  __shared__ __attribute__((aligned(16))) uint8_t lds[2][St::kBytes];
+  constexpr int NW = WN * WM * WK;  // waves per workgroup
+  static_assert(NW == 4 || NW == 8, "four or eight waves");
+  static_assert(WK == 1 || (WK == 4 && WN * WM == 1), "K split only over four waves of one position");
+  constexpr int BN = 32 * TN * WN;
+  constexpr int BM = 32 * TM * WM;
+  using St = Stage<BN, BM, WK, NW>;
+  constexpr int kL = St::kMaxLoads;
+  static_assert(WK == 1 || TN * TM * 64 * 16 * 4 <= St::kBytes, "K-split partials fit in one stage");
+  static_assert(NS == 4 || NS == 8, "ring of four or eight stages");
+  static_assert(NS - 2 <= 63 / (kL > 0 ? kL : 1), "vmcnt range");
+  __shared__ __attribute__((aligned(16))) uint8_t st0[St::kBytes];
+  __shared__ __attribute__((aligned(16))) uint8_t st1[St::kBytes];
+  __shared__ __attribute__((aligned(16))) uint8_t st2[St::kBytes];
+  __shared__ __attribute__((aligned(16))) uint8_t st3[St::kBytes];
+  __shared__ __attribute__((aligned(16))) uint8_t st4[NS > 4 ? St::kBytes : 16];
+  __shared__ __attribute__((aligned(16))) uint8_t st5[NS > 4 ? St::kBytes : 16];
+  __shared__ __attribute__((aligned(16))) uint8_t st6[NS > 4 ? St::kBytes : 16];
+  __shared__ __attribute__((aligned(16))) uint8_t st7[NS > 4 ? St::kBytes : 16];
 
   const int tid = threadIdx.x;
   const int lane = tid & 63;
-  const int wave = tid >> 6;
-  const int wn = wave % WAVES_N;
-  const int wm = wave / WAVES_N;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const int wn = wave % WN;
+  const int wm = (wave / WN) % WM;
+  const int wk = wave / (WN * WM);
   const int h = lane >> 5;
   const int l32 = lane & 31;
+  const int my_loads = (St::kGroups - wave + NW - 1) / NW;  // kL or kL - 1
 
   // Tiles sharing a weight tile (consecutive m tiles) go to the same XCD: the
   // hardware deals workgroups round-robin over the 8 XCDs.
@@ -149,6 +208,10 @@ __global__ __launch_bounds__(kThreads) void gemm_kernel(
   v16i magic;
 #pragma unroll
   for (int r = 0; r < 16; ++r) magic[r] = kMagicBits;
+  // Opaque to the optimiser: the splat then lives in one register tuple that
+  // every MFMA reads as its C operand, instead of being rebuilt (16 moves)
+  // in each MFMA's destination registers before every block.
+  asm volatile("" : "+v"(magic));
 
   float acc[TN][TM][16];
 #pragma unroll
@@ -158,29 +221,31 @@ __global__ __launch_bounds__(kThreads) void gemm_kernel(
 #pragma unroll
       for (int r = 0; r < 16; ++r) acc[i][j][r] = 0.0f;
 
-  // One block: fragments and scales from LDS, TN x TM MFMAs, fp32 epilogue.
+  // One K block of this wave: fragments and scales from LDS, TN x TM MFMAs,
+  // then the fp32 epilogue (or, for the block-sum export, the integer sums).
   auto compute = [&](const uint8_t* st, int b) __attribute__((always_inline)) {
+    const uint8_t* sb = st + wk * St::kBlockBytes;
     v4i afrag[TN];
     uint2 sraw[TN][4];
 #pragma unroll
     for (int i = 0; i < TN; ++i) {
       const int col = (wn * TN + i) * 32;
-      const uint2 araw = *reinterpret_cast<const uint2*>(st + St::kA + (col + l32) * 16 + 8 * h);
+      const v2u araw = *reinterpret_cast<const v2u*>(sb + St::kA + (col + l32) * 16 + 8 * h);
       afrag[i][0] = static_cast<int>(low_nibbles_x16(araw.x));
       afrag[i][1] = static_cast<int>(low_nibbles_x16(araw.y));
       afrag[i][2] = static_cast<int>(high_nibbles_x16(araw.x));
       afrag[i][3] = static_cast<int>(high_nibbles_x16(araw.y));
 #pragma unroll
       for (int q = 0; q < 4; ++q)
-        sraw[i][q] = *reinterpret_cast<const uint2*>(st + St::kSW + (col + 8 * q + 4 * h) * 2);
+        sraw[i][q] = *reinterpret_cast<const uint2*>(sb + St::kSW + (col + 8 * q + 4 * h) * 2);
     }
     v4i bfrag[TM];
     float sxv[TM];
 #pragma unroll
     for (int j = 0; j < TM; ++j) {
-      const int row = (wm * TM + j) * 32 + l32;
-      bfrag[j] = *reinterpret_cast<const v4i*>(st + St::kB + row * kBlock + 16 * h);
-      sxv[j] = *reinterpret_cast<const float*>(st + St::kSX + row * 4);
+      const int rg = wm * TM + j;
+      bfrag[j] = *reinterpret_cast<const v4i*>(sb + St::kB + ((rg * 2 + h) * 32 + l32) * 16);
+      sxv[j] = *reinterpret_cast<const float*>(sb + St::kSX + (rg * 32 + l32) * 4);
     }
     v16i d[TN][TM];
 #pragma unroll
@@ -224,47 +289,118 @@ __global__ __launch_bounds__(kThreads) void gemm_kernel(
 
   if (b_begin < b_end) {
     const int last = b_end - 1;
-    const int c0 = tid;
-    const int c1 = tid + kThreads;
-    const uint8_t* base0;
-    const uint8_t* base1;
-    int64_t stride0, stride1;
-    chunk_address<BN, BM>(min(c0, St::kChunks - 1), pw, ws, qxs, sxs, N, M_pad, n0, m0, &base0, &stride0);
-    chunk_address<BN, BM>(min(c1, St::kChunks - 1), pw, ws, qxs, sxs, N, M_pad, n0, m0, &base1, &stride1);
+    const int nsteps = (b_end - b_begin + WK - 1) / WK;
+    // DMA sources of this lane, one per instruction; a wave with fewer
+    // groups than kL leaves its last slot unused.
+    const uint8_t* src0;
+    const uint8_t* src1;
+    const uint8_t* src2;
+    uint32_t str0, str1, str2;
+    int kk0, kk1, kk2;
+    static_assert(kL <= 3, "three DMA instructions per wave and stage at most");
+    chunk_source<BN, BM, WK, NW>((wave + 0 * NW) * 64 + lane, pw, ws, qxs, sxs, N, M_pad, n0, m0, &src0, &str0, &kk0);
+    chunk_source<BN, BM, WK, NW>((wave + 1 * NW) * 64 + lane, pw, ws, qxs, sxs, N, M_pad, n0, m0, &src1, &str1, &kk1);
+    chunk_source<BN, BM, WK, NW>((wave + 2 * NW) * 64 + lane, pw, ws, qxs, sxs, N, M_pad, n0, m0, &src2, &str2, &kk2);
 
-    // Register ring of kDepth = 4 blocks held in eight named variables: an
-    // array (or references to one) would be placed in scratch memory.
-    uint4 r0a, r0b, r1a, r1b, r2a, r2b, r3a, r3b;
-#define W4A8_FETCH(A, B, BLK)                                                  \
-  do {                                                                         \
-    const int blk_ = (BLK);                                                    \
-    A = *reinterpret_cast<const uint4*>(base0 + blk_ * stride0);               \
-    B = *reinterpret_cast<const uint4*>(base1 + blk_ * stride1);               \
+    // Stage `st` <- the WK blocks of step s (clamped to the last block, so
+    // the steps past the end re-read it and every wave issues the same
+    // number of DMAs per step).
+#define W4A8_DMA(ST, S)                                                                          \
+  do {                                                                                           \
+    const int sd_ = (S);                                                                          \
+    const int bsd_ = b_begin + sd_ * WK;                                                           \
+    if (kL > 0 && my_loads > 0)                                                                  \
+      dma16(src0 + static_cast<uint64_t>(static_cast<uint32_t>(min(bsd_ + kk0, last))) * str0,        \
+            (ST) + (wave + 0 * NW) * 1024);                                                         \
+    if (kL > 1 && my_loads > 1)                                                                  \
+      dma16(src1 + static_cast<uint64_t>(static_cast<uint32_t>(min(bsd_ + kk1, last))) * str1,        \
+            (ST) + (wave + 1 * NW) * 1024);                                                         \
+    if (kL > 2 && my_loads > 2)                                                                  \
+      dma16(src2 + static_cast<uint64_t>(static_cast<uint32_t>(min(bsd_ + kk2, last))) * str2,        \
+            (ST) + (wave + 2 * NW) * 1024);                                                         \
   } while (0)
-#define W4A8_PIPE_STEP(A, B, ST, BLK)                                           \
-  do {                                                                         \
-    const int b_ = (BLK);                                                      \
-    if (c0 < St::kChunks) *reinterpret_cast<uint4*>((ST) + c0 * 16) = A;       \
-    if (c1 < St::kChunks) *reinterpret_cast<uint4*>((ST) + c1 * 16) = B;       \
-    W4A8_FETCH(A, B, min(b_ + kDepth, last));                                  \
-    lds_barrier();                                                             \
-    if (b_ < b_end) compute((ST), b_);                                         \
+    // Step s: wait for this wave's DMAs into CUR (the NS - 2 later stages
+    // may stay in flight), publish CUR, refill the stage drained last step
+    // with step s + NS - 1, compute.  vmcnt counts loads and stores together,
+    // and a store may complete ahead of older loads, so the block-sum export
+    // (which stores inside the loop) drains the counter instead.
+#define W4A8_STEP(CUR, NEXT, S)                                                                  \
+  do {                                                                                           \
+    const int s_ = (S);                                                                          \
+    if (MODE == 1) wait_vmcnt<0>();                                                              \
+    else if (my_loads == kL) wait_vmcnt<(NS - 2) * kL>();                                        \
+    else wait_vmcnt<(NS - 2) * (kL - 1)>();                                                      \
+    stage_barrier();                                                                             \
+    W4A8_DMA(NEXT, s_ + NS - 1);                                                                 \
+    const int b_ = b_begin + s_ * WK + wk;                                                       \
+    if (s_ < nsteps && b_ < b_end) compute((CUR), b_);                                           \
   } while (0)
-    W4A8_FETCH(r0a, r0b, min(b_begin + 0, last));
-    W4A8_FETCH(r1a, r1b, min(b_begin + 1, last));
-    W4A8_FETCH(r2a, r2b, min(b_begin + 2, last));
-    W4A8_FETCH(r3a, r3b, min(b_begin + 3, last));
-    for (int bb = b_begin; bb < b_end; bb += kDepth) {
-      W4A8_PIPE_STEP(r0a, r0b, lds[0], bb + 0);
-      W4A8_PIPE_STEP(r1a, r1b, lds[1], bb + 1);
-      W4A8_PIPE_STEP(r2a, r2b, lds[0], bb + 2);
-      W4A8_PIPE_STEP(r3a, r3b, lds[1], bb + 3);
+    W4A8_DMA(st0, 0);
+    W4A8_DMA(st1, 1);
+    W4A8_DMA(st2, 2);
+    if constexpr (NS == 4) {
+      for (int s = 0; s < nsteps; s += NS) {
+        W4A8_STEP(st0, st3, s + 0);
+        W4A8_STEP(st1, st0, s + 1);
+        W4A8_STEP(st2, st1, s + 2);
+        W4A8_STEP(st3, st2, s + 3);
+      }
+    } else {
+      W4A8_DMA(st3, 3);
+      W4A8_DMA(st4, 4);
+      W4A8_DMA(st5, 5);
+      W4A8_DMA(st6, 6);
+      for (int s = 0; s < nsteps; s += NS) {
+        W4A8_STEP(st0, st7, s + 0);
+        W4A8_STEP(st1, st0, s + 1);
+        W4A8_STEP(st2, st1, s + 2);
+        W4A8_STEP(st3, st2, s + 3);
+        W4A8_STEP(st4, st3, s + 4);
+        W4A8_STEP(st5, st4, s + 5);
+        W4A8_STEP(st6, st5, s + 6);
+        W4A8_STEP(st7, st6, s + 7);
+      }
     }
-#undef W4A8_PIPE_STEP
-#undef W4A8_FETCH
+#undef W4A8_STEP
+#undef W4A8_DMA
+    // The refills past the end are still in flight: drain them before the
+    // stages are reused or the workgroup ends.
+    wait_vmcnt<0>();
   }
 
   if (MODE == 1) return;
+
+  // Waves wk > 0 hand their accumulators to wave wk = 0 of their (n, m)
+  // position through LDS; that wave adds them in wk order.
+  if (WK > 1) {
+    stage_barrier();
+    const int pos = wave % (WN * WM);
+    if (wk > 0) {
+      const int slot = pos * (WK - 1) + wk - 1;
+      float* dst = reinterpret_cast<float*>(slot == 0 ? st0 : slot == 1 ? st1 : st2);
+#pragma unroll
+      for (int i = 0; i < TN; ++i)
+#pragma unroll
+        for (int j = 0; j < TM; ++j)
+#pragma unroll
+          for (int r = 0; r < 16; ++r) dst[((i * TM + j) * 16 + r) * 64 + lane] = acc[i][j][r];
+    }
+    stage_barrier();
+    if (wk == 0) {
+#pragma unroll
+      for (int k = 1; k < WK; ++k) {
+        const int slot = pos * (WK - 1) + k - 1;
+        const float* src = reinterpret_cast<const float*>(slot == 0 ? st0 : slot == 1 ? st1 : st2);
+#pragma unroll
+        for (int i = 0; i < TN; ++i)
+#pragma unroll
+          for (int j = 0; j < TM; ++j)
+#pragma unroll
+            for (int r = 0; r < 16; ++r) acc[i][j][r] += src[((i * TM + j) * 16 + r) * 64 + lane];
+      }
+    }
+  }
+  const bool owner = wk == 0;  // wave that holds the workgroup's result for its (n, m) position
 
   if (ksplit > 1) {
     // Partial tiles meet in library scratch.  Every access to it and to the
@@ -272,17 +408,19 @@ __global__ __launch_bounds__(kThreads) void gemm_kernel(
     // explicit wait makes each lane's partial stores complete before the
     // workgroup takes its ticket.
     __shared__ int last_flag;
+    if (owner) {
 #pragma unroll
-    for (int i = 0; i < TN; ++i)
+      for (int i = 0; i < TN; ++i)
 #pragma unroll
-      for (int j = 0; j < TM; ++j) {
-        const int m = m_base + 32 * j + l32;
+        for (int j = 0; j < TM; ++j) {
+          const int m = m_base + 32 * j + l32;
 #pragma unroll
-        for (int r = 0; r < 16; ++r) {
-          const int n = n_base + 32 * i + 8 * (r / 4) + 4 * h + (r % 4);
-          if (m < M && n < N) store_agent(partials + (static_cast<int64_t>(split) * M + m) * N + n, acc[i][j][r]);
+          for (int r = 0; r < 16; ++r) {
+            const int n = n_base + 32 * i + 8 * (r / 4) + 4 * h + (r % 4);
+            if (m < M && n < N) store_agent(partials + (static_cast<int64_t>(split) * M + m) * N + n, acc[i][j][r]);
+          }
         }
-      }
+    }
     __builtin_amdgcn_s_waitcnt(0);
     __syncthreads();
     if (threadIdx.x == 0)
@@ -290,23 +428,26 @@ __global__ __launch_bounds__(kThreads) void gemm_kernel(
                   static_cast<uint32_t>(ksplit - 1);
     __syncthreads();
     if (!last_flag) return;
+    if (owner) {
 #pragma unroll
-    for (int i = 0; i < TN; ++i)
+      for (int i = 0; i < TN; ++i)
 #pragma unroll
-      for (int j = 0; j < TM; ++j) {
-        const int m = m_base + 32 * j + l32;
+        for (int j = 0; j < TM; ++j) {
+          const int m = m_base + 32 * j + l32;
 #pragma unroll
-        for (int r = 0; r < 16; ++r) {
-          const int n = n_base + 32 * i + 8 * (r / 4) + 4 * h + (r % 4);
-          float t = 0.0f;
-          if (m < M && n < N)
-            for (int sp = 0; sp < ksplit; ++sp) t += load_agent(partials + (static_cast<int64_t>(sp) * M + m) * N + n);
-          acc[i][j][r] = t;
+          for (int r = 0; r < 16; ++r) {
+            const int n = n_base + 32 * i + 8 * (r / 4) + 4 * h + (r % 4);
+            float t = 0.0f;
+            if (m < M && n < N)
+              for (int sp = 0; sp < ksplit; ++sp) t += load_agent(partials + (static_cast<int64_t>(sp) * M + m) * N + n);
+            acc[i][j][r] = t;
+          }
         }
-      }
+    }
     if (threadIdx.x == 0) __hip_atomic_store(&tickets[1 + id], 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
   }
 
+  if (!owner) return;
 #pragma unroll
   for (int i = 0; i < TN; ++i)
 #pragma unroll
@@ -323,47 +464,44 @@ __global__ __launch_bounds__(kThreads) void gemm_kernel(
 }
 
 struct Plan {
-  int tn, tm, waves_m;   // MFMA tiles per wave (n, m), waves along m
+  int tn, tm, wn, wm, wk;  // MFMA tiles per wave (n, m); waves along n, m and K
   int wg_n, wg_m;
   int tiles_n, tiles_m, m_pad;
   int ksplit, bps;
 };
 
-Plan make_plan(int tn, int tm, int waves_m, int M, int N) {
+Plan make_plan(int tn, int tm, int wn, int wm, int wk, int M, int N) {
   Plan p{};
   p.tn = tn;
   p.tm = tm;
-  p.waves_m = waves_m;
-  p.wg_n = 32 * tn * (4 / waves_m);
-  p.wg_m = 32 * tm * waves_m;
+  p.wn = wn;
+  p.wm = wm;
+  p.wk = wk;
+  p.wg_n = 32 * tn * wn;
+  p.wg_m = 32 * tm * wm;
   p.tiles_n = (N + p.wg_n - 1) / p.wg_n;
   p.tiles_m = (M + p.wg_m - 1) / p.wg_m;
   p.m_pad = p.tiles_m * p.wg_m;
   return p;
 }
 
-// Largest tile that still yields a full wave of workgroups; split K only when
-// even the smallest tile leaves CUs idle (split partials cost HBM traffic).
+// Each wave owns 32 x 64 outputs (32 x 32 for at most 32 tokens).  Large
+// problems take the widest workgroup tile that still fills the chip twice
+// over: the bytes staged per MFMA fall as the tile grows (the activation
+// codes of a block are shared by all BN weight columns).  Otherwise the four
+// waves of a workgroup split K over one small tile.  Split K across
+// workgroups only when even that leaves CUs idle.
 Plan plan_gemm(int M, int K, int N) {
-  constexpr int kFull = 256;
+  constexpr int kCUs = 256;
+  const int tm = M <= 32 ? 1 : 2;
   Plan p;
-  if (M <= 32) {
-    p = make_plan(2, 1, 1, M, N);      // 256 x 32
-  } else if (M <= 64) {
-    p = make_plan(2, 1, 2, M, N);      // 128 x 64
-  } else {
-    p = make_plan(2, 2, 2, M, N);      // 128 x 128
-    if (p.tiles_n * p.tiles_m < kFull) p = make_plan(1, 2, 2, M, N);  // 64 x 128
-    if (p.tiles_n * p.tiles_m < kFull) p = make_plan(1, 1, 2, M, N);  // 64 x 64
-  }
-  // Fewer than two tiles per CU leave too few waves to hide latency: split K
-  // towards four workgroups per CU, keeping at least 64 blocks per split (the
-  // partial tiles cost HBM traffic that short splits do not amortise).
+  if (M > 64) p = make_plan(1, 2, 4, 2, 1, M, N);       // 128 x 128, eight waves
+  else p = make_plan(1, tm, 4, 1, 1, M, N);             // 128 x 32 or 128 x 64
+  if (p.tiles_n * p.tiles_m < 2 * kCUs) p = make_plan(1, tm, 1, 1, 4, M, N);
   const int nb = K / kBlock;
   const int tiles = p.tiles_n * p.tiles_m;
   constexpr int kMinBlocksPerSplit = 64;
-  constexpr int kTargetGroups = 1024;
-  int ks = tiles < 2 * kFull ? (kTargetGroups + tiles - 1) / tiles : 1;
+  int ks = tiles < kCUs ? (2 * kCUs + tiles - 1) / tiles : 1;
   const int ks_max = nb / kMinBlocksPerSplit;
   if (ks > ks_max) ks = ks_max;
   if (ks < 1) ks = 1;
@@ -371,6 +509,10 @@ Plan plan_gemm(int M, int K, int N) {
   p.ksplit = (nb + p.bps - 1) / p.bps;
   return p;
 }
+
+// Four stages: deeper rings cost LDS that is better spent on occupancy
+// (measured: eight stages were slower on every prefill shape).
+constexpr int kRing = 4;
 
 size_t align256(size_t v) { return (v + 255) & ~static_cast<size_t>(255); }
 
@@ -403,23 +545,26 @@ int launch_gemm(const GemmArgs& a, int mode, hipStream_t stream) {
   // no scales (w_scales may be null), so it stages bytes of the packed weights
   // instead (at least as large as the scales would be) and never reads them.
   const uint16_t* ws = mode == 1 ? reinterpret_cast<const uint16_t*>(a.packed_w) : a.w_scales;
-#define W4A8_GEMM_LAUNCH(TN, TM, WM, MODE)                                                             \
-  hipLaunchKernelGGL((gemm_kernel<TN, TM, WM, MODE>), grid, dim3(256), 0, stream, a.packed_w, ws,        \
-                     qxs, sxs, a.M, p.m_pad, a.K, a.N, p.tiles_n, p.tiles_m, p.bps, a.out, a.sums,       \
-                     partials, sc->tickets)
-  if (mode == 1) {
-    if (p.waves_m == 1) W4A8_GEMM_LAUNCH(2, 1, 1, 1);
-    else if (p.tn == 2 && p.tm == 2) W4A8_GEMM_LAUNCH(2, 2, 2, 1);
-    else if (p.tn == 2) W4A8_GEMM_LAUNCH(2, 1, 2, 1);
-    else if (p.tm == 2) W4A8_GEMM_LAUNCH(1, 2, 2, 1);
-    else W4A8_GEMM_LAUNCH(1, 1, 2, 1);
-  } else {
-    if (p.waves_m == 1) W4A8_GEMM_LAUNCH(2, 1, 1, 0);
-    else if (p.tn == 2 && p.tm == 2) W4A8_GEMM_LAUNCH(2, 2, 2, 0);
-    else if (p.tn == 2) W4A8_GEMM_LAUNCH(2, 1, 2, 0);
-    else if (p.tm == 2) W4A8_GEMM_LAUNCH(1, 2, 2, 0);
-    else W4A8_GEMM_LAUNCH(1, 1, 2, 0);
-  }
+#define W4A8_GEMM_LAUNCH(TN, TM, WN, WM, WK, MODE)                                                     \
+  hipLaunchKernelGGL((gemm_kernel<TN, TM, WN, WM, WK, MODE, kRing>), grid, dim3(64 * WN * WM * WK), 0,     \
+                     stream, a.packed_w, ws, qxs, sxs, a.M, p.m_pad, a.K, a.N, p.tiles_n, p.tiles_m,       \
+                     p.bps, a.out, a.sums, partials, sc->tickets)
+#define W4A8_GEMM_MODE(MODE)                                                                           \
+  do {                                                                                                 \
+    if (p.wk == 4) {                                                                                   \
+      if (p.tm == 2) W4A8_GEMM_LAUNCH(1, 2, 1, 1, 4, MODE);                                            \
+      else W4A8_GEMM_LAUNCH(1, 1, 1, 1, 4, MODE);                                                      \
+    } else if (p.wm == 2) {                                                                            \
+      W4A8_GEMM_LAUNCH(1, 2, 4, 2, 1, MODE);                                                           \
+    } else if (p.tm == 2) {                                                                            \
+      W4A8_GEMM_LAUNCH(1, 2, 4, 1, 1, MODE);                                                           \
+    } else {                                                                                           \
+      W4A8_GEMM_LAUNCH(1, 1, 4, 1, 1, MODE);                                                           \
+    }                                                                                                  \
+  } while (0)
+  if (mode == 1) W4A8_GEMM_MODE(1);
+  else W4A8_GEMM_MODE(0);
+#undef W4A8_GEMM_MODE
 #undef W4A8_GEMM_LAUNCH
   W4A8_HIP(hipGetLastError());
   return W4A8_OK;

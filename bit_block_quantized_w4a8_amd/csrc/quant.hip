@@ -78,13 +78,16 @@ int launch_quantize_export(const uint16_t* x, int M, int K, int8_t* qx, float* s
 
 // ------------------------------------------------------ GEMM pre-pass
 // Quantises x [M][K] into the staging layout read by the MFMA GEMM:
-//   qxs [K/32][M_pad][32] int8: the 32 codes of (block b, row m), ordered so that
-//       lane half h of an MFMA operand reads bytes 16h .. 16h+15 and finds
-//       elements 8h .. 8h+7 followed by 16+8h .. 16+8h+7 (the order in which
-//       the weight nibbles unpack, see gemm.hip);
+//   qxs int8, per block b: [M_pad/32][2][32][16] -- row group (32 rows), lane
+//       half h, row within the group, 16 bytes.  Half h of (block b, row m)
+//       holds elements 8h .. 8h+7 followed by 16+8h .. 16+8h+7, the order in
+//       which the weight nibbles unpack (see gemm.hip), so lane (h, r) of an
+//       MFMA operand finds its 16 bytes at ((group * 2 + h) * 32 + r) * 16 and
+//       a wave's 64 fragment reads touch 64 consecutive 16-byte slots;
 //   sxs [K/32][M_pad] fp32 block scales.
 // Rows M .. M_pad-1 are written as zeros (codes and scales).
-// Group lane g holds elements 8g .. 8g+7, which land at byte 8 * (0, 2, 1, 3)[g].
+// Group lane g holds elements 8g .. 8g+7, which belong at byte 8 * (0, 2, 1, 3)[g]
+// of the row's 32 codes: half (0, 1, 0, 1)[g], offset (0, 0, 8, 8)[g].
 __global__ __launch_bounds__(256) void quantize_stage_kernel(const uint16_t* __restrict__ x, int M,
                                                              int M_pad, int K,
                                                              uint8_t* __restrict__ qxs,
@@ -100,8 +103,8 @@ __global__ __launch_bounds__(256) void quantize_stage_kernel(const uint16_t* __r
   if (m < M) unpack_half8(*reinterpret_cast<const uint4*>(x + m * K + 8 * e), v);
   float scale;
   const uint2 codes = quantize8_group4(v, &scale);
-  const int off = 8 * (((g & 1) << 1) | (g >> 1));
-  *reinterpret_cast<uint2*>(qxs + (b * M_pad + m) * kBlock + off) = codes;
+  const int64_t row_slot = ((m >> 5) * 2 + (g & 1)) * 32 + (m & 31);
+  *reinterpret_cast<uint2*>(qxs + b * M_pad * kBlock + row_slot * 16 + 8 * (g >> 1)) = codes;
   if (g == 0) sxs[b * M_pad + m] = scale;
 }
 
