@@ -13,7 +13,7 @@
 // its B operand (columns m).  In the 32x32 result, lane l holds token column
 // m = l % 32 and weight rows n = 8(r/4) + 4(l/32) + r%4 in register r, so the
 // token scale is one value per lane and the 16 weight scales of a lane are
-// fp16 values that v_fma_mix_f32 consumes without conversion.
+// four runs of four consecutive columns.
 //
 // Operand fragments: lane half h = l / 32 of an A operand loads bytes 8h .. 8h+7
 // of the 16-byte weight group of its column; their low nibbles are elements
@@ -29,9 +29,9 @@
 // They are copied straight into LDS with global_load_lds_dwordx4 (no register
 // round trip): chunk c of a stage is 16 bytes, and 64-chunk group g is one
 // DMA instruction of wave g % NW (NW waves), whose lane i lands at chunk
-// 64g + i.  A ring of NS LDS stages is filled NS - 1 steps ahead; each wave
-// waits on its own DMA count (s_waitcnt vmcnt) and a workgroup barrier then
-// publishes the stage.  The staged activation codes are laid out so that a
+// 64g + i.  A ring of four LDS stages is filled three steps ahead (deeper
+// rings cost LDS that is worth more as occupancy); each wave waits on its own
+// DMA count (s_waitcnt vmcnt) and a workgroup barrier then publishes the stage.  The staged activation codes are laid out so that a
 // wave's 64 B-fragment reads hit 64 consecutive 16-byte slots (no LDS bank
 // conflicts).
 //
@@ -44,7 +44,7 @@
 // Epilogue per element and block, with the accumulator started at the bits of
 // 1.5 * 2^23 so that D = 1.5 * 2^23 + 16 * I as an fp32 number:
 //   t   = fma(D, sxq, -1.5 * 2^23 * sxq) = RN(I * sxq * 16),  sxq = sx' / 16
-//   acc = fma(t, sw, acc)                  (v_fma_mix_f32, sw read as fp16)
+//   acc = fma(t, sw, acc)                  (sw widened to fp32 once per stage)
 // where sx' is sx with its two lowest significand bits cleared, which makes
 // 1.5 * 2^23 * sxq exact (relative change of sx below 2^-22).
 #include "kernels.hpp"
@@ -58,6 +58,8 @@ typedef int v16i __attribute__((ext_vector_type(16)));
 // Plain vector types for LDS reads: every read then keeps the alias
 // information that lets the compiler tell it apart from DMA into another stage.
 typedef unsigned v2u __attribute__((ext_vector_type(2)));
+typedef float v2f __attribute__((ext_vector_type(2)));
+typedef float v4f __attribute__((ext_vector_type(4)));
 
 
 // Byte layout of one LDS stage: WK K blocks of one workgroup tile.
@@ -72,7 +74,8 @@ struct Stage {
   static constexpr int kChunks = WK * kBlockChunks;
   static constexpr int kGroups = (kChunks + 63) / 64;   // DMA instructions per stage
   static constexpr int kMaxLoads = (kGroups + NW - 1) / NW;  // per wave
-  static constexpr int kBytes = kGroups * 64 * 16;      // padded to whole groups
+  static constexpr int kSWF = kGroups * 64 * 16;       // weight scales widened to fp32 [WK][BN]
+  static constexpr int kBytes = kSWF + WK * BN * 4;
   static_assert(kBlockBytes % 16 == 0, "16-byte chunks");
   static_assert(2 * kMaxLoads <= 63, "vmcnt range");
 };
@@ -152,7 +155,7 @@ __device__ __forceinline__ void chunk_source(int c, const uint8_t* pw, const uin
   }
 }
 
-template <int TN, int TM, int WN, int WM, int WK, int MODE, int NS>
+template <int TN, int TM, int WN, int WM, int WK, int MODE>
 __global__ __launch_bounds__(64 * WN * WM * WK) __attribute__((amdgpu_waves_per_eu(MODE == 0 && WK == 1 ? 4 : 1)))
 void gemm_kernel(
     const uint8_t* __restrict__ pw, const uint16_t* __restrict__ ws, const uint8_t* __restrict__ qxs,
@@ -167,16 +170,19 @@ void gemm_kernel(
   using St = Stage<BN, BM, WK, NW>;
   constexpr int kL = St::kMaxLoads;
   static_assert(WK == 1 || TN * TM * 64 * 16 * 4 <= St::kBytes, "K-split partials fit in one stage");
-  static_assert(NS == 4 || NS == 8, "ring of four or eight stages");
-  static_assert(NS - 2 <= 63 / (kL > 0 ? kL : 1), "vmcnt range");
+  static_assert(2 * kL <= 63, "vmcnt range");
+  // Wave 0 widens a stage's weight scales to fp32 (two per lane) one step
+  // ahead of use, which turns every half-rate v_fma_mix_f32 of the epilogue
+  // into a full-rate v_fma_f32 but leaves each stage one step less time to
+  // arrive.  The K-split tiles are short on latency hiding, so they keep the
+  // fp16 scales and the three-step lead.
+  constexpr bool kWiden = MODE == 0 && WK == 1;
+  static_assert(!kWiden || BN == 128, "one wave widens the scales of a stage, two per lane");
+  // Ring of four stages: blocks are fetched three steps ahead.
   __shared__ __attribute__((aligned(16))) uint8_t st0[St::kBytes];
   __shared__ __attribute__((aligned(16))) uint8_t st1[St::kBytes];
   __shared__ __attribute__((aligned(16))) uint8_t st2[St::kBytes];
   __shared__ __attribute__((aligned(16))) uint8_t st3[St::kBytes];
-  __shared__ __attribute__((aligned(16))) uint8_t st4[NS > 4 ? St::kBytes : 16];
-  __shared__ __attribute__((aligned(16))) uint8_t st5[NS > 4 ? St::kBytes : 16];
-  __shared__ __attribute__((aligned(16))) uint8_t st6[NS > 4 ? St::kBytes : 16];
-  __shared__ __attribute__((aligned(16))) uint8_t st7[NS > 4 ? St::kBytes : 16];
 
   const int tid = threadIdx.x;
   const int lane = tid & 63;
@@ -226,7 +232,8 @@ void gemm_kernel(
   auto compute = [&](const uint8_t* st, int b) __attribute__((always_inline)) {
     const uint8_t* sb = st + wk * St::kBlockBytes;
     v4i afrag[TN];
-    uint2 sraw[TN][4];
+    v4f swf[TN][4];
+    v2u sraw[TN][4];
 #pragma unroll
     for (int i = 0; i < TN; ++i) {
       const int col = (wn * TN + i) * 32;
@@ -236,8 +243,10 @@ void gemm_kernel(
       afrag[i][2] = static_cast<int>(high_nibbles_x16(araw.x));
       afrag[i][3] = static_cast<int>(high_nibbles_x16(araw.y));
 #pragma unroll
-      for (int q = 0; q < 4; ++q)
-        sraw[i][q] = *reinterpret_cast<const uint2*>(sb + St::kSW + (col + 8 * q + 4 * h) * 2);
+      for (int q = 0; q < 4; ++q) {
+        if (kWiden) swf[i][q] = *reinterpret_cast<const v4f*>(st + St::kSWF + (wk * BN + col + 8 * q + 4 * h) * 4);
+        else sraw[i][q] = *reinterpret_cast<const v2u*>(sb + St::kSW + (col + 8 * q + 4 * h) * 2);
+      }
     }
     v4i bfrag[TM];
     float sxv[TM];
@@ -280,8 +289,13 @@ void gemm_kernel(
       for (int j = 0; j < TM; ++j)
 #pragma unroll
         for (int r = 0; r < 16; ++r) {
-          const uint32_t word = (r & 2) ? sraw[i][r / 4].y : sraw[i][r / 4].x;
-          const float sw = half_bits_to_float((r & 1) ? (word >> 16) : (word & 0xFFFFu));
+          float sw;
+          if (kWiden) {
+            sw = swf[i][r / 4][r % 4];
+          } else {
+            const uint32_t word = (r & 2) ? sraw[i][r / 4].y : sraw[i][r / 4].x;
+            sw = half_bits_to_float((r & 1) ? (word >> 16) : (word & 0xFFFFu));  // folds into v_fma_mix_f32
+          }
           const float t = fmaf(__int_as_float(d[i][j][r]), sxq[j], cx[j]);
           acc[i][j][r] = fmaf(t, sw, acc[i][j][r]);
         }
@@ -319,47 +333,53 @@ void gemm_kernel(
       dma16(src2 + static_cast<uint64_t>(static_cast<uint32_t>(min(bsd_ + kk2, last))) * str2,        \
             (ST) + (wave + 2 * NW) * 1024);                                                         \
   } while (0)
-    // Step s: wait for this wave's DMAs into CUR (the NS - 2 later stages
-    // may stay in flight), publish CUR, refill the stage drained last step
-    // with step s + NS - 1, compute.  vmcnt counts loads and stores together,
-    // and a store may complete ahead of older loads, so the block-sum export
-    // (which stores inside the loop) drains the counter instead.
-#define W4A8_STEP(CUR, NEXT, S)                                                                  \
+    // Widening runs one step ahead: stage s + 1 is converted while the waves
+    // compute stage s, and the next barrier publishes it.
+    auto convert_scales = [&](uint8_t* st) __attribute__((always_inline)) {
+      if (kWiden && wave == 0) {
+        const int kk = lane / (BN / 2);
+        const int p = lane % (BN / 2);
+        const uint32_t two = *reinterpret_cast<const uint32_t*>(st + kk * St::kBlockBytes + St::kSW + 4 * p);
+        v2f f;
+        f.x = half_bits_to_float(two & 0xFFFFu);
+        f.y = half_bits_to_float(two >> 16);
+        *reinterpret_cast<v2f*>(st + St::kSWF + (kk * BN + 2 * p) * 4) = f;
+      }
+    };
+    // Step s: wait for this wave's DMAs into the stage of step s + 1 when
+    // widening (else of step s), publish it, refill the stage drained last
+    // step with step s + 3, widen the scales of step s + 1, compute step s.
+    // vmcnt counts loads and stores together, and a store may complete ahead
+    // of older loads, so the block-sum export (which stores inside the loop)
+    // drains the counter instead.
+#define W4A8_STEP(CUR, NXT, REFILL, S)                                                           \
   do {                                                                                           \
     const int s_ = (S);                                                                          \
     if (MODE == 1) wait_vmcnt<0>();                                                              \
-    else if (my_loads == kL) wait_vmcnt<(NS - 2) * kL>();                                        \
-    else wait_vmcnt<(NS - 2) * (kL - 1)>();                                                      \
+    else if (kWiden && my_loads == kL) wait_vmcnt<kL>();                                         \
+    else if (kWiden) wait_vmcnt<kL - 1>();                                                       \
+    else if (my_loads == kL) wait_vmcnt<2 * kL>();                                               \
+    else wait_vmcnt<2 * (kL - 1)>();                                                             \
     stage_barrier();                                                                             \
-    W4A8_DMA(NEXT, s_ + NS - 1);                                                                 \
+    W4A8_DMA(REFILL, s_ + 3);                                                                    \
+    convert_scales(NXT);                                                                         \
     const int b_ = b_begin + s_ * WK + wk;                                                       \
     if (s_ < nsteps && b_ < b_end) compute((CUR), b_);                                           \
   } while (0)
     W4A8_DMA(st0, 0);
     W4A8_DMA(st1, 1);
     W4A8_DMA(st2, 2);
-    if constexpr (NS == 4) {
-      for (int s = 0; s < nsteps; s += NS) {
-        W4A8_STEP(st0, st3, s + 0);
-        W4A8_STEP(st1, st0, s + 1);
-        W4A8_STEP(st2, st1, s + 2);
-        W4A8_STEP(st3, st2, s + 3);
-      }
-    } else {
-      W4A8_DMA(st3, 3);
-      W4A8_DMA(st4, 4);
-      W4A8_DMA(st5, 5);
-      W4A8_DMA(st6, 6);
-      for (int s = 0; s < nsteps; s += NS) {
-        W4A8_STEP(st0, st7, s + 0);
-        W4A8_STEP(st1, st0, s + 1);
-        W4A8_STEP(st2, st1, s + 2);
-        W4A8_STEP(st3, st2, s + 3);
-        W4A8_STEP(st4, st3, s + 4);
-        W4A8_STEP(st5, st4, s + 5);
-        W4A8_STEP(st6, st5, s + 6);
-        W4A8_STEP(st7, st6, s + 7);
-      }
+    if (kWiden) {
+      if (my_loads == kL) wait_vmcnt<2 * kL>();
+      else wait_vmcnt<2 * (kL - 1)>();
+      stage_barrier();
+      convert_scales(st0);
+    }
+    for (int s = 0; s < nsteps; s += 4) {
+      W4A8_STEP(st0, st1, st3, s + 0);
+      W4A8_STEP(st1, st2, st0, s + 1);
+      W4A8_STEP(st2, st3, st1, s + 2);
+      W4A8_STEP(st3, st0, st2, s + 3);
     }
 #undef W4A8_STEP
 #undef W4A8_DMA
@@ -510,10 +530,6 @@ Plan plan_gemm(int M, int K, int N) {
   return p;
 }
 
-// Four stages: deeper rings cost LDS that is better spent on occupancy
-// (measured: eight stages were slower on every prefill shape).
-constexpr int kRing = 4;
-
 size_t align256(size_t v) { return (v + 255) & ~static_cast<size_t>(255); }
 
 }  // namespace
@@ -546,7 +562,7 @@ int launch_gemm(const GemmArgs& a, int mode, hipStream_t stream) {
   // instead (at least as large as the scales would be) and never reads them.
   const uint16_t* ws = mode == 1 ? reinterpret_cast<const uint16_t*>(a.packed_w) : a.w_scales;
 #define W4A8_GEMM_LAUNCH(TN, TM, WN, WM, WK, MODE)                                                     \
-  hipLaunchKernelGGL((gemm_kernel<TN, TM, WN, WM, WK, MODE, kRing>), grid, dim3(64 * WN * WM * WK), 0,     \
+  hipLaunchKernelGGL((gemm_kernel<TN, TM, WN, WM, WK, MODE>), grid, dim3(64 * WN * WM * WK), 0,     \
                      stream, a.packed_w, ws, qxs, sxs, a.M, p.m_pad, a.K, a.N, p.tiles_n, p.tiles_m,       \
                      p.bps, a.out, a.sums, partials, sc->tickets)
 #define W4A8_GEMM_MODE(MODE)                                                                           \
