@@ -71,6 +71,7 @@ def load_library() -> ctypes.CDLL:
         "w4a8_linear": ([p, p, p, i64, i64, i64, p, p], i32),
         "w4a8_linear_path": ([p, p, p, i64, i64, i64, p, i32, p], i32),
         "w4a8_linear_argmax": ([p, p, p, i64, i64, i64, p, p, p], i32),
+        "w4a8_norm_linear_argmax": ([p, ctypes.c_float, p, p, i64, i64, i64, p, p, p], i32),
         "w4a8_quantize_act": ([p, i64, i64, p, p, p], i32),
         "w4a8_block_sums": ([p, p, i64, i64, i64, p, i32, p], i32),
         "w4a8_gemv_max_m": ([], i32),
@@ -192,6 +193,31 @@ def linear_argmax(x: torch.Tensor, packed: torch.Tensor, w_scales: torch.Tensor,
     _ready(x)
     _check("w4a8_linear_argmax", load_library().w4a8_linear_argmax(
         x.data_ptr(), packed.data_ptr(), w_scales.data_ptr(), m, k, n,
+        logits.data_ptr() if want_logits else None, argmax.data_ptr(), _stream(x)))
+    return (argmax, logits) if want_logits else argmax
+
+
+def norm_linear_argmax(x: torch.Tensor, packed: torch.Tensor, w_scales: torch.Tensor, eps: float = 1e-6,
+                       logits: torch.Tensor | bool | None = None, argmax: torch.Tensor | None = None):
+    """LM-head argmax on the fp32 residual stream: argmax of linear(fp16(x / rms(x))) per row.
+    Returns argmax int32 [M], or (argmax, logits) as linear_argmax does."""
+    _need(x, "x", torch.float32, 2)
+    k, n = _weights_shape(packed, w_scales)
+    m = x.shape[0]
+    if x.shape[1] != k:
+        raise ValueError(f"x has K = {x.shape[1]}, weights have K = {k}")
+    want_logits = logits is not None and logits is not False
+    if logits is True:
+        logits = torch.empty((m, n), dtype=torch.float32, device=x.device)
+    elif want_logits:
+        _need(logits, "logits", torch.float32, 2)
+    if argmax is None:
+        argmax = torch.empty((m,), dtype=torch.int32, device=x.device)
+    else:
+        _need(argmax, "argmax", torch.int32, 1)
+    _ready(x)
+    _check("w4a8_norm_linear_argmax", load_library().w4a8_norm_linear_argmax(
+        x.data_ptr(), eps, packed.data_ptr(), w_scales.data_ptr(), m, k, n,
         logits.data_ptr() if want_logits else None, argmax.data_ptr(), _stream(x)))
     return (argmax, logits) if want_logits else argmax
 

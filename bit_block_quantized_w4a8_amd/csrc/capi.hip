@@ -328,6 +328,33 @@ int w4a8_decoder_layer(float* x, int64_t M, int64_t H, const w4a8_weights* qkv, 
   do {                              \
     if ((rc = (call)) != W4A8_OK) return rc; \
   } while (0)
+  if (M == 1 && gemv_fused_supported(kGemvCast, true, Hi, static_cast<int>(qkv->N)) &&
+      gemv_fused_supported(kGemvGated, true, Hi, 2 * F)) {
+    // One token: four GEMV launches, with the normalisation in the prologue
+    // of qkv and gate/up and the cast, residual and gated product in the
+    // epilogues (the same values as the launches below, up to the summation
+    // order of the norm).
+    GemvArgs qa{nullptr, qkv->packed_w, qkv->w_scales, 1, Hi, static_cast<int>(qkv->N), q, nullptr, nullptr, nullptr};
+    qa.xf = x;
+    qa.eps = eps;
+    qa.y16 = a;
+    qa.n16 = Hi;
+    W4A8_STEP(launch_gemv(qa, kGemvCast, stream));
+    GemvArgs oa{a, o->packed_w, o->w_scales, 1, Hi, Hi, nullptr, nullptr, nullptr, nullptr};
+    oa.resid = x;
+    oa.alpha = residual_scale;
+    W4A8_STEP(launch_gemv(oa, kGemvResid, stream));
+    GemvArgs ga{nullptr, gate_up->packed_w, gate_up->w_scales, 1, Hi, 2 * F, nullptr, nullptr, nullptr, nullptr};
+    ga.xf = x;
+    ga.eps = eps;
+    ga.y16 = u;
+    W4A8_STEP(launch_gemv(ga, kGemvGated, stream));
+    GemvArgs da{u, down->packed_w, down->w_scales, 1, F, Hi, nullptr, nullptr, nullptr, nullptr};
+    da.resid = x;
+    da.alpha = residual_scale;
+    W4A8_STEP(launch_gemv(da, kGemvResid, stream));
+    return W4A8_OK;
+  }
   W4A8_STEP(launch_residual_norm_cast(x, nullptr, 0, 0.0f, eps, Mi, Hi, n, stream));
   W4A8_STEP(w4a8_linear(n, qkv->packed_w, qkv->w_scales, M, H, qkv->N, q, stream));
   W4A8_STEP(launch_cast_rows(q, qkv->N, Mi, Hi, a, stream));
@@ -339,6 +366,36 @@ int w4a8_decoder_layer(float* x, int64_t M, int64_t H, const w4a8_weights* qkv, 
   W4A8_STEP(launch_residual_norm_cast(x, d, H, residual_scale, eps, Mi, Hi, nullptr, stream));
 #undef W4A8_STEP
   return W4A8_OK;
+}
+
+int w4a8_norm_linear_argmax(const float* x, float eps, const uint8_t* packed_w, const uint16_t* w_scales,
+                            int64_t M, int64_t K, int64_t N, float* logits, int32_t* argmax, hipStream_t stream) {
+  W4A8_REQUIRE(x && aligned(x, 16), "x must be a 16-byte aligned pointer");
+  W4A8_REQUIRE(eps >= 0.0f, "eps must be non-negative");
+  // The weights and sizes are checked as for the fp16 entry point (x stands in for the fp16 input).
+  int rc = check_linear_args(reinterpret_cast<const uint16_t*>(x), packed_w, w_scales, M, K, N, kMaxArgmaxRows);
+  if (rc != W4A8_OK) return rc;
+  W4A8_REQUIRE(argmax && aligned(argmax, 4), "argmax must be a 4-byte aligned pointer");
+  W4A8_REQUIRE(!logits || aligned(logits, 16), "logits must be 16-byte aligned");
+  DeviceState* st = nullptr;
+  rc = current_state(&st);
+  if (rc != W4A8_OK) return rc;
+  const int Mi = static_cast<int>(M), Ki = static_cast<int>(K), Ni = static_cast<int>(N);
+  if (M == 1 && gemv_fused_supported(kGemvArgmax, true, Ki, Ni)) {
+    GemvArgs a{nullptr, packed_w, w_scales, 1, Ki, Ni, nullptr, nullptr, logits, argmax};
+    a.xf = x;
+    a.eps = eps;
+    return launch_gemv(a, kGemvArgmax, stream);
+  }
+  // Otherwise normalise into library scratch, then the fused-argmax GEMV.
+  Scratch* sc = nullptr;
+  rc = scratch_for(static_cast<size_t>(M) * K * 2, &sc);
+  if (rc != W4A8_OK) return rc;
+  uint16_t* y = static_cast<uint16_t*>(sc->work);
+  rc = launch_residual_norm_cast(const_cast<float*>(x), nullptr, 0, 0.0f, eps, Mi, Ki, y, stream);
+  if (rc != W4A8_OK) return rc;
+  GemvArgs a{y, packed_w, w_scales, Mi, Ki, Ni, nullptr, nullptr, logits, argmax};
+  return launch_gemv(a, kGemvArgmax, stream);
 }
 
 int w4a8_gemv_max_m(void) { return gemv_max_m(); }

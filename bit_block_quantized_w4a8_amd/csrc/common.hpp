@@ -46,6 +46,10 @@ int scratch_for(size_t work_bytes, Scratch** out);  // grows `work` if needed
 __device__ __forceinline__ float half_bits_to_float(uint32_t h) {
   return static_cast<float>(__builtin_bit_cast(_Float16, static_cast<unsigned short>(h)));
 }
+// fp32 -> fp16 bits, round to nearest even.
+__device__ __forceinline__ uint16_t float_to_half_bits(float v) {
+  return __builtin_bit_cast(unsigned short, static_cast<_Float16>(v));
+}
 
 // Quantise one 32-element activation block held by an aligned quad of lanes,
 // eight consecutive elements per lane (lane % 4 = g holds elements 8g .. 8g+7).

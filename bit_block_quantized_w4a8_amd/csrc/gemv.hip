@@ -4,38 +4,49 @@
 namespace w4a8 {
 namespace gemv_detail {
 
-W4A8_GEMV_INSTANTIATE(0, 1)
+W4A8_GEMV_INSTANTIATE(kGemvOut, 1, false)
 
-extern template int launch_rows_mr<0, 2>(const GemvArgs&, int, int, const uint16_t*, float*, int32_t*, float*,
-                                         int32_t*, Scratch*, unsigned long long*, hipStream_t);
-extern template int launch_rows_mr<0, 4>(const GemvArgs&, int, int, const uint16_t*, float*, int32_t*, float*,
-                                         int32_t*, Scratch*, unsigned long long*, hipStream_t);
-extern template int launch_rows_mr<0, 8>(const GemvArgs&, int, int, const uint16_t*, float*, int32_t*, float*,
-                                         int32_t*, Scratch*, unsigned long long*, hipStream_t);
-extern template int launch_rows_mr<1, 1>(const GemvArgs&, int, int, const uint16_t*, float*, int32_t*, float*,
-                                         int32_t*, Scratch*, unsigned long long*, hipStream_t);
-extern template int launch_rows_mr<1, 8>(const GemvArgs&, int, int, const uint16_t*, float*, int32_t*, float*,
-                                         int32_t*, Scratch*, unsigned long long*, hipStream_t);
-extern template int launch_rows_mr<2, 1>(const GemvArgs&, int, int, const uint16_t*, float*, int32_t*, float*,
-                                         int32_t*, Scratch*, unsigned long long*, hipStream_t);
-extern template int launch_rows_mr<2, 8>(const GemvArgs&, int, int, const uint16_t*, float*, int32_t*, float*,
-                                         int32_t*, Scratch*, unsigned long long*, hipStream_t);
+#define W4A8_GEMV_EXTERN(MODE, MR, NORM)                                                                  \
+  extern template int launch_rows_mr<MODE, MR, NORM>(const GemvArgs&, int, Scratch*, unsigned long long*, \
+                                                     hipStream_t);
+W4A8_GEMV_EXTERN(kGemvOut, 2, false)
+W4A8_GEMV_EXTERN(kGemvOut, 4, false)
+W4A8_GEMV_EXTERN(kGemvOut, 8, false)
+W4A8_GEMV_EXTERN(kGemvSums, 1, false)
+W4A8_GEMV_EXTERN(kGemvSums, 8, false)
+W4A8_GEMV_EXTERN(kGemvArgmax, 1, false)
+W4A8_GEMV_EXTERN(kGemvArgmax, 8, false)
+W4A8_GEMV_EXTERN(kGemvArgmax, 1, true)
+W4A8_GEMV_EXTERN(kGemvCast, 1, true)
+W4A8_GEMV_EXTERN(kGemvResid, 1, false)
+W4A8_GEMV_EXTERN(kGemvGated, 1, true)
+#undef W4A8_GEMV_EXTERN
+
+// Rows r0 .. r0 + rows - 1 of the call.
+GemvArgs row_slice(const GemvArgs& a, int r0, int rows) {
+  GemvArgs s = a;
+  s.M = rows;
+  if (a.x) s.x = a.x + static_cast<int64_t>(r0) * a.K;
+  if (a.xf) s.xf = a.xf + static_cast<int64_t>(r0) * a.K;
+  if (a.out) s.out = a.out + static_cast<int64_t>(r0) * a.N;
+  if (a.sums) s.sums = a.sums + static_cast<int64_t>(r0) * a.N * (a.K / kBlock);
+  if (a.logits) s.logits = a.logits + static_cast<int64_t>(r0) * a.N;
+  if (a.argmax) s.argmax = a.argmax + r0;
+  if (a.resid) s.resid = a.resid + static_cast<int64_t>(r0) * a.N;
+  return s;
+}
 
 template <int MODE>
 int launch_rows(const GemvArgs& a, int r0, int rows, Scratch* sc, hipStream_t stream) {
   const int cols = pick_columns(a.N);
-  const uint16_t* x = a.x + static_cast<int64_t>(r0) * a.K;
-  float* out = a.out ? a.out + static_cast<int64_t>(r0) * a.N : nullptr;
-  int32_t* sums = a.sums ? a.sums + static_cast<int64_t>(r0) * a.N * (a.K / kBlock) : nullptr;
-  float* logits = a.logits ? a.logits + static_cast<int64_t>(r0) * a.N : nullptr;
-  int32_t* am = a.argmax ? a.argmax + r0 : nullptr;
-  unsigned long long* slots = sc->slots + (MODE == 2 ? r0 : 0);
-  if (rows == 1) return launch_rows_mr<MODE, 1>(a, rows, cols, x, out, sums, logits, am, sc, slots, stream);
-  if constexpr (MODE == 0) {
-    if (rows == 2) return launch_rows_mr<MODE, 2>(a, rows, cols, x, out, sums, logits, am, sc, slots, stream);
-    if (rows <= 4) return launch_rows_mr<MODE, 4>(a, rows, cols, x, out, sums, logits, am, sc, slots, stream);
+  const GemvArgs s = row_slice(a, r0, rows);
+  unsigned long long* slots = sc->slots + (MODE == kGemvArgmax ? r0 : 0);
+  if (rows == 1) return launch_rows_mr<MODE, 1, false>(s, cols, sc, slots, stream);
+  if constexpr (MODE == kGemvOut) {
+    if (rows == 2) return launch_rows_mr<MODE, 2, false>(s, cols, sc, slots, stream);
+    if (rows <= 4) return launch_rows_mr<MODE, 4, false>(s, cols, sc, slots, stream);
   }
-  return launch_rows_mr<MODE, 8>(a, rows, cols, x, out, sums, logits, am, sc, slots, stream);
+  return launch_rows_mr<MODE, 8, false>(s, cols, sc, slots, stream);
 }
 
 }  // namespace gemv_detail
@@ -45,15 +56,36 @@ using gemv_detail::launch_rows;
 
 size_t gemv_scratch_bytes(int, int, int) { return 0; }
 
+bool gemv_fused_supported(int mode, bool norm, int K, int N) {
+  if (mode < kGemvCast && !(mode == kGemvArgmax && norm)) return false;
+  if (!norm) return true;
+  // The normalising prologue needs every block of the row in one chunk.
+  const int cols = gemv_detail::pick_columns(N);
+  const int loads = gemv_detail::pick_loads(K / kBlock, cols);
+  int r = loads <= 2 ? 2 : loads <= 4 ? 4 : cols == 8 ? 8 : loads <= 8 ? 8 : 16;
+  return (gemv_detail::kThreads / cols) * r >= K / kBlock;
+}
+
 int launch_gemv(const GemvArgs& a, int mode, hipStream_t stream) {
   Scratch* sc = nullptr;
   int rc = scratch_for(0, &sc);
   if (rc != W4A8_OK) return rc;
+  if (mode >= kGemvCast || a.xf) {
+    // Fused decoder-layer kernels: one token row.
+    if (a.M != 1 || !gemv_fused_supported(mode, a.xf != nullptr, a.K, a.N))
+      return hip_fail(hipErrorInvalidValue, "gemv: fused launch outside its shapes");
+    const int cols = gemv_detail::pick_columns(a.N);
+    using gemv_detail::launch_rows_mr;
+    if (mode == kGemvCast) return launch_rows_mr<kGemvCast, 1, true>(a, cols, sc, sc->slots, stream);
+    if (mode == kGemvResid) return launch_rows_mr<kGemvResid, 1, false>(a, cols, sc, sc->slots, stream);
+    if (mode == kGemvGated) return launch_rows_mr<kGemvGated, 1, true>(a, cols, sc, sc->slots, stream);
+    return launch_rows_mr<kGemvArgmax, 1, true>(a, cols, sc, sc->slots, stream);
+  }
   for (int r0 = 0; r0 < a.M; r0 += kRowsMax) {
     const int rows = a.M - r0 < kRowsMax ? a.M - r0 : kRowsMax;
-    if (mode == 0) rc = launch_rows<0>(a, r0, rows, sc, stream);
-    else if (mode == 1) rc = launch_rows<1>(a, r0, rows, sc, stream);
-    else rc = launch_rows<2>(a, r0, rows, sc, stream);
+    if (mode == kGemvOut) rc = launch_rows<kGemvOut>(a, r0, rows, sc, stream);
+    else if (mode == kGemvSums) rc = launch_rows<kGemvSums>(a, r0, rows, sc, stream);
+    else rc = launch_rows<kGemvArgmax>(a, r0, rows, sc, stream);
     if (rc != W4A8_OK) return rc;
   }
   return W4A8_OK;

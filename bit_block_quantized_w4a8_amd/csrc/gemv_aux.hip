@@ -3,9 +3,9 @@
 
 namespace w4a8 {
 namespace gemv_detail {
-W4A8_GEMV_INSTANTIATE(1, 1)
-W4A8_GEMV_INSTANTIATE(1, 8)
-W4A8_GEMV_INSTANTIATE(2, 1)
-W4A8_GEMV_INSTANTIATE(2, 8)
+W4A8_GEMV_INSTANTIATE(kGemvSums, 1, false)
+W4A8_GEMV_INSTANTIATE(kGemvSums, 8, false)
+W4A8_GEMV_INSTANTIATE(kGemvArgmax, 1, false)
+W4A8_GEMV_INSTANTIATE(kGemvArgmax, 8, false)
 }  // namespace gemv_detail
 }  // namespace w4a8

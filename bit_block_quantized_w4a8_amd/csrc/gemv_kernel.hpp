@@ -8,15 +8,24 @@
 // x-techcon article, section on moving less data).  Here every workgroup
 // quantises the activations it needs into LDS, then streams its weights.
 //
-// Work split: a workgroup owns C consecutive output columns (C = 8 .. 64) over
-// all of K, so no result crosses workgroups.  Its 256 lanes form C columns x
+// Work split: a workgroup owns C output columns (C = 8 .. 64) over all of K,
+// so no result crosses workgroups.  Its 256 lanes form C columns x
 // S = 256 / C block slots; one load instruction of a wave reads 64 / C blocks
-// of C columns, i.e. 64/C runs of 16*C contiguous bytes of the K-block-major
-// weights.  K is walked in chunks of 64 blocks: the weight loads of a chunk
-// are issued first, the chunk's activations are quantised into LDS while they
-// are in flight, and then every lane forms its blocks' int8 dot products.
-// Slots are reduced with cross-lane shuffles and waves through LDS, in a fixed
-// order, so results are identical from run to run.
+// of C columns, i.e. runs of 16*C contiguous bytes of the K-block-major
+// weights.  K is walked in chunks: the weight loads of a chunk are issued
+// first, the chunk's activations are quantised into LDS while they are in
+// flight, and then every lane forms its blocks' int8 dot products.  Slots are
+// reduced with cross-lane shuffles and waves through LDS, in a fixed order,
+// so results are identical from run to run.
+//
+// Decoder-layer fusion (the pages fold residual and element-wise work into
+// neighbouring operators: sciencestack summary of the ML Drift paper,
+// Figure 4): with NORM the input is the fp32 residual stream x, and the
+// prologue forms fp16(x / sqrt(mean(x^2) + eps)) before quantising it; the
+// epilogue can also write an fp16 copy of the leading columns (kGemvCast),
+// add the result into the residual stream (kGemvResid), or multiply paired
+// gate and up columns (kGemvGated: a workgroup owns C/2 columns f and their
+// partners N/2 + f).
 #pragma once
 
 #include "kernels.hpp"
@@ -44,26 +53,45 @@ __device__ __forceinline__ uint32_t atomic_add_agent(uint32_t* p, uint32_t v) {
   return __hip_atomic_fetch_add(p, v, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
 }
 
+// Output column of lane column c in tile `tile`.
+template <int MODE, int C>
+__device__ __forceinline__ int column_of(int tile, int c, int N) {
+  if constexpr (MODE == kGemvGated) {
+    constexpr int kHalf = C / 2;
+    return c < kHalf ? tile * kHalf + c : N / 2 + tile * kHalf + (c - kHalf);
+  } else {
+    return tile * C + c;
+  }
+}
+
 // C: output columns per workgroup; R: weight loads per lane per chunk, so a
 // chunk holds R * 256 / C blocks.  The host picks R to cover K in one chunk
 // when it can (every weight load of the workgroup then in flight at once).
-template <int MR, int MODE, int C, int R>
-__global__ __launch_bounds__(kThreads) void gemv_kernel(
-    const uint16_t* __restrict__ x, const uint8_t* __restrict__ pw, const uint16_t* __restrict__ ws,
-    int M, int K, int N, float* __restrict__ out, int32_t* __restrict__ sums,
-    float* __restrict__ logits, int32_t* __restrict__ argmax_out, uint32_t* __restrict__ tickets,
-    unsigned long long* __restrict__ slots, int never_set) {
+// NORM: the input is the fp32 residual stream, normalised in the prologue
+// (the host guarantees one chunk and one batch of quantisation tasks).
+template <int MR, int MODE, int C, int R, bool NORM>
+__global__ __launch_bounds__(kThreads) void gemv_kernel(GemvArgs a, uint32_t* __restrict__ tickets,
+                                                        unsigned long long* __restrict__ slots, int never_set) {
   constexpr int S = kThreads / C;           // block slots per round
   constexpr int kChunkBlocks = S * R;
   static_assert(kChunkBlocks <= kMaxChunkBlocks && R <= kMaxLoadsPerLane, "chunk too large");
+  static_assert(MODE != kGemvGated || C >= 2, "gated tiles pair columns");
   // Activation loads per lane per batch: every task of a full chunk, at most 8.
   constexpr int XQ = (MR * kChunkBlocks * 4 + kThreads - 1) / kThreads < 8
                          ? (MR * kChunkBlocks * 4 + kThreads - 1) / kThreads : 8;
 
   __shared__ uint32_t q_lds[MR][kChunkBlocks][8];  // int8 codes, 8 dwords per block
   __shared__ float s_lds[MR][kChunkBlocks];         // sx / 16 per block
+  __shared__ float red[kWaves][MR][C];
+
+  const uint16_t* __restrict__ x = a.x;
+  const uint8_t* __restrict__ pw = a.packed_w;
+  const uint16_t* __restrict__ ws = a.w_scales;
+  const int M = a.M, K = a.K, N = a.N;
 
   const int tid = threadIdx.x;
+  const int lane = tid & 63;
+  const int wave = tid >> 6;
   const int c = tid % C;
   const int slot = tid / C;
   // Neighbouring column tiles share 128-byte lines of the weight scales (a
@@ -72,7 +100,7 @@ __global__ __launch_bounds__(kThreads) void gemv_kernel(
   // the same XCD: otherwise every XCD would fetch the shared lines again.
   const int tiles = gridDim.x;
   const int tile = (tiles & 7) == 0 ? (blockIdx.x & 7) * (tiles >> 3) + (blockIdx.x >> 3) : blockIdx.x;
-  const int n = tile * C + c;
+  const int n = column_of<MODE, C>(tile, c, N);
   const int nb = K / kBlock;
 
   float acc[MR];
@@ -92,8 +120,21 @@ __global__ __launch_bounds__(kThreads) void gemv_kernel(
     //    weight load of the chunk, and quantisation starts as soon as the
     //    activations arrive while the weights are still in flight.
     uint4 xv[XQ];
+    float4 xa[NORM ? XQ : 1], xb[NORM ? XQ : 1];
+    if constexpr (NORM) {
 #pragma unroll
-    for (int j = 0; j < XQ; ++j) xv[j] = load_x16(x, K, kb0, nbc, min(j * kThreads + tid, tasks - 1));
+      for (int j = 0; j < XQ; ++j) {
+        const int g = min(j * kThreads + tid, tasks - 1);
+        const int m = g / (nbc * 4);
+        const int e = g % (nbc * 4);
+        const float* p = a.xf + static_cast<int64_t>(m) * K + static_cast<int64_t>(kb0) * kBlock + 8 * e;
+        xa[j] = *reinterpret_cast<const float4*>(p);
+        xb[j] = *reinterpret_cast<const float4*>(p + 4);
+      }
+    } else {
+#pragma unroll
+      for (int j = 0; j < XQ; ++j) xv[j] = load_x16(x, K, kb0, nbc, min(j * kThreads + tid, tasks - 1));
+    }
     __builtin_amdgcn_sched_barrier(0);  // keep the activation loads ahead of the weights
     uint4 w[R];
     uint32_t s[R];
@@ -102,40 +143,97 @@ __global__ __launch_bounds__(kThreads) void gemv_kernel(
       const int bl = min(slot + r * S, nbc - 1);
       const int64_t g = static_cast<int64_t>(kb0 + bl) * N + n;
       w[r] = *reinterpret_cast<const uint4*>(pw + g * kPackedBytes);
-      s[r] = MODE == 1 ? 0u : ws[g];  // the block-sum export reads no scales
+      s[r] = MODE == kGemvSums ? 0u : ws[g];  // the block-sum export reads no scales
     }
     __builtin_amdgcn_sched_barrier(0);
 
-    // 2. Quantise into LDS.  The first batch is straight-line code after the
-    //    loads; further batches (many rows or a long chunk) loop behind it.
-    auto quantize_batch = [&](int t0) {
-#pragma unroll
-      for (int j = 0; j < XQ; ++j) {
-        if (t0 + j * kThreads < tasks) {  // uniform: skips batches with no task
-          const int g = t0 + j * kThreads + tid;
-          float v[8];
-          unpack_half8(xv[j], v);
-          float scale;
-          const uint2 codes = quantize8_group4(v, &scale);
-          if (g < tasks) {
-            const int m = g / (nbc * 4);
-            const int e = g % (nbc * 4);
-            *reinterpret_cast<uint2*>(&q_lds[m][e >> 2][2 * (e & 3)]) = codes;
-            if ((e & 3) == 0) s_lds[m][e >> 2] = scale * 0.0625f;
-          }
-        }
+    // 2. Quantise into LDS.
+    auto store_codes = [&](int g, const float* v) __attribute__((always_inline)) {
+      float scale;
+      const uint2 codes = quantize8_group4(v, &scale);
+      if (g < tasks) {
+        const int m = g / (nbc * 4);
+        const int e = g % (nbc * 4);
+        *reinterpret_cast<uint2*>(&q_lds[m][e >> 2][2 * (e & 3)]) = codes;
+        if ((e & 3) == 0) s_lds[m][e >> 2] = scale * 0.0625f;
       }
     };
-    quantize_batch(0);
-    // A use of every first-batch load outside the branches above: without it
-    // the compiler sinks the loads of later batches into their branch, behind
-    // the weight loads, where they would wait for every weight to arrive.
+    if constexpr (NORM) {
+      // Sum of squares of each row (one chunk holds the whole row), in a fixed
+      // order: per lane, then across the wave, then the four waves.
+      float ss[MR];
 #pragma unroll
-    for (int j = 0; j < XQ; ++j) keep ^= xv[j].x;
-    for (int t0 = XQ * kThreads; t0 < tasks; t0 += XQ * kThreads) {
+      for (int m = 0; m < MR; ++m) ss[m] = 0.0f;
 #pragma unroll
-      for (int j = 0; j < XQ; ++j) xv[j] = load_x16(x, K, kb0, nbc, min(t0 + j * kThreads + tid, tasks - 1));
-      quantize_batch(t0);
+      for (int j = 0; j < XQ; ++j) {
+        const int g = j * kThreads + tid;
+        if (g < tasks) {
+          const int m = g / (nbc * 4);
+          float q = xa[j].x * xa[j].x;
+          q = fmaf(xa[j].y, xa[j].y, q);
+          q = fmaf(xa[j].z, xa[j].z, q);
+          q = fmaf(xa[j].w, xa[j].w, q);
+          q = fmaf(xb[j].x, xb[j].x, q);
+          q = fmaf(xb[j].y, xb[j].y, q);
+          q = fmaf(xb[j].z, xb[j].z, q);
+          q = fmaf(xb[j].w, xb[j].w, q);
+#pragma unroll
+          for (int mm = 0; mm < MR; ++mm)
+            if (m == mm) ss[mm] += q;
+        }
+      }
+#pragma unroll
+      for (int m = 0; m < MR; ++m) {
+#pragma unroll
+        for (int off = 32; off >= 1; off >>= 1) ss[m] += __shfl_xor(ss[m], off);
+        if (lane == 0) red[wave][m][0] = ss[m];
+      }
+      __syncthreads();
+      float inv[MR];
+#pragma unroll
+      for (int m = 0; m < MR; ++m)
+        inv[m] = 1.0f / sqrtf((((red[0][m][0] + red[1][m][0]) + red[2][m][0]) + red[3][m][0]) /
+                                  static_cast<float>(K) + a.eps);
+#pragma unroll
+      for (int j = 0; j < XQ; ++j) {
+        if (j * kThreads < tasks) {  // uniform
+          const int g = j * kThreads + tid;
+          const int m = min(g, tasks - 1) / (nbc * 4);
+          float im = inv[0];
+#pragma unroll
+          for (int mm = 1; mm < MR; ++mm)
+            if (m == mm) im = inv[mm];
+          const float raw[8] = {xa[j].x, xa[j].y, xa[j].z, xa[j].w, xb[j].x, xb[j].y, xb[j].z, xb[j].w};
+          float v[8];
+#pragma unroll
+          for (int k = 0; k < 8; ++k) v[k] = half_bits_to_float(float_to_half_bits(raw[k] * im));
+          store_codes(g, v);
+        }
+      }
+    } else {
+      // The first batch is straight-line code after the loads; further
+      // batches (many rows or a long chunk) loop behind it.
+      auto quantize_batch = [&](int t0) {
+#pragma unroll
+        for (int j = 0; j < XQ; ++j) {
+          if (t0 + j * kThreads < tasks) {  // uniform: skips batches with no task
+            float v[8];
+            unpack_half8(xv[j], v);
+            store_codes(t0 + j * kThreads + tid, v);
+          }
+        }
+      };
+      quantize_batch(0);
+      // A use of every first-batch load outside the branches above: without it
+      // the compiler sinks the loads of later batches into their branch, behind
+      // the weight loads, where they would wait for every weight to arrive.
+#pragma unroll
+      for (int j = 0; j < XQ; ++j) keep ^= xv[j].x;
+      for (int t0 = XQ * kThreads; t0 < tasks; t0 += XQ * kThreads) {
+#pragma unroll
+        for (int j = 0; j < XQ; ++j) xv[j] = load_x16(x, K, kb0, nbc, min(t0 + j * kThreads + tid, tasks - 1));
+        quantize_batch(t0);
+      }
     }
     __syncthreads();
 
@@ -156,20 +254,20 @@ __global__ __launch_bounds__(kThreads) void gemv_kernel(
             const uint4 qa = *reinterpret_cast<const uint4*>(&q_lds[m][bl][0]);
             const uint4 qb = *reinterpret_cast<const uint4*>(&q_lds[m][bl][4]);
             // a = bits(1.5 * 2^23) + 16 * I   (bytes of l*, h* hold 16 * weight)
-            int a = kMagicBits;
-            a = __builtin_amdgcn_sdot4(static_cast<int>(l0), static_cast<int>(qa.x), a, false);
-            a = __builtin_amdgcn_sdot4(static_cast<int>(l1), static_cast<int>(qa.y), a, false);
-            a = __builtin_amdgcn_sdot4(static_cast<int>(l2), static_cast<int>(qa.z), a, false);
-            a = __builtin_amdgcn_sdot4(static_cast<int>(l3), static_cast<int>(qa.w), a, false);
-            a = __builtin_amdgcn_sdot4(static_cast<int>(h0), static_cast<int>(qb.x), a, false);
-            a = __builtin_amdgcn_sdot4(static_cast<int>(h1), static_cast<int>(qb.y), a, false);
-            a = __builtin_amdgcn_sdot4(static_cast<int>(h2), static_cast<int>(qb.z), a, false);
-            a = __builtin_amdgcn_sdot4(static_cast<int>(h3), static_cast<int>(qb.w), a, false);
-            if (MODE == 1) {
-              sums[(static_cast<int64_t>(m) * N + n) * nb + kb0 + bl] = (a - kMagicBits) >> 4;
+            int acc_i = kMagicBits;
+            acc_i = __builtin_amdgcn_sdot4(static_cast<int>(l0), static_cast<int>(qa.x), acc_i, false);
+            acc_i = __builtin_amdgcn_sdot4(static_cast<int>(l1), static_cast<int>(qa.y), acc_i, false);
+            acc_i = __builtin_amdgcn_sdot4(static_cast<int>(l2), static_cast<int>(qa.z), acc_i, false);
+            acc_i = __builtin_amdgcn_sdot4(static_cast<int>(l3), static_cast<int>(qa.w), acc_i, false);
+            acc_i = __builtin_amdgcn_sdot4(static_cast<int>(h0), static_cast<int>(qb.x), acc_i, false);
+            acc_i = __builtin_amdgcn_sdot4(static_cast<int>(h1), static_cast<int>(qb.y), acc_i, false);
+            acc_i = __builtin_amdgcn_sdot4(static_cast<int>(h2), static_cast<int>(qb.z), acc_i, false);
+            acc_i = __builtin_amdgcn_sdot4(static_cast<int>(h3), static_cast<int>(qb.w), acc_i, false);
+            if (MODE == kGemvSums) {
+              a.sums[(static_cast<int64_t>(m) * N + n) * nb + kb0 + bl] = (acc_i - kMagicBits) >> 4;
             } else {
               // t = RN(16 * I * sw); acc += t * (sx / 16)
-              const float t = fmaf(__int_as_float(a), swf, cst);
+              const float t = fmaf(__int_as_float(acc_i), swf, cst);
               acc[m] = fmaf(t, s_lds[m][bl], acc[m]);
             }
           }
@@ -180,7 +278,7 @@ __global__ __launch_bounds__(kThreads) void gemv_kernel(
   }
 
   if (never_set) tickets[0] = keep;  // `never_set` is 0: the store only keeps `keep` alive
-  if (MODE == 1) return;
+  if (MODE == kGemvSums) return;
 
   // Slots of one wave: lanes c, c + C, c + 2C, ... hold the same column.
 #pragma unroll
@@ -188,9 +286,6 @@ __global__ __launch_bounds__(kThreads) void gemv_kernel(
 #pragma unroll
     for (int off = C; off < 64; off <<= 1) acc[m] += __shfl_xor(acc[m], off);
 
-  __shared__ float red[kWaves][MR][C];
-  const int lane = tid & 63;
-  const int wave = tid >> 6;
   if (lane < C) {
 #pragma unroll
     for (int m = 0; m < MR; ++m) red[wave][m][lane] = acc[m];
@@ -207,16 +302,42 @@ __global__ __launch_bounds__(kThreads) void gemv_kernel(
     v[m] = t;
   }
 
-  if (MODE == 0) {
+  if constexpr (MODE == kGemvOut || MODE == kGemvCast) {
     if (lane < C) {
 #pragma unroll
-      for (int m = 0; m < MR; ++m)
-        if (m < M) out[static_cast<int64_t>(m) * N + n] = v[m];
+      for (int m = 0; m < MR; ++m) {
+        if (m < M) {
+          if (MODE == kGemvOut || a.out) a.out[static_cast<int64_t>(m) * N + n] = v[m];
+          if (MODE == kGemvCast && n < a.n16) a.y16[static_cast<int64_t>(m) * a.n16 + n] = float_to_half_bits(v[m]);
+        }
+      }
+    }
+    return;
+  }
+  if constexpr (MODE == kGemvResid) {
+    if (lane < C) {
+#pragma unroll
+      for (int m = 0; m < MR; ++m) {
+        if (m < M) {
+          float* xr = a.resid + static_cast<int64_t>(m) * N + n;
+          *xr = fmaf(a.alpha, v[m], *xr);
+        }
+      }
+    }
+    return;
+  }
+  if constexpr (MODE == kGemvGated) {
+    constexpr int kHalf = C / 2;
+#pragma unroll
+    for (int m = 0; m < MR; ++m) {
+      const float up = __shfl(v[m], (lane + kHalf) & 63);  // lane < C/2: its up column
+      if (lane < kHalf && m < M)
+        a.y16[static_cast<int64_t>(m) * (N / 2) + n] = float_to_half_bits(v[m] * up);
     }
     return;
   }
 
-  // MODE 2: argmax over all columns of each row.  Keys meet in one 64-bit
+  // kGemvArgmax: argmax over all columns of each row.  Keys meet in one 64-bit
   // atomic max per row; the workgroup that finishes last publishes the index
   // and clears the slots.  Every cross-workgroup access is a device-scope
   // atomic, and each atomic waits for the previous one's result.
@@ -224,7 +345,7 @@ __global__ __launch_bounds__(kThreads) void gemv_kernel(
 #pragma unroll
   for (int m = 0; m < MR; ++m) {
     if (m >= M) break;
-    if (logits && lane < C) logits[static_cast<int64_t>(m) * N + n] = v[m];
+    if (a.logits && lane < C) a.logits[static_cast<int64_t>(m) * N + n] = v[m];
     unsigned long long key = lane < C ? argmax_key(v[m], static_cast<uint32_t>(n)) : 0ull;
 #pragma unroll
     for (int off = 32; off >= 1; off >>= 1) {
@@ -244,7 +365,7 @@ __global__ __launch_bounds__(kThreads) void gemv_kernel(
       for (int m = 0; m < M; ++m) {
         const unsigned long long k =
             __hip_atomic_exchange(&slots[m], 0ull, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-        argmax_out[m] = static_cast<int32_t>(0xFFFFFFFFu - static_cast<uint32_t>(k & 0xFFFFFFFFull));
+        a.argmax[m] = static_cast<int32_t>(0xFFFFFFFFu - static_cast<uint32_t>(k & 0xFFFFFFFFull));
       }
       __hip_atomic_store(&tickets[0], 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
     }
@@ -270,17 +391,16 @@ inline int pick_loads(int nb, int cols) {
   return r;
 }
 
-template <int MODE, int MR, int C>
-int launch_rows_c(const GemvArgs& a, int rows, int loads, const uint16_t* x, float* out, int32_t* sums,
-                  float* logits, int32_t* am, Scratch* sc, unsigned long long* slots, hipStream_t stream) {
+// `a` already points at the launch's first row.
+template <int MODE, int MR, int C, bool NORM>
+int launch_rows_c(const GemvArgs& a, int loads, Scratch* sc, unsigned long long* slots, hipStream_t stream) {
   const dim3 grid(a.N / C);
   // The block-sum export, the argmax and 8-row launches use one load count per
-  // tile width (surplus loads are clamped duplicates); only the decode GEMV of
-  // 1, 2 and 4 rows is specialised on K, to keep the build small.
-  constexpr bool kSpecialise = MODE == 0 && MR <= 4;
-#define W4A8_GEMV_LAUNCH(R)                                                                                  \
-  hipLaunchKernelGGL((gemv_kernel<MR, MODE, C, R>), grid, dim3(kThreads), 0, stream, x, a.packed_w, a.w_scales, \
-                     rows, a.K, a.N, out, sums, logits, am, sc->tickets, slots, 0)
+  // tile width (surplus loads are clamped duplicates); the decode GEMV of 1, 2
+  // and 4 rows and the fused one-row kernels are specialised on K.
+  constexpr bool kSpecialise = (MODE == kGemvOut && MR <= 4) || NORM || MODE >= kGemvCast;
+#define W4A8_GEMV_LAUNCH(R) \
+  hipLaunchKernelGGL((gemv_kernel<MR, MODE, C, R, NORM>), grid, dim3(kThreads), 0, stream, a, sc->tickets, slots, 0)
   if constexpr (!kSpecialise) {
     if constexpr (C == 8) W4A8_GEMV_LAUNCH(8);
     else W4A8_GEMV_LAUNCH(16);
@@ -299,23 +419,22 @@ int launch_rows_c(const GemvArgs& a, int rows, int loads, const uint16_t* x, flo
   return W4A8_OK;
 }
 
-template <int MODE, int MR>
-int launch_rows_mr(const GemvArgs& a, int rows, int cols, const uint16_t* x, float* out,
-                   int32_t* sums, float* logits, int32_t* am, Scratch* sc, unsigned long long* slots,
-                   hipStream_t stream) {
+template <int MODE, int MR, bool NORM>
+int launch_rows_mr(const GemvArgs& a, int cols, Scratch* sc, unsigned long long* slots, hipStream_t stream) {
   const int loads = pick_loads(a.K / kBlock, cols);
-  if (cols == 64) return launch_rows_c<MODE, MR, 64>(a, rows, loads, x, out, sums, logits, am, sc, slots, stream);
-  if (cols == 32) return launch_rows_c<MODE, MR, 32>(a, rows, loads, x, out, sums, logits, am, sc, slots, stream);
-  if (cols == 16) return launch_rows_c<MODE, MR, 16>(a, rows, loads, x, out, sums, logits, am, sc, slots, stream);
-  return launch_rows_c<MODE, MR, 8>(a, rows, loads, x, out, sums, logits, am, sc, slots, stream);
+  if (cols == 64) return launch_rows_c<MODE, MR, 64, NORM>(a, loads, sc, slots, stream);
+  if (cols == 32) return launch_rows_c<MODE, MR, 32, NORM>(a, loads, sc, slots, stream);
+  if (cols == 16) return launch_rows_c<MODE, MR, 16, NORM>(a, loads, sc, slots, stream);
+  return launch_rows_c<MODE, MR, 8, NORM>(a, loads, sc, slots, stream);
 }
 
-// launch_rows_mr is instantiated in gemv.hip (MODE 0, 1 row), gemv_rows.hip
-// (MODE 0, 2, 4 and 8 rows) and gemv_aux.hip (block-sum export and argmax).
+// launch_rows_mr is instantiated in gemv.hip (decode GEMV, 1 row), gemv_rows.hip
+// (2, 4 and 8 rows), gemv_aux.hip (block-sum export and argmax) and
+// gemv_fused.hip (the one-row decoder-layer kernels).
 
-#define W4A8_GEMV_INSTANTIATE(MODE, MR)                                                                \
-  template int launch_rows_mr<MODE, MR>(const GemvArgs&, int, int, const uint16_t*, float*, int32_t*, \
-                                        float*, int32_t*, Scratch*, unsigned long long*, hipStream_t);
+#define W4A8_GEMV_INSTANTIATE(MODE, MR, NORM)                                                      \
+  template int launch_rows_mr<MODE, MR, NORM>(const GemvArgs&, int, Scratch*, unsigned long long*, \
+                                              hipStream_t);
 
 }  // namespace gemv_detail
 }  // namespace w4a8

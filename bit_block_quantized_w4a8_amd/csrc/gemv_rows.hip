@@ -3,8 +3,8 @@
 
 namespace w4a8 {
 namespace gemv_detail {
-W4A8_GEMV_INSTANTIATE(0, 2)
-W4A8_GEMV_INSTANTIATE(0, 4)
-W4A8_GEMV_INSTANTIATE(0, 8)
+W4A8_GEMV_INSTANTIATE(kGemvOut, 2, false)
+W4A8_GEMV_INSTANTIATE(kGemvOut, 4, false)
+W4A8_GEMV_INSTANTIATE(kGemvOut, 8, false)
 }  // namespace gemv_detail
 }  // namespace w4a8

@@ -15,18 +15,36 @@ int launch_quantize_stage(const uint16_t* x, int M, int M_pad, int K, uint8_t* q
                           hipStream_t stream);
 
 // Decode GEMV (int8 dot products, activations quantised in the kernel).
-// mode: 0 = scaled output, 1 = integer block sums, 2 = fused argmax (+ optional logits).
+enum GemvMode {
+  kGemvOut = 0,     // out[m][n] = y (fp32)
+  kGemvSums = 1,    // integer block sums
+  kGemvArgmax = 2,  // fused argmax over the row (+ optional logits)
+  kGemvCast = 3,    // out (nullable) and y16[m][n] = fp16(y) for n < n16
+  kGemvResid = 4,   // resid[m][n] = fma(alpha, y, resid[m][n])
+  kGemvGated = 5,   // y16[m][f] = fp16(y[f] * y[N/2 + f]) for f < N/2
+};
 struct GemvArgs {
-  const uint16_t* x;
+  const uint16_t* x;     // fp16 [M][K]; unused when xf is set
   const uint8_t* packed_w;
   const uint16_t* w_scales;
   int M, K, N;
-  float* out;            // mode 0
-  int32_t* sums;         // mode 1
-  float* logits;         // mode 2, may be null
-  int32_t* argmax;       // mode 2
+  float* out;            // kGemvOut, kGemvCast (nullable)
+  int32_t* sums;         // kGemvSums
+  float* logits;         // kGemvArgmax, may be null
+  int32_t* argmax;       // kGemvArgmax
+  // Decoder-layer fusion (one token row):
+  const float* xf = nullptr;  // fp32 [M][K] residual stream, normalised in the prologue:
+                              // x_in = fp16(xf / sqrt(mean(xf^2) + eps))
+  float eps = 0.0f;
+  float* resid = nullptr;     // kGemvResid
+  float alpha = 0.0f;
+  uint16_t* y16 = nullptr;    // kGemvCast: [M][n16]; kGemvGated: [M][N/2]
+  int n16 = 0;
 };
 int launch_gemv(const GemvArgs& a, int mode, hipStream_t stream);
+// Whether a fused (one-row) GEMV launch supports the shape: the normalising
+// prologue needs the whole row of K in one chunk.
+bool gemv_fused_supported(int mode, bool norm, int K, int N);
 size_t gemv_scratch_bytes(int M, int K, int N);
 
 // Prefill GEMM (int8 MFMA on pre-quantised activations).

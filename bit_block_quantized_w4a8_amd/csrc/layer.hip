@@ -23,10 +23,6 @@ namespace {
 
 constexpr int kGlueThreads = 256;
 
-__device__ __forceinline__ uint16_t float_to_half_bits(float v) {
-  return __builtin_bit_cast(unsigned short, static_cast<_Float16>(v));
-}
-
 // Fixed-order workgroup sum: wave shuffles, then the 4 wave totals in order.
 __device__ __forceinline__ float block_sum(float v, float* red) {
 #pragma unroll

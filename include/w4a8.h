@@ -167,11 +167,33 @@ W4A8_API int w4a8_decoder_layer_workspace(int64_t M, int64_t H, const w4a8_weigh
  * not touched by other calls in flight.  Allocates nothing (the linears use the
  * library scratch as w4a8_linear does), so a warmed-up call can be captured in
  * a HIP graph.  M must not exceed 65536.
+ * With M = 1, when the GEMV tiles of qkv and gate/up cover all of K = H in one
+ * chunk (H <= 2048 for N >= 32768, H <= 4096 for N >= 16384, H <= 8192
+ * otherwise), the layer runs as four GEMV launches: the normalisation sits in the prologue of qkv and
+ * gate/up, the fp16 cast of q[:, :H], the residual adds and the gated product
+ * in the epilogues (the pages fold such element-wise work into neighbouring
+ * operators: sciencestack summary of the ML Drift paper, Figure 4).  The
+ * result equals the nine-launch chain up to the summation order inside
+ * rms(x); q is still written to the workspace.
  */
 W4A8_API int w4a8_decoder_layer(float* x, int64_t M, int64_t H, const w4a8_weights* qkv,
                                 const w4a8_weights* o, const w4a8_weights* gate_up,
                                 const w4a8_weights* down, float residual_scale, float eps,
                                 void* workspace, size_t workspace_bytes, hipStream_t stream);
+
+/*
+ * LM-head argmax on the residual stream: argmax[m] = first index of the
+ * maximum over n of w4a8_linear(fp16(x[m] / rms(x[m])))[n], with rms as in
+ * w4a8_residual_norm_cast; logits (nullable) receive the fp32 row.
+ *   x       fp32 [M][K], 16-byte aligned, not modified
+ *   others  as w4a8_linear_argmax (M <= 64)
+ * M = 1 runs one GEMV launch with the normalisation in its prologue when K
+ * fits one GEMV chunk; otherwise the rows are normalised into library scratch
+ * first.
+ */
+W4A8_API int w4a8_norm_linear_argmax(const float* x, float eps, const uint8_t* packed_w,
+                                     const uint16_t* w_scales, int64_t M, int64_t K, int64_t N,
+                                     float* logits, int32_t* argmax, hipStream_t stream);
 
 /* Largest M that W4A8_PATH_AUTO sends to the decode GEMV. */
 W4A8_API int w4a8_gemv_max_m(void);

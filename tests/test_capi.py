@@ -14,7 +14,7 @@ def lib():
 
 def test_exports_every_declared_symbol(lib):
     names = w4.declared_functions()
-    assert len(names) == 12, names
+    assert len(names) == 13, names
     for name in names:
         assert hasattr(lib, name), name
 
@@ -60,6 +60,20 @@ def test_other_entry_points_validate(lib):
     assert lib.w4a8_block_sums(P(ALIGNED), P(ALIGNED), 1, 64, 128, P(ALIGNED), 7, None) == w4.W4A8_EINVAL
     assert lib.w4a8_pack_weights(P(ALIGNED), P(ALIGNED), 64, 100, P(ALIGNED), P(ALIGNED), None) == w4.W4A8_EINVAL
     assert lib.w4a8_pack_weights(P(ALIGNED), P(ALIGNED), 64, 128, P(ALIGNED + 1), P(ALIGNED), None) == w4.W4A8_EINVAL
+
+
+def test_norm_linear_argmax_validates(lib):
+    f = ctypes.c_float
+    ok = dict(x=ALIGNED, eps=1e-6, pw=ALIGNED, ws=ALIGNED, m=1, k=64, n=128, logits=0, am=ALIGNED)
+
+    def call(**kw):
+        a = {**ok, **kw}
+        return lib.w4a8_norm_linear_argmax(P(a["x"]), f(a["eps"]), P(a["pw"]), P(a["ws"]), a["m"], a["k"], a["n"],
+                                           P(a["logits"]), P(a["am"]), None)
+    for bad in [dict(x=0), dict(x=ALIGNED + 8), dict(eps=-1.0), dict(m=65), dict(k=48), dict(n=96),
+                dict(am=0), dict(am=ALIGNED + 2), dict(logits=ALIGNED + 4), dict(pw=ALIGNED + 8)]:
+        assert call(**bad) == w4.W4A8_EINVAL, bad
+    assert call() == w4.W4A8_ENOINIT
 
 
 def test_python_binding_rejects_cpu_tensors():

@@ -125,9 +125,32 @@ def test_chain_of_layers_and_lm_head_argmax():
     assert np.array_equal(am, tf)
 
 
+@pytest.mark.parametrize("m,h,vocab", [(1, 256, 4096), (1, 2048, 262144), (2, 256, 4096), (1, 8192, 4096)])
+def test_norm_linear_argmax(m, h, vocab):
+    """LM-head argmax on the fp32 residual stream (one fused launch for one row; rows normalised
+    first otherwise), against the oracle and against the two-step GPU path."""
+    qh = synth.int4_values(synth.rng(50 + h, 0), vocab, h)
+    sh = synth.weight_scales(synth.rng(50 + h, 1), vocab, h)
+    head = w4.Weights.pack(dev(qh), dev(sh))
+    x = (np.random.default_rng(h + m).standard_normal((m, h)) * 3).astype(np.float32)
+    am, logits = w4.norm_linear_argmax(dev(x), head.packed, head.w_scales, eps=EPS, logits=True)
+    am, logits = host(am), host(logits)
+    ref = oracle.linear(oracle.rms_norm_fp16(x, EPS), qh, sh)
+    assert np.abs(logits - ref).max() < 1e-2
+    assert np.array_equal(am, oracle.argmax_first(logits))  # the fused argmax of its own logits
+    want = oracle.argmax_first(ref)
+    for r in range(m):
+        if am[r] != want[r]:
+            assert ref[r, want[r]] - ref[r, am[r]] < 1e-2, (am, want)
+    # two-step path: normalise, then the fp16 fused-argmax GEMV
+    hd = w4.residual_norm_cast(dev(x), eps=EPS)
+    am2, logits2 = w4.linear_argmax(hd, head.packed, head.w_scales, logits=True)
+    assert np.abs(host(logits2) - logits).max() < 1e-2
+
+
 def test_graph_replay_matches_eager():
-    """A captured token (2 layers + norm + fused argmax) replays bit-identically to eager runs,
-    with eager work and synchronisations between the replays."""
+    """A captured token (2 layers + norm + fused argmax, and the one-launch normalising argmax)
+    replays bit-identically to eager runs, with eager work and synchronisations between the replays."""
     h, n_qkv, f, vocab = 256, 320, 512, 2048
     layers = [_weights(40 + i, h, n_qkv, f)[1] for i in range(2)]
     qh = synth.int4_values(synth.rng(41, 0), vocab, h)
@@ -139,19 +162,22 @@ def test_graph_replay_matches_eager():
                      dtype=torch.uint8, device=DEV)
     hb = torch.empty((1, h), dtype=torch.float16, device=DEV)
     am = torch.empty((1,), dtype=torch.int32, device=DEV)
+    am_fused = torch.empty((1,), dtype=torch.int32, device=DEV)
 
     def token():
         for lw in layers:
             w4.decoder_layer(x, lw["qkv"], lw["o"], lw["gate_up"], lw["down"], SCALE, EPS, ws)
         w4.residual_norm_cast(x, eps=EPS, y=hb)
         w4.linear_argmax(hb, head.packed, head.w_scales, argmax=am)
+        w4.norm_linear_argmax(x, head.packed, head.w_scales, eps=EPS, argmax=am_fused)
 
-    eager_x, eager_am = [], []
+    eager_x, eager_am, eager_fused = [], [], []
     x.copy_(dev(x0))
     for _ in range(3):
         token()
         eager_x.append(host(x).copy())
         eager_am.append(int(host(am)[0]))
+        eager_fused.append(int(host(am_fused)[0]))
 
     side = torch.cuda.Stream()
     side.wait_stream(torch.cuda.current_stream())
@@ -167,5 +193,6 @@ def test_graph_replay_matches_eager():
         graph.replay()
         assert np.array_equal(host(x), eager_x[i]), f"replay {i}"
         assert int(host(am)[0]) == eager_am[i], f"replay {i}"
+        assert int(host(am_fused)[0]) == eager_fused[i], f"replay {i}"
         scratch = w4.linear(dev(np.ones((2, h), np.float16)), head.packed, head.w_scales)  # eager work between
         host(scratch)
