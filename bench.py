@@ -456,7 +456,7 @@ def main():
                                "down 8192x2048; weights cold (rotation over replicas)",
                    "M": 1, "hidden": 2048, "replicas": dec["replicas"],
                    "rotation_bytes": dec["rotation_bytes"], "frac_hbm_peak": round(value / HBM_PEAK_GBS, 4)},
-        "roofline": {"bound": "hbm", "kernel": "gemv_kernel<1,0,8> (gate_up 2048x16384, M=1)",
+        "roofline": {"bound": "hbm", "kernel": "gemv_kernel<1,0,32,8> (gate_up 2048x16384, M=1)",
                      "achieved": gu["GB_s"], "peak": HBM_PEAK_GBS, "unit": "GB/s",
                      "frac": round(gu["GB_s"] / HBM_PEAK_GBS, 4), "traffic": measured_traffic(),
                      "bytes_per_launch": gu["bytes"], "us_per_launch": gu["us"]},

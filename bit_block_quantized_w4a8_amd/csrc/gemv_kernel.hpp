@@ -107,6 +107,13 @@ __global__ __launch_bounds__(kThreads) void gemv_kernel(GemvArgs a, uint32_t* __
 #pragma unroll
   for (int m = 0; m < MR; ++m) acc[m] = 0.0f;
   uint32_t keep = 0;
+  // The residual entries this workgroup updates, fetched before the weights
+  // so that the epilogue does not wait on a memory round trip.
+  float resid_in[MR];
+  if constexpr (MODE == kGemvResid) {
+#pragma unroll
+    for (int m = 0; m < MR; ++m) resid_in[m] = a.resid[static_cast<int64_t>(min(m, M - 1)) * N + n];
+  }
 
   for (int kb0 = 0; kb0 < nb; kb0 += kChunkBlocks) {
     const int nbc = min(kChunkBlocks, nb - kb0);
@@ -318,10 +325,7 @@ __global__ __launch_bounds__(kThreads) void gemv_kernel(GemvArgs a, uint32_t* __
     if (lane < C) {
 #pragma unroll
       for (int m = 0; m < MR; ++m) {
-        if (m < M) {
-          float* xr = a.resid + static_cast<int64_t>(m) * N + n;
-          *xr = fmaf(a.alpha, v[m], *xr);
-        }
+        if (m < M) a.resid[static_cast<int64_t>(m) * N + n] = fmaf(a.alpha, v[m], resid_in[m]);
       }
     }
     return;
