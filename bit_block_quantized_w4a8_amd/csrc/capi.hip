@@ -154,12 +154,12 @@ int w4a8_init(int device) {
     return W4A8_EUNSUPPORTED;
   }
   Scratch& sc = st.sc;
-  sc.bytes = kMaxTickets * sizeof(uint32_t) + kMaxArgmaxRows * sizeof(unsigned long long);
+  sc.bytes = kMaxTickets * sizeof(uint32_t) + kMaxArgmaxRows * kArgmaxSpread * sizeof(unsigned long long);
   W4A8_HIP(hipMalloc(&sc.base, sc.bytes));
   W4A8_HIP(hipMemset(sc.base, 0, sc.bytes));
   sc.slots = static_cast<unsigned long long*>(sc.base);
   sc.tickets = reinterpret_cast<uint32_t*>(static_cast<char*>(sc.base) +
-                                           kMaxArgmaxRows * sizeof(unsigned long long));
+                                           kMaxArgmaxRows * kArgmaxSpread * sizeof(unsigned long long));
   W4A8_HIP(hipMalloc(&sc.work, kInitialWork));
   sc.work_bytes = kInitialWork;
   W4A8_HIP(hipDeviceSynchronize());

@@ -34,12 +34,15 @@ struct Scratch {
   void* base = nullptr;
   size_t bytes = 0;
   uint32_t* tickets = nullptr;       // split-K / argmax completion counters, self-resetting
-  unsigned long long* slots = nullptr;  // argmax keys, self-resetting
+  unsigned long long* slots = nullptr;  // argmax keys [kMaxArgmaxRows][kArgmaxSpread], reset by the finaliser
   void* work = nullptr;              // staging: quantised activations, split-K partials
   size_t work_bytes = 0;
 };
 constexpr int kMaxTickets = 1 << 16;
 constexpr int kMaxArgmaxRows = 64;
+// Argmax keys of one row are spread over this many slots (tile % spread), so
+// the per-workgroup atomic maxima of a launch do not all meet on one address.
+constexpr int kArgmaxSpread = 64;
 int scratch_for(size_t work_bytes, Scratch** out);  // grows `work` if needed
 
 // ------------------------------------------------------------- device side

@@ -40,7 +40,7 @@ template <int MODE>
 int launch_rows(const GemvArgs& a, int r0, int rows, Scratch* sc, hipStream_t stream) {
   const int cols = pick_columns(a.N);
   const GemvArgs s = row_slice(a, r0, rows);
-  unsigned long long* slots = sc->slots + (MODE == kGemvArgmax ? r0 : 0);
+  unsigned long long* slots = sc->slots + (MODE == kGemvArgmax ? r0 * kArgmaxSpread : 0);
   if (rows == 1) return launch_rows_mr<MODE, 1, false>(s, cols, sc, slots, stream);
   if constexpr (MODE == kGemvOut) {
     if (rows == 2) return launch_rows_mr<MODE, 2, false>(s, cols, sc, slots, stream);
@@ -55,6 +55,33 @@ using gemv_detail::kRowsMax;
 using gemv_detail::launch_rows;
 
 size_t gemv_scratch_bytes(int, int, int) { return 0; }
+
+namespace {
+// One wave per row: the maximum key over the row's slots gives the index
+// (lowest column among equal values); the slots are cleared for the next
+// launch.  Device-scope accesses: the slots were written by device-scope
+// atomics of the previous kernel.
+__global__ __launch_bounds__(64) void argmax_finalize_kernel(unsigned long long* __restrict__ slots,
+                                                             int32_t* __restrict__ argmax_out) {
+  static_assert(kArgmaxSpread == 64, "one lane per slot");
+  const int m = blockIdx.x;
+  unsigned long long* row = slots + m * kArgmaxSpread;
+  unsigned long long key = __hip_atomic_load(&row[threadIdx.x], __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+#pragma unroll
+  for (int off = 32; off >= 1; off >>= 1) {
+    const unsigned long long o = __shfl_xor(key, off);
+    key = o > key ? o : key;
+  }
+  __hip_atomic_store(&row[threadIdx.x], 0ull, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+  if (threadIdx.x == 0) argmax_out[m] = static_cast<int32_t>(0xFFFFFFFFu - static_cast<uint32_t>(key & 0xFFFFFFFFull));
+}
+
+int launch_argmax_finalize(Scratch* sc, int M, int32_t* argmax, hipStream_t stream) {
+  hipLaunchKernelGGL(argmax_finalize_kernel, dim3(M), dim3(64), 0, stream, sc->slots, argmax);
+  W4A8_HIP(hipGetLastError());
+  return W4A8_OK;
+}
+}  // namespace
 
 bool gemv_fused_supported(int mode, bool norm, int K, int N) {
   if (mode < kGemvCast && !(mode == kGemvArgmax && norm)) return false;
@@ -79,7 +106,9 @@ int launch_gemv(const GemvArgs& a, int mode, hipStream_t stream) {
     if (mode == kGemvCast) return launch_rows_mr<kGemvCast, 1, true>(a, cols, sc, sc->slots, stream);
     if (mode == kGemvResid) return launch_rows_mr<kGemvResid, 1, false>(a, cols, sc, sc->slots, stream);
     if (mode == kGemvGated) return launch_rows_mr<kGemvGated, 1, true>(a, cols, sc, sc->slots, stream);
-    return launch_rows_mr<kGemvArgmax, 1, true>(a, cols, sc, sc->slots, stream);
+    rc = launch_rows_mr<kGemvArgmax, 1, true>(a, cols, sc, sc->slots, stream);
+    if (rc != W4A8_OK) return rc;
+    return launch_argmax_finalize(sc, 1, a.argmax, stream);
   }
   for (int r0 = 0; r0 < a.M; r0 += kRowsMax) {
     const int rows = a.M - r0 < kRowsMax ? a.M - r0 : kRowsMax;
@@ -88,6 +117,7 @@ int launch_gemv(const GemvArgs& a, int mode, hipStream_t stream) {
     else rc = launch_rows<kGemvArgmax>(a, r0, rows, sc, stream);
     if (rc != W4A8_OK) return rc;
   }
+  if (mode == kGemvArgmax) return launch_argmax_finalize(sc, a.M, a.argmax, stream);
   return W4A8_OK;
 }
 

@@ -341,11 +341,10 @@ __global__ __launch_bounds__(kThreads) void gemv_kernel(GemvArgs a, uint32_t* __
     return;
   }
 
-  // kGemvArgmax: argmax over all columns of each row.  Keys meet in one 64-bit
-  // atomic max per row; the workgroup that finishes last publishes the index
-  // and clears the slots.  Every cross-workgroup access is a device-scope
-  // atomic, and each atomic waits for the previous one's result.
-  bool never = false;  // stays false: depends on every returned key, see below
+  // kGemvArgmax: argmax over all columns of each row.  Each workgroup folds
+  // its best key into one of kArgmaxSpread slots of the row with an atomic
+  // max whose result it does not wait for; argmax_finalize_kernel, launched
+  // next on the stream, reduces the slots, publishes the index and clears them.
 #pragma unroll
   for (int m = 0; m < MR; ++m) {
     if (m >= M) break;
@@ -357,22 +356,8 @@ __global__ __launch_bounds__(kThreads) void gemv_kernel(GemvArgs a, uint32_t* __
       key = o > key ? o : key;
     }
     if (lane == 0)
-      never |= __hip_atomic_fetch_max(&slots[m], key, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) == ~0ull;
-  }
-  if (lane == 0) {
-    // A key of a finite value is below 2^64 - 1, so `never` is false and `inc`
-    // is 1; the data dependency on every returned key orders the ticket after
-    // all the maxima.
-    const uint32_t inc = never ? 2u : 1u;
-    const uint32_t done = atomic_add_agent(&tickets[0], inc);
-    if (done == gridDim.x - 1) {
-      for (int m = 0; m < M; ++m) {
-        const unsigned long long k =
-            __hip_atomic_exchange(&slots[m], 0ull, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-        a.argmax[m] = static_cast<int32_t>(0xFFFFFFFFu - static_cast<uint32_t>(k & 0xFFFFFFFFull));
-      }
-      __hip_atomic_store(&tickets[0], 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-    }
+      __hip_atomic_fetch_max(&slots[m * kArgmaxSpread + (tile & (kArgmaxSpread - 1))], key, __ATOMIC_RELAXED,
+                             __HIP_MEMORY_SCOPE_AGENT);
   }
 }
 
