@@ -86,19 +86,22 @@ int launch_quantize_export(const uint16_t* x, int M, int K, int8_t* qx, float* s
 //       a wave's 64 fragment reads touch 64 consecutive 16-byte slots;
 //   sxs [K/32][M_pad] fp32 block scales.
 // Rows M .. M_pad-1 are written as zeros (codes and scales).
-// Group lane g holds elements 8g .. 8g+7, which belong at byte 8 * (0, 2, 1, 3)[g]
-// of the row's 32 codes: half (0, 1, 0, 1)[g], offset (0, 0, 8, 8)[g].
+// A quad of lanes quantises one (row, block); consecutive quads take
+// consecutive rows of the same block, so a wave writes whole runs of the
+// staging layout.  Group lane g holds elements 8g .. 8g+7, which belong at
+// byte 8 * (0, 2, 1, 3)[g] of the row's 32 codes: half (0, 1, 0, 1)[g],
+// offset (0, 0, 8, 8)[g].
 __global__ __launch_bounds__(256) void quantize_stage_kernel(const uint16_t* __restrict__ x, int M,
                                                              int M_pad, int K,
                                                              uint8_t* __restrict__ qxs,
                                                              float* __restrict__ sxs) {
-  const int64_t per_row = K / 8;
   const int64_t t = static_cast<int64_t>(blockIdx.x) * blockDim.x + threadIdx.x;
-  if (t >= per_row * M_pad) return;
-  const int64_t m = t / per_row;
-  const int64_t e = t % per_row;
-  const int64_t b = e / 4;
-  const int g = static_cast<int>(e & 3);
+  if (t >= static_cast<int64_t>(K / 8) * M_pad) return;
+  const int g = static_cast<int>(t & 3);
+  const int64_t q = t >> 2;
+  const int64_t m = q % M_pad;
+  const int64_t b = q / M_pad;
+  const int64_t e = 4 * b + g;  // 8-element group index within the row
   float v[8] = {0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f};
   if (m < M) unpack_half8(*reinterpret_cast<const uint4*>(x + m * K + 8 * e), v);
   float scale;
