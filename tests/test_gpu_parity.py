@@ -228,6 +228,25 @@ def test_prefill_projection_sampled(proj):
     assert_close(got[:, cols], oracle.linear(x, qw[cols], sw[cols]), proj)
 
 
+# One shape per GEMM tile plan: 128 x 32 (four waves along n), K split over four
+# waves at M <= 32, 128 x 64, K split at 32 < M <= 64 and M > 64, eight-wave
+# 128 x 128, and K split across workgroups (few tiles, long K) at both M ranges.
+GEMM_PLANS = [(8, 64, 65536), (8, 96, 192), (40, 64, 65536), (40, 1024, 640), (130, 64, 32768),
+              (130, 1024, 640), (8, 8192, 128), (130, 8192, 64)]
+
+
+@pytest.mark.parametrize("m,k,n", GEMM_PLANS)
+def test_gemm_every_tile_plan(m, k, n):
+    x, qw, sw = inputs(m * 11 + k + n, m, k, n, outliers=True)
+    packed, ws = packed_on_gpu(qw, sw)
+    xd = dev(x)
+    assert_close(host(w4.linear(xd, packed, ws, path=w4.PATH_GEMM)), oracle.linear(x, qw, sw),
+                 f"GEMM M={m} K={k} N={n}")
+    qx, _ = oracle.quantize_activations(x)
+    got = host(w4.block_sums(xd, packed, path=w4.PATH_GEMM))
+    assert np.array_equal(got.astype(np.int64), oracle.block_sums(qx, qw))
+
+
 @pytest.mark.parametrize("m", synth.WORKLOADS["wide"]["M"])
 def test_wide_linear_full(m):
     x, qw, sw = synth.workload_inputs("wide", m)["wide"]
