@@ -297,6 +297,16 @@ def bench_e2e(w4, torch, synth, timer, decode_steps):
         token()
     graph_s, ids_graph = decode(graph.replay)
 
+    # The LM head alone (302 MB of weights and scales, more than the 256 MB memory-side cache,
+    # so every launch streams it from HBM): plain linear and normalising argmax.
+    head_bytes = algorithmic_bytes(1, *synth.LM_HEAD_SHAPE)
+    x16 = torch.zeros((1, h), dtype=torch.float16, device=dev)
+    logits_out = torch.empty((1, synth.LM_HEAD_SHAPE[1]), dtype=torch.float32, device=dev)
+    head_linear_ms = back_to_back(torch, timer, lambda i: w4.linear(x16, head.packed, head.w_scales,
+                                                                     out=logits_out), 20)
+    head_argmax_ms = back_to_back(torch, timer, lambda i: w4.norm_linear_argmax(
+        x, head.packed, head.w_scales, eps=E2E_EPS, argmax=am), 20)
+
     tok_s_stream = decode_steps / stream_s
     tok_s_graph = decode_steps / graph_s
     ceiling = HBM_PEAK_GBS * 1e9 / token_bytes
@@ -313,6 +323,12 @@ def bench_e2e(w4, torch, synth, timer, decode_steps):
         "frac_of_hbm_token_ceiling": round(tok_s_graph / ceiling, 4),
         "hbm_token_ceiling_tok_s": round(ceiling, 1),
         "graph_ids_match_stream": ids_graph == ids_stream,
+        "lm_head": {"K": h, "N": synth.LM_HEAD_SHAPE[1], "bytes": head_bytes,
+                    "linear_us": round(head_linear_ms * 1e3, 2),
+                    "linear_GB_s": round(head_bytes / (head_linear_ms * 1e6), 1),
+                    "linear_frac_hbm": round(head_bytes / (head_linear_ms * 1e6) / HBM_PEAK_GBS, 4),
+                    "norm_argmax_us": round(head_argmax_ms * 1e3, 2),
+                    "note": "M=1 GEMV streaming 302 MB (above the memory-side cache) per launch"},
         "first_ids": ids_stream[:8],
         "note": "sync every token: the argmax index is copied to the host after each step",
     }

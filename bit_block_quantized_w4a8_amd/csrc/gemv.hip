@@ -87,8 +87,9 @@ bool gemv_fused_supported(int mode, bool norm, int K, int N) {
   if (mode < kGemvCast && !(mode == kGemvArgmax && norm)) return false;
   if (!norm) return true;
   // The normalising prologue needs every block of the row in one chunk.
+  // (The fused modes other than the residual epilogue always run 256 threads.)
   const int cols = gemv_detail::pick_columns(N);
-  const int loads = gemv_detail::pick_loads(K / kBlock, cols);
+  const int loads = gemv_detail::pick_loads(K / kBlock, cols, gemv_detail::kThreads);
   int r = loads <= 2 ? 2 : loads <= 4 ? 4 : cols == 8 ? 8 : loads <= 8 ? 8 : 16;
   return (gemv_detail::kThreads / cols) * r >= K / kBlock;
 }

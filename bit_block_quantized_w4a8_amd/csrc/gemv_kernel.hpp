@@ -9,8 +9,8 @@
 // quantises the activations it needs into LDS, then streams its weights.
 //
 // Work split: a workgroup owns C output columns (C = 8 .. 64) over all of K,
-// so no result crosses workgroups.  Its 256 lanes form C columns x
-// S = 256 / C block slots; one load instruction of a wave reads 64 / C blocks
+// so no result crosses workgroups.  Its T lanes (256, or 512 for long K and
+// 8-column tiles) form C columns x S = T / C block slots; one load instruction of a wave reads 64 / C blocks
 // of C columns, i.e. runs of 16*C contiguous bytes of the K-block-major
 // weights.  K is walked in chunks: the weight loads of a chunk are issued
 // first, the chunk's activations are quantised into LDS while they are in
@@ -34,8 +34,8 @@
 namespace w4a8 {
 namespace gemv_detail {
 
-constexpr int kThreads = 256;
-constexpr int kWaves = kThreads / 64;
+constexpr int kThreads = 256;      // default workgroup size
+constexpr int kWideThreads = 512;  // long-K, narrow tiles (see launch_rows_c)
 constexpr int kRowsMax = 8;        // token rows per launch
 constexpr int kMaxLoadsPerLane = 16;
 constexpr int kMaxChunkBlocks = 256;
@@ -69,16 +69,16 @@ __device__ __forceinline__ int column_of(int tile, int c, int N) {
 // when it can (every weight load of the workgroup then in flight at once).
 // NORM: the input is the fp32 residual stream, normalised in the prologue
 // (the host guarantees one chunk and one batch of quantisation tasks).
-template <int MR, int MODE, int C, int R, bool NORM>
-__global__ __launch_bounds__(kThreads) void gemv_kernel(GemvArgs a, uint32_t* __restrict__ tickets,
-                                                        unsigned long long* __restrict__ slots, int never_set) {
-  constexpr int S = kThreads / C;           // block slots per round
+template <int MR, int MODE, int C, int R, bool NORM, int T>
+__global__ __launch_bounds__(T) void gemv_kernel(GemvArgs a, uint32_t* __restrict__ tickets,
+                                                 unsigned long long* __restrict__ slots, int never_set) {
+  constexpr int kWaves = T / 64;
+  constexpr int S = T / C;                  // block slots per round
   constexpr int kChunkBlocks = S * R;
   static_assert(kChunkBlocks <= kMaxChunkBlocks && R <= kMaxLoadsPerLane, "chunk too large");
   static_assert(MODE != kGemvGated || C >= 2, "gated tiles pair columns");
   // Activation loads per lane per batch: every task of a full chunk, at most 8.
-  constexpr int XQ = (MR * kChunkBlocks * 4 + kThreads - 1) / kThreads < 8
-                         ? (MR * kChunkBlocks * 4 + kThreads - 1) / kThreads : 8;
+  constexpr int XQ = (MR * kChunkBlocks * 4 + T - 1) / T < 8 ? (MR * kChunkBlocks * 4 + T - 1) / T : 8;
 
   __shared__ uint32_t q_lds[MR][kChunkBlocks][8];  // int8 codes, 8 dwords per block
   __shared__ float s_lds[MR][kChunkBlocks];         // sx / 16 per block
@@ -131,7 +131,7 @@ __global__ __launch_bounds__(kThreads) void gemv_kernel(GemvArgs a, uint32_t* __
     if constexpr (NORM) {
 #pragma unroll
       for (int j = 0; j < XQ; ++j) {
-        const int g = min(j * kThreads + tid, tasks - 1);
+        const int g = min(j * T + tid, tasks - 1);
         const int m = g / (nbc * 4);
         const int e = g % (nbc * 4);
         const float* p = a.xf + static_cast<int64_t>(m) * K + static_cast<int64_t>(kb0) * kBlock + 8 * e;
@@ -140,7 +140,7 @@ __global__ __launch_bounds__(kThreads) void gemv_kernel(GemvArgs a, uint32_t* __
       }
     } else {
 #pragma unroll
-      for (int j = 0; j < XQ; ++j) xv[j] = load_x16(x, K, kb0, nbc, min(j * kThreads + tid, tasks - 1));
+      for (int j = 0; j < XQ; ++j) xv[j] = load_x16(x, K, kb0, nbc, min(j * T + tid, tasks - 1));
     }
     __builtin_amdgcn_sched_barrier(0);  // keep the activation loads ahead of the weights
     uint4 w[R];
@@ -173,7 +173,7 @@ __global__ __launch_bounds__(kThreads) void gemv_kernel(GemvArgs a, uint32_t* __
       for (int m = 0; m < MR; ++m) ss[m] = 0.0f;
 #pragma unroll
       for (int j = 0; j < XQ; ++j) {
-        const int g = j * kThreads + tid;
+        const int g = j * T + tid;
         if (g < tasks) {
           const int m = g / (nbc * 4);
           float q = xa[j].x * xa[j].x;
@@ -198,13 +198,16 @@ __global__ __launch_bounds__(kThreads) void gemv_kernel(GemvArgs a, uint32_t* __
       __syncthreads();
       float inv[MR];
 #pragma unroll
-      for (int m = 0; m < MR; ++m)
-        inv[m] = 1.0f / sqrtf((((red[0][m][0] + red[1][m][0]) + red[2][m][0]) + red[3][m][0]) /
-                                  static_cast<float>(K) + a.eps);
+      for (int m = 0; m < MR; ++m) {
+        float t = red[0][m][0];
+#pragma unroll
+        for (int wv = 1; wv < kWaves; ++wv) t += red[wv][m][0];
+        inv[m] = 1.0f / sqrtf(t / static_cast<float>(K) + a.eps);
+      }
 #pragma unroll
       for (int j = 0; j < XQ; ++j) {
-        if (j * kThreads < tasks) {  // uniform
-          const int g = j * kThreads + tid;
+        if (j * T < tasks) {  // uniform
+          const int g = j * T + tid;
           const int m = min(g, tasks - 1) / (nbc * 4);
           float im = inv[0];
 #pragma unroll
@@ -223,10 +226,10 @@ __global__ __launch_bounds__(kThreads) void gemv_kernel(GemvArgs a, uint32_t* __
       auto quantize_batch = [&](int t0) {
 #pragma unroll
         for (int j = 0; j < XQ; ++j) {
-          if (t0 + j * kThreads < tasks) {  // uniform: skips batches with no task
+          if (t0 + j * T < tasks) {  // uniform: skips batches with no task
             float v[8];
             unpack_half8(xv[j], v);
-            store_codes(t0 + j * kThreads + tid, v);
+            store_codes(t0 + j * T + tid, v);
           }
         }
       };
@@ -236,9 +239,9 @@ __global__ __launch_bounds__(kThreads) void gemv_kernel(GemvArgs a, uint32_t* __
       // the weight loads, where they would wait for every weight to arrive.
 #pragma unroll
       for (int j = 0; j < XQ; ++j) keep ^= xv[j].x;
-      for (int t0 = XQ * kThreads; t0 < tasks; t0 += XQ * kThreads) {
+      for (int t0 = XQ * T; t0 < tasks; t0 += XQ * T) {
 #pragma unroll
-        for (int j = 0; j < XQ; ++j) xv[j] = load_x16(x, K, kb0, nbc, min(t0 + j * kThreads + tid, tasks - 1));
+        for (int j = 0; j < XQ; ++j) xv[j] = load_x16(x, K, kb0, nbc, min(t0 + j * T + tid, tasks - 1));
         quantize_batch(t0);
       }
     }
@@ -371,25 +374,29 @@ inline int pick_columns(int N) {
   return 8;
 }
 
+// Workgroup size: 512 threads for 8-column tiles over more than 4096 K (every
+// lane then quantises and multiplies half as many blocks), else 256.
+inline int pick_threads(int K, int cols, int rows) { return cols == 8 && K > 4096 && rows == 1 ? kWideThreads : kThreads; }
+
 // Weight loads per lane: enough for all K blocks in one chunk, capped by
 // registers (16) and LDS (256 blocks of codes per row).
-inline int pick_loads(int nb, int cols) {
-  const int slots = kThreads / cols;
+inline int pick_loads(int nb, int cols, int threads) {
+  const int slots = threads / cols;
   int r = 2;
   while (r < kMaxLoadsPerLane && r * slots < nb && 2 * r * slots <= kMaxChunkBlocks) r *= 2;
   return r;
 }
 
 // `a` already points at the launch's first row.
-template <int MODE, int MR, int C, bool NORM>
-int launch_rows_c(const GemvArgs& a, int loads, Scratch* sc, unsigned long long* slots, hipStream_t stream) {
+template <int MODE, int MR, int C, bool NORM, int T>
+int launch_rows_ct(const GemvArgs& a, int loads, Scratch* sc, unsigned long long* slots, hipStream_t stream) {
   const dim3 grid(a.N / C);
   // The block-sum export, the argmax and 8-row launches use one load count per
   // tile width (surplus loads are clamped duplicates); the decode GEMV of 1, 2
   // and 4 rows and the fused one-row kernels are specialised on K.
   constexpr bool kSpecialise = (MODE == kGemvOut && MR <= 4) || NORM || MODE >= kGemvCast;
 #define W4A8_GEMV_LAUNCH(R) \
-  hipLaunchKernelGGL((gemv_kernel<MR, MODE, C, R, NORM>), grid, dim3(kThreads), 0, stream, a, sc->tickets, slots, 0)
+  hipLaunchKernelGGL((gemv_kernel<MR, MODE, C, R, NORM, T>), grid, dim3(T), 0, stream, a, sc->tickets, slots, 0)
   if constexpr (!kSpecialise) {
     if constexpr (C == 8) W4A8_GEMV_LAUNCH(8);
     else W4A8_GEMV_LAUNCH(16);
@@ -397,24 +404,36 @@ int launch_rows_c(const GemvArgs& a, int loads, Scratch* sc, unsigned long long*
     W4A8_GEMV_LAUNCH(2);
   } else if (loads <= 4) {
     W4A8_GEMV_LAUNCH(4);
-  } else if constexpr (C == 8) {
+  } else if constexpr (C == 8 && T == kThreads) {
     W4A8_GEMV_LAUNCH(8);  // 8 columns: 8 loads per lane already cover 256 blocks
-  } else {
+  } else if constexpr (T == kThreads) {
     if (loads <= 8) W4A8_GEMV_LAUNCH(8);
     else W4A8_GEMV_LAUNCH(16);
+  } else {
+    return hip_fail(hipErrorInvalidValue, "gemv: no wide-workgroup kernel for this K");
   }
 #undef W4A8_GEMV_LAUNCH
   W4A8_HIP(hipGetLastError());
   return W4A8_OK;
 }
 
+template <int MODE, int MR, int C, bool NORM>
+int launch_rows_c(const GemvArgs& a, Scratch* sc, unsigned long long* slots, hipStream_t stream) {
+  constexpr bool kWideOk = C == 8 && MR == 1 && (MODE == kGemvOut || MODE == kGemvResid) && !NORM;
+  if constexpr (kWideOk) {
+    if (pick_threads(a.K, C, MR) == kWideThreads)
+      return launch_rows_ct<MODE, MR, C, NORM, kWideThreads>(a, pick_loads(a.K / kBlock, C, kWideThreads), sc,
+                                                              slots, stream);
+  }
+  return launch_rows_ct<MODE, MR, C, NORM, kThreads>(a, pick_loads(a.K / kBlock, C, kThreads), sc, slots, stream);
+}
+
 template <int MODE, int MR, bool NORM>
 int launch_rows_mr(const GemvArgs& a, int cols, Scratch* sc, unsigned long long* slots, hipStream_t stream) {
-  const int loads = pick_loads(a.K / kBlock, cols);
-  if (cols == 64) return launch_rows_c<MODE, MR, 64, NORM>(a, loads, sc, slots, stream);
-  if (cols == 32) return launch_rows_c<MODE, MR, 32, NORM>(a, loads, sc, slots, stream);
-  if (cols == 16) return launch_rows_c<MODE, MR, 16, NORM>(a, loads, sc, slots, stream);
-  return launch_rows_c<MODE, MR, 8, NORM>(a, loads, sc, slots, stream);
+  if (cols == 64) return launch_rows_c<MODE, MR, 64, NORM>(a, sc, slots, stream);
+  if (cols == 32) return launch_rows_c<MODE, MR, 32, NORM>(a, sc, slots, stream);
+  if (cols == 16) return launch_rows_c<MODE, MR, 16, NORM>(a, sc, slots, stream);
+  return launch_rows_c<MODE, MR, 8, NORM>(a, sc, slots, stream);
 }
 
 // launch_rows_mr is instantiated in gemv.hip (decode GEMV, 1 row), gemv_rows.hip
