@@ -9,7 +9,7 @@ bytes of one layer / time of one layer, in GB/s; a step is one such layer.
 
 Also reported, each on its own keys: the prefill stage (the same projections at
 M = 512 with outlier channels, int8 TOPS against the int8 MFMA peak), the
-decode-batch sweep on K = 4096, N = 14336 at M in {1, 4, 8, 16} for both
+decode-batch sweep on K = 4096, N = 14336 at M in {1, 2, 3, 4, 8, 16} for both
 kernels, the end-to-end token loop (26 layers + a 262144-entry LM head with
 the fused argmax, 512-token prefill, 128 decode steps with a host sync every
 token; stream-ordered and replayed from a HIP graph), the roofline of the
@@ -40,6 +40,8 @@ REPLICA_BYTES_MIN = 1 << 30    # weight rotation size for cold-cache timing
 TRAFFIC_FILE = os.path.join("profiles", "gemv_gate_up_hbm_traffic.json")
 COPY_BYTES = 256 << 20         # calibration copy for the HBM byte counters
 GEMV_SOURCES = ["gemv_kernel.hpp", "gemv.hip", "common.hpp"]
+# The gate_up GEMV launch: gemv_kernel<rows, mode, columns, loads per lane, norm, threads>.
+GATE_UP_KERNEL = "gemv_kernel<1,0,64,8,false,512>"
 
 
 def gemv_source_hash():
@@ -203,7 +205,8 @@ def bench_wide(w4, torch, synth, timer, iters):
     packed, ws = w4.pack_weights(torch.from_numpy(qw).to(dev), torch.from_numpy(sw).to(dev))
     reps, r = replicas(w4, torch, {"w": (packed, ws)}, algorithmic_bytes(1, k, n))
     reps = reps["w"]
-    for m in synth.WORKLOADS["wide"]["M"]:
+    # the workload's batch sizes plus 2 and 3 rows, around the GEMV/GEMM crossover
+    for m in sorted(set(synth.WORKLOADS["wide"]["M"]) | {2, 3}):
         x = torch.from_numpy(synth.workload_inputs("wide", m)["wide"][0]).to(dev)
         out = torch.empty((m, n), dtype=torch.float32, device=dev)
         row = {}
@@ -213,7 +216,7 @@ def bench_wide(w4, torch, synth, timer, iters):
             us = 1000.0 * back_to_back(torch, timer, lambda i: w4.linear(x, *reps[i % r], path=path, out=out), iters)
             b = algorithmic_bytes(m, k, n)
             row[name] = {"us": round(us, 2), "GB_s": round(b / us / 1e3, 1)}
-        row["auto"] = "gemv" if m <= w4.gemv_max_m() else "gemm"
+        row["auto"] = "gemv" if w4.auto_path(m, k, n) == w4.PATH_GEMV else "gemm"
         res[f"M={m}"] = row
     return {"K": k, "N": n, "replicas": r, "results": res}
 
@@ -379,7 +382,7 @@ def summarize_traffic(fetch_csv, write_csv):
     w_factor = write["copy"] / expect_kib
     gemv_bytes = (fetch["gemv"] / f_factor + write["gemv"] / w_factor) * 1024
     out = {
-        "kernel": "gemv_kernel<1,0,32,8> (decode gate_up 2048x16384, M=1, cold weights)",
+        "kernel": GATE_UP_KERNEL + " (decode gate_up 2048x16384, M=1, cold weights)",
         "fetch_kib_per_launch": fetch["gemv"], "write_kib_per_launch": write["gemv"],
         "copy_fetch_kib": fetch["copy"], "copy_write_kib": write["copy"], "copy_bytes": COPY_BYTES,
         "fetch_scale": round(f_factor, 4), "write_scale": round(w_factor, 4),
@@ -472,7 +475,7 @@ def main():
                                "down 8192x2048; weights cold (rotation over replicas)",
                    "M": 1, "hidden": 2048, "replicas": dec["replicas"],
                    "rotation_bytes": dec["rotation_bytes"], "frac_hbm_peak": round(value / HBM_PEAK_GBS, 4)},
-        "roofline": {"bound": "hbm", "kernel": "gemv_kernel<1,0,32,8> (gate_up 2048x16384, M=1)",
+        "roofline": {"bound": "hbm", "kernel": GATE_UP_KERNEL + " (gate_up 2048x16384, M=1)",
                      "achieved": gu["GB_s"], "peak": HBM_PEAK_GBS, "unit": "GB/s",
                      "frac": round(gu["GB_s"] / HBM_PEAK_GBS, 4), "traffic": measured_traffic(),
                      "bytes_per_launch": gu["bytes"], "us_per_launch": gu["us"]},

@@ -21,7 +21,7 @@ import torch
 __all__ = [
     "PATH_AUTO", "PATH_GEMV", "PATH_GEMM", "W4A8Error", "library_path", "load_library",
     "declared_functions", "init", "pack_weights", "linear", "linear_argmax",
-    "quantize_act", "block_sums", "gemv_max_m", "Weights", "residual_norm_cast",
+    "quantize_act", "block_sums", "gemv_max_m", "auto_path", "Weights", "residual_norm_cast",
     "decoder_layer_workspace", "decoder_layer",
 ]
 
@@ -75,6 +75,7 @@ def load_library() -> ctypes.CDLL:
         "w4a8_quantize_act": ([p, i64, i64, p, p, p], i32),
         "w4a8_block_sums": ([p, p, i64, i64, i64, p, i32, p], i32),
         "w4a8_gemv_max_m": ([], i32),
+        "w4a8_auto_path": ([i64, i64, i64], i32),
         "w4a8_residual_norm_cast": ([p, p, i64, ctypes.c_float, ctypes.c_float, i64, i64, p, p], i32),
         "w4a8_decoder_layer_workspace": ([i64, i64, ctypes.POINTER(_CWeights), ctypes.POINTER(_CWeights),
                                           ctypes.POINTER(ctypes.c_size_t)], i32),
@@ -251,6 +252,11 @@ def block_sums(x: torch.Tensor, packed: torch.Tensor, path: int = PATH_AUTO) -> 
 
 def gemv_max_m() -> int:
     return int(load_library().w4a8_gemv_max_m())
+
+
+def auto_path(m: int, k: int, n: int) -> int:
+    """PATH_GEMV or PATH_GEMM: the kernel PATH_AUTO runs for an m x k by k x n linear."""
+    return int(load_library().w4a8_auto_path(m, k, n))
 
 
 class Weights:

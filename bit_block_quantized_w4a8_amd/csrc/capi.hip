@@ -26,6 +26,7 @@ bool g_any_ready = false;
 std::mutex g_mutex;
 
 int g_gemv_max_m = -1;
+bool g_gemv_max_m_forced = false;
 
 int current_state(DeviceState** out) {
   if (!g_any_ready) {
@@ -126,11 +127,28 @@ int gemv_max_m() {
     int v = 4;
     if (const char* e = std::getenv("W4A8_GEMV_MAX_M")) {
       const int u = std::atoi(e);
-      if (u >= 0 && u <= 64) v = u;
+      if (u >= 0 && u <= 64) {
+        v = u;
+        g_gemv_max_m_forced = true;
+      }
     }
     g_gemv_max_m = v;
   }
   return g_gemv_max_m;
+}
+
+// Stage of W4A8_PATH_AUTO.  The GEMV's time grows with M (every workgroup
+// quantises all M rows of x it reads and forms M dot products per weight
+// load) while the GEMM's barely moves at small M, so the crossover falls with
+// the size of the weight matrix: measured on MI355X with cold weights, the GEMV
+// is faster through M = 4 for 2048 x 2560, 2048 x 16384 and 8192 x 2048, but
+// only through M = 2 for 4096 x 14336 (2^25.8 values).  W4A8_GEMV_MAX_M in the
+// environment replaces the rule by a plain M threshold.
+int auto_path(int64_t M, int64_t K, int64_t N) {
+  const int lim = gemv_max_m();
+  if (g_gemv_max_m_forced) return M <= lim ? W4A8_PATH_GEMV : W4A8_PATH_GEMM;
+  const bool big = K * N > (int64_t{1} << 25);
+  return M <= (big ? (lim < 2 ? lim : 2) : lim) ? W4A8_PATH_GEMV : W4A8_PATH_GEMM;
 }
 
 }  // namespace w4a8
@@ -192,7 +210,7 @@ int w4a8_linear_path(const uint16_t* x, const uint8_t* packed_w, const uint16_t*
   DeviceState* st = nullptr;
   rc = current_state(&st);
   if (rc != W4A8_OK) return rc;
-  if (path == W4A8_PATH_AUTO) path = M <= gemv_max_m() ? W4A8_PATH_GEMV : W4A8_PATH_GEMM;
+  if (path == W4A8_PATH_AUTO) path = auto_path(M, K, N);
   if (path == W4A8_PATH_GEMV) {
     GemvArgs a{x, packed_w, w_scales, static_cast<int>(M), static_cast<int>(K), static_cast<int>(N),
                out, nullptr, nullptr, nullptr};
@@ -248,7 +266,7 @@ int w4a8_block_sums(const uint16_t* x, const uint8_t* packed_w, int64_t M, int64
   DeviceState* st = nullptr;
   rc = current_state(&st);
   if (rc != W4A8_OK) return rc;
-  if (path == W4A8_PATH_AUTO) path = M <= gemv_max_m() ? W4A8_PATH_GEMV : W4A8_PATH_GEMM;
+  if (path == W4A8_PATH_AUTO) path = auto_path(M, K, N);
   if (path == W4A8_PATH_GEMV) {
     GemvArgs a{x, packed_w, nullptr, static_cast<int>(M), static_cast<int>(K), static_cast<int>(N),
                nullptr, sums, nullptr, nullptr};
@@ -399,6 +417,8 @@ int w4a8_norm_linear_argmax(const float* x, float eps, const uint8_t* packed_w, 
 }
 
 int w4a8_gemv_max_m(void) { return gemv_max_m(); }
+
+int w4a8_auto_path(int64_t M, int64_t K, int64_t N) { return auto_path(M, K, N); }
 
 const char* w4a8_last_error(void) { return g_error; }
 

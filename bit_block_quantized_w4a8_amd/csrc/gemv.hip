@@ -7,7 +7,7 @@ namespace gemv_detail {
 W4A8_GEMV_INSTANTIATE(kGemvOut, 1, false)
 
 #define W4A8_GEMV_EXTERN(MODE, MR, NORM)                                                                  \
-  extern template int launch_rows_mr<MODE, MR, NORM>(const GemvArgs&, int, Scratch*, unsigned long long*, \
+  extern template int launch_rows_mr<MODE, MR, NORM>(const GemvArgs&, Scratch*, unsigned long long*, \
                                                      hipStream_t);
 W4A8_GEMV_EXTERN(kGemvOut, 2, false)
 W4A8_GEMV_EXTERN(kGemvOut, 4, false)
@@ -38,15 +38,14 @@ GemvArgs row_slice(const GemvArgs& a, int r0, int rows) {
 
 template <int MODE>
 int launch_rows(const GemvArgs& a, int r0, int rows, Scratch* sc, hipStream_t stream) {
-  const int cols = pick_columns(a.N);
   const GemvArgs s = row_slice(a, r0, rows);
   unsigned long long* slots = sc->slots + (MODE == kGemvArgmax ? r0 * kArgmaxSpread : 0);
-  if (rows == 1) return launch_rows_mr<MODE, 1, false>(s, cols, sc, slots, stream);
+  if (rows == 1) return launch_rows_mr<MODE, 1, false>(s, sc, slots, stream);
   if constexpr (MODE == kGemvOut) {
-    if (rows == 2) return launch_rows_mr<MODE, 2, false>(s, cols, sc, slots, stream);
-    if (rows <= 4) return launch_rows_mr<MODE, 4, false>(s, cols, sc, slots, stream);
+    if (rows == 2) return launch_rows_mr<MODE, 2, false>(s, sc, slots, stream);
+    if (rows <= 4) return launch_rows_mr<MODE, 4, false>(s, sc, slots, stream);
   }
-  return launch_rows_mr<MODE, 8, false>(s, cols, sc, slots, stream);
+  return launch_rows_mr<MODE, 8, false>(s, sc, slots, stream);
 }
 
 }  // namespace gemv_detail
@@ -87,11 +86,7 @@ bool gemv_fused_supported(int mode, bool norm, int K, int N) {
   if (mode < kGemvCast && !(mode == kGemvArgmax && norm)) return false;
   if (!norm) return true;
   // The normalising prologue needs every block of the row in one chunk.
-  // (The fused modes other than the residual epilogue always run 256 threads.)
-  const int cols = gemv_detail::pick_columns(N);
-  const int loads = gemv_detail::pick_loads(K / kBlock, cols, gemv_detail::kThreads);
-  int r = loads <= 2 ? 2 : loads <= 4 ? 4 : cols == 8 ? 8 : loads <= 8 ? 8 : 16;
-  return (gemv_detail::kThreads / cols) * r >= K / kBlock;
+  return gemv_detail::chunk_blocks(gemv_detail::pick_plan(K, N, true)) >= K / kBlock;
 }
 
 int launch_gemv(const GemvArgs& a, int mode, hipStream_t stream) {
@@ -102,12 +97,11 @@ int launch_gemv(const GemvArgs& a, int mode, hipStream_t stream) {
     // Fused decoder-layer kernels: one token row.
     if (a.M != 1 || !gemv_fused_supported(mode, a.xf != nullptr, a.K, a.N))
       return hip_fail(hipErrorInvalidValue, "gemv: fused launch outside its shapes");
-    const int cols = gemv_detail::pick_columns(a.N);
     using gemv_detail::launch_rows_mr;
-    if (mode == kGemvCast) return launch_rows_mr<kGemvCast, 1, true>(a, cols, sc, sc->slots, stream);
-    if (mode == kGemvResid) return launch_rows_mr<kGemvResid, 1, false>(a, cols, sc, sc->slots, stream);
-    if (mode == kGemvGated) return launch_rows_mr<kGemvGated, 1, true>(a, cols, sc, sc->slots, stream);
-    rc = launch_rows_mr<kGemvArgmax, 1, true>(a, cols, sc, sc->slots, stream);
+    if (mode == kGemvCast) return launch_rows_mr<kGemvCast, 1, true>(a, sc, sc->slots, stream);
+    if (mode == kGemvResid) return launch_rows_mr<kGemvResid, 1, false>(a, sc, sc->slots, stream);
+    if (mode == kGemvGated) return launch_rows_mr<kGemvGated, 1, true>(a, sc, sc->slots, stream);
+    rc = launch_rows_mr<kGemvArgmax, 1, true>(a, sc, sc->slots, stream);
     if (rc != W4A8_OK) return rc;
     return launch_argmax_finalize(sc, 1, a.argmax, stream);
   }

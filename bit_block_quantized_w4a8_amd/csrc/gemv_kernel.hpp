@@ -9,14 +9,14 @@
 // quantises the activations it needs into LDS, then streams its weights.
 //
 // Work split: a workgroup owns C output columns (C = 8 .. 64) over all of K,
-// so no result crosses workgroups.  Its T lanes (256, or 512 for long K and
-// 8-column tiles) form C columns x S = T / C block slots; one load instruction of a wave reads 64 / C blocks
+// so no result crosses workgroups.  Its T lanes (256, or 512 for some one-row
+// shapes) form C columns x S = T / C block slots; one load instruction of a wave reads 64 / C blocks
 // of C columns, i.e. runs of 16*C contiguous bytes of the K-block-major
 // weights.  K is walked in chunks: the weight loads of a chunk are issued
 // first, the chunk's activations are quantised into LDS while they are in
 // flight, and then every lane forms its blocks' int8 dot products.  Slots are
-// reduced with cross-lane shuffles and waves through LDS, in a fixed order,
-// so results are identical from run to run.
+// summed within 16-lane rows by DPP moves and across rows and waves through
+// LDS, in a fixed order, so results are identical from run to run.
 //
 // Decoder-layer fusion (the pages fold residual and element-wise work into
 // neighbouring operators: sciencestack summary of the ML Drift paper,
@@ -35,7 +35,7 @@ namespace w4a8 {
 namespace gemv_detail {
 
 constexpr int kThreads = 256;      // default workgroup size
-constexpr int kWideThreads = 512;  // long-K, narrow tiles (see launch_rows_c)
+constexpr int kWideThreads = 512;  // some one-row shapes (see pick_plan)
 constexpr int kRowsMax = 8;        // token rows per launch
 constexpr int kMaxLoadsPerLane = 16;
 constexpr int kMaxChunkBlocks = 256;
@@ -51,6 +51,24 @@ __device__ __forceinline__ uint4 load_x16(const uint16_t* __restrict__ x, int K,
 
 __device__ __forceinline__ uint32_t atomic_add_agent(uint32_t* p, uint32_t v) {
   return __hip_atomic_fetch_add(p, v, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+}
+
+// DPP move within 16-lane rows (no LDS traffic); out-of-row sources read 0.
+template <int kCtrl>
+__device__ __forceinline__ float dpp_move(float v) {
+  return __int_as_float(__builtin_amdgcn_mov_dpp(__float_as_int(v), kCtrl, 0xF, 0xF, true));
+}
+
+// Sum over the lanes of each 16-lane row that share lane % P (P = 1, 2, 4, 8 or
+// 16): afterwards every lane holds its row's sum for its residue.  The same
+// additions run in every row, so the lanes a caller reads give fixed results.
+template <int P>
+__device__ __forceinline__ float row_sum(float v) {
+  if constexpr (P < 2) v += dpp_move<0xB1>(v);   // quad_perm [1,0,3,2]: lane ^ 1
+  if constexpr (P < 4) v += dpp_move<0x4E>(v);   // quad_perm [2,3,0,1]: lane ^ 2
+  if constexpr (P < 8) v += dpp_move<0x124>(v);  // row_ror 4
+  if constexpr (P < 16) v += dpp_move<0x128>(v); // row_ror 8
+  return v;
 }
 
 // Output column of lane column c in tile `tile`.
@@ -74,6 +92,8 @@ __global__ __launch_bounds__(T) void gemv_kernel(GemvArgs a, uint32_t* __restric
                                                  unsigned long long* __restrict__ slots, int never_set) {
   constexpr int kWaves = T / 64;
   constexpr int S = T / C;                  // block slots per round
+  // Partial sums per column per wave once each 16-lane row is reduced.
+  constexpr int kParts = C <= 16 ? 4 : 64 / C;
   constexpr int kChunkBlocks = S * R;
   static_assert(kChunkBlocks <= kMaxChunkBlocks && R <= kMaxLoadsPerLane, "chunk too large");
   static_assert(MODE != kGemvGated || C >= 2, "gated tiles pair columns");
@@ -82,7 +102,8 @@ __global__ __launch_bounds__(T) void gemv_kernel(GemvArgs a, uint32_t* __restric
 
   __shared__ uint32_t q_lds[MR][kChunkBlocks][8];  // int8 codes, 8 dwords per block
   __shared__ float s_lds[MR][kChunkBlocks];         // sx / 16 per block
-  __shared__ float red[kWaves][MR][C];
+  __shared__ float red[kWaves][MR][kParts][C];
+  __shared__ float red_ss[NORM ? kWaves : 1][MR][4];
 
   const uint16_t* __restrict__ x = a.x;
   const uint8_t* __restrict__ pw = a.packed_w;
@@ -191,17 +212,18 @@ __global__ __launch_bounds__(T) void gemv_kernel(GemvArgs a, uint32_t* __restric
       }
 #pragma unroll
       for (int m = 0; m < MR; ++m) {
-#pragma unroll
-        for (int off = 32; off >= 1; off >>= 1) ss[m] += __shfl_xor(ss[m], off);
-        if (lane == 0) red[wave][m][0] = ss[m];
+        const float rs = row_sum<1>(ss[m]);
+        if ((lane & 15) == 0) red_ss[wave][m][lane >> 4] = rs;
       }
       __syncthreads();
       float inv[MR];
 #pragma unroll
       for (int m = 0; m < MR; ++m) {
-        float t = red[0][m][0];
+        float t = 0.0f;
 #pragma unroll
-        for (int wv = 1; wv < kWaves; ++wv) t += red[wv][m][0];
+        for (int wv = 0; wv < kWaves; ++wv)
+#pragma unroll
+          for (int r = 0; r < 4; ++r) t += red_ss[wv][m][r];
         inv[m] = 1.0f / sqrtf(t / static_cast<float>(K) + a.eps);
       }
 #pragma unroll
@@ -290,15 +312,15 @@ __global__ __launch_bounds__(T) void gemv_kernel(GemvArgs a, uint32_t* __restric
   if (never_set) tickets[0] = keep;  // `never_set` is 0: the store only keeps `keep` alive
   if (MODE == kGemvSums) return;
 
-  // Slots of one wave: lanes c, c + C, c + 2C, ... hold the same column.
+  // Slots of one wave: lanes c, c + C, c + 2C, ... hold the same column.  They
+  // are summed within each 16-lane row, and the kParts row sums of every wave
+  // through LDS, in a fixed order.
 #pragma unroll
-  for (int m = 0; m < MR; ++m)
+  for (int m = 0; m < MR; ++m) acc[m] = row_sum<C < 16 ? C : 16>(acc[m]);
+  if (C >= 16 || (lane & 15) < C) {
+    const int part = C <= 16 ? lane >> 4 : lane / C;
 #pragma unroll
-    for (int off = C; off < 64; off <<= 1) acc[m] += __shfl_xor(acc[m], off);
-
-  if (lane < C) {
-#pragma unroll
-    for (int m = 0; m < MR; ++m) red[wave][m][lane] = acc[m];
+    for (int m = 0; m < MR; ++m) red[wave][m][part][lane % C] = acc[m];
   }
   __syncthreads();
   if (wave != 0) return;
@@ -306,9 +328,11 @@ __global__ __launch_bounds__(T) void gemv_kernel(GemvArgs a, uint32_t* __restric
   float v[MR];
 #pragma unroll
   for (int m = 0; m < MR; ++m) {
-    float t = red[0][m][lane % C];
+    float t = 0.0f;
 #pragma unroll
-    for (int wv = 1; wv < kWaves; ++wv) t += red[wv][m][lane % C];
+    for (int wv = 0; wv < kWaves; ++wv)
+#pragma unroll
+      for (int p = 0; p < kParts; ++p) t += red[wv][m][p][lane % C];
     v[m] = t;
   }
 
@@ -364,40 +388,56 @@ __global__ __launch_bounds__(T) void gemv_kernel(GemvArgs a, uint32_t* __restric
   }
 }
 
-// Column tile: the widest tile that still gives at least 512 workgroups.
-// Wider tiles repeat the in-kernel quantisation of x in fewer workgroups;
-// 8 columns is the narrowest that keeps every load on whole 128-byte lines.
-inline int pick_columns(int N) {
-  if (N / 64 >= 512) return 64;
-  if (N / 32 >= 512) return 32;
-  if (N / 16 >= 512) return 16;
-  return 8;
-}
-
-// Workgroup size: 512 threads for 8-column tiles over more than 4096 K (every
-// lane then quantises and multiplies half as many blocks), else 256.
-inline int pick_threads(int K, int cols, int rows) { return cols == 8 && K > 4096 && rows == 1 ? kWideThreads : kThreads; }
+// Launch shape: C columns per workgroup, T threads, R weight loads per lane.
+struct Plan {
+  int cols, threads, loads;
+};
 
 // Weight loads per lane: enough for all K blocks in one chunk, capped by
-// registers (16) and LDS (256 blocks of codes per row).
+// registers (16, or 8 in 512-thread workgroups, where 16 ran slower than two
+// chunks) and LDS (256 blocks of codes per row).
 inline int pick_loads(int nb, int cols, int threads) {
   const int slots = threads / cols;
+  const int cap = threads == kWideThreads ? 8 : kMaxLoadsPerLane;
   int r = 2;
-  while (r < kMaxLoadsPerLane && r * slots < nb && 2 * r * slots <= kMaxChunkBlocks) r *= 2;
+  while (r < cap && r * slots < nb && 2 * r * slots <= kMaxChunkBlocks) r *= 2;
   return r;
 }
+
+// Column tile: the widest that still gives at least 512 workgroups.  Wider
+// tiles repeat the in-kernel quantisation of x in fewer workgroups; 8 columns
+// is the narrowest that keeps every load on whole 128-byte lines.  One-row
+// kernels (`wide`) also take 512-thread workgroups: of 64 columns when that
+// gives 256..511 workgroups (half as many quantisations of x as 32-column
+// tiles, the same lanes per column), and of 8 columns over more than 4096 K
+// (every lane then quantises and multiplies half as many blocks).
+inline Plan pick_plan(int K, int N, bool wide) {
+  int cols = 8, threads = kThreads;
+  if (N / 64 >= 512) cols = 64;
+  else if (wide && N / 64 >= 256) cols = 64, threads = kWideThreads;
+  else if (N / 32 >= 512) cols = 32;
+  else if (N / 16 >= 512) cols = 16;
+  else if (wide && K > 4096) threads = kWideThreads;
+  return {cols, threads, pick_loads(K / kBlock, cols, threads)};
+}
+
+// Kernels specialised on K (one chunk when it fits): the decode GEMV of 1, 2
+// and 4 rows and the fused one-row kernels.  The block-sum export, the argmax
+// of fp16 rows and 8-row launches use one load count per tile width (surplus
+// loads are clamped duplicates).
+template <int MODE, int MR, bool NORM>
+constexpr bool kSpecialised = (MODE == kGemvOut && MR <= 4) || NORM || MODE >= kGemvCast;
+// 512-thread workgroups: one-row kernels specialised on K.
+template <int MODE, int MR, bool NORM>
+constexpr bool kWideOk = MR == 1 && kSpecialised<MODE, MR, NORM>;
 
 // `a` already points at the launch's first row.
 template <int MODE, int MR, int C, bool NORM, int T>
 int launch_rows_ct(const GemvArgs& a, int loads, Scratch* sc, unsigned long long* slots, hipStream_t stream) {
   const dim3 grid(a.N / C);
-  // The block-sum export, the argmax and 8-row launches use one load count per
-  // tile width (surplus loads are clamped duplicates); the decode GEMV of 1, 2
-  // and 4 rows and the fused one-row kernels are specialised on K.
-  constexpr bool kSpecialise = (MODE == kGemvOut && MR <= 4) || NORM || MODE >= kGemvCast;
 #define W4A8_GEMV_LAUNCH(R) \
   hipLaunchKernelGGL((gemv_kernel<MR, MODE, C, R, NORM, T>), grid, dim3(T), 0, stream, a, sc->tickets, slots, 0)
-  if constexpr (!kSpecialise) {
+  if constexpr (!kSpecialised<MODE, MR, NORM>) {
     if constexpr (C == 8) W4A8_GEMV_LAUNCH(8);
     else W4A8_GEMV_LAUNCH(16);
   } else if (loads <= 2) {
@@ -409,6 +449,8 @@ int launch_rows_ct(const GemvArgs& a, int loads, Scratch* sc, unsigned long long
   } else if constexpr (T == kThreads) {
     if (loads <= 8) W4A8_GEMV_LAUNCH(8);
     else W4A8_GEMV_LAUNCH(16);
+  } else if constexpr (C > 8) {
+    W4A8_GEMV_LAUNCH(8);  // pick_loads caps 512-thread workgroups at 8
   } else {
     return hip_fail(hipErrorInvalidValue, "gemv: no wide-workgroup kernel for this K");
   }
@@ -417,23 +459,27 @@ int launch_rows_ct(const GemvArgs& a, int loads, Scratch* sc, unsigned long long
   return W4A8_OK;
 }
 
+// Blocks one launch of the plan covers per chunk (the R it launches above).
+inline int chunk_blocks(const Plan& p) {
+  const int r = p.loads <= 2 ? 2 : p.loads <= 4 ? 4 : p.cols == 8 || p.threads == kWideThreads ? 8 : p.loads;
+  return p.threads / p.cols * r;
+}
+
 template <int MODE, int MR, int C, bool NORM>
-int launch_rows_c(const GemvArgs& a, Scratch* sc, unsigned long long* slots, hipStream_t stream) {
-  constexpr bool kWideOk = C == 8 && MR == 1 && (MODE == kGemvOut || MODE == kGemvResid) && !NORM;
-  if constexpr (kWideOk) {
-    if (pick_threads(a.K, C, MR) == kWideThreads)
-      return launch_rows_ct<MODE, MR, C, NORM, kWideThreads>(a, pick_loads(a.K / kBlock, C, kWideThreads), sc,
-                                                              slots, stream);
+int launch_rows_c(const GemvArgs& a, const Plan& p, Scratch* sc, unsigned long long* slots, hipStream_t stream) {
+  if constexpr (kWideOk<MODE, MR, NORM> && (C == 8 || C == 64)) {
+    if (p.threads == kWideThreads) return launch_rows_ct<MODE, MR, C, NORM, kWideThreads>(a, p.loads, sc, slots, stream);
   }
-  return launch_rows_ct<MODE, MR, C, NORM, kThreads>(a, pick_loads(a.K / kBlock, C, kThreads), sc, slots, stream);
+  return launch_rows_ct<MODE, MR, C, NORM, kThreads>(a, p.loads, sc, slots, stream);
 }
 
 template <int MODE, int MR, bool NORM>
-int launch_rows_mr(const GemvArgs& a, int cols, Scratch* sc, unsigned long long* slots, hipStream_t stream) {
-  if (cols == 64) return launch_rows_c<MODE, MR, 64, NORM>(a, sc, slots, stream);
-  if (cols == 32) return launch_rows_c<MODE, MR, 32, NORM>(a, sc, slots, stream);
-  if (cols == 16) return launch_rows_c<MODE, MR, 16, NORM>(a, sc, slots, stream);
-  return launch_rows_c<MODE, MR, 8, NORM>(a, sc, slots, stream);
+int launch_rows_mr(const GemvArgs& a, Scratch* sc, unsigned long long* slots, hipStream_t stream) {
+  const Plan p = pick_plan(a.K, a.N, kWideOk<MODE, MR, NORM>);
+  if (p.cols == 64) return launch_rows_c<MODE, MR, 64, NORM>(a, p, sc, slots, stream);
+  if (p.cols == 32) return launch_rows_c<MODE, MR, 32, NORM>(a, p, sc, slots, stream);
+  if (p.cols == 16) return launch_rows_c<MODE, MR, 16, NORM>(a, p, sc, slots, stream);
+  return launch_rows_c<MODE, MR, 8, NORM>(a, p, sc, slots, stream);
 }
 
 // launch_rows_mr is instantiated in gemv.hip (decode GEMV, 1 row), gemv_rows.hip
@@ -441,7 +487,7 @@ int launch_rows_mr(const GemvArgs& a, int cols, Scratch* sc, unsigned long long*
 // gemv_fused.hip (the one-row decoder-layer kernels).
 
 #define W4A8_GEMV_INSTANTIATE(MODE, MR, NORM)                                                      \
-  template int launch_rows_mr<MODE, MR, NORM>(const GemvArgs&, int, Scratch*, unsigned long long*, \
+  template int launch_rows_mr<MODE, MR, NORM>(const GemvArgs&, Scratch*, unsigned long long*, \
                                               hipStream_t);
 
 }  // namespace gemv_detail

@@ -61,6 +61,8 @@ int launch_gemm(const GemmArgs& a, int mode, hipStream_t stream);
 size_t gemm_scratch_bytes(int M, int K, int N);
 
 int gemv_max_m();
+// Kernel W4A8_PATH_AUTO picks for an M x K by K x N linear.
+int auto_path(int64_t M, int64_t K, int64_t N);
 
 // Glue of the synthetic decoder layer (layer.hip).
 int launch_residual_norm_cast(float* x, const float* d, int64_t ld_d, float alpha, float eps, int M, int H,

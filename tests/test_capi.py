@@ -14,13 +14,22 @@ def lib():
 
 def test_exports_every_declared_symbol(lib):
     names = w4.declared_functions()
-    assert len(names) == 13, names
+    assert len(names) == 14, names
     for name in names:
         assert hasattr(lib, name), name
 
 
 def test_gemv_threshold(lib):
     assert 1 <= lib.w4a8_gemv_max_m() <= 64
+
+
+def test_auto_path_rule():
+    """Host-side stage rule: GEMV through M = 2 always, through M = 4 for weight matrices of at
+    most 2^25 values, the GEMM above (the environment override is not set under pytest)."""
+    gemv, gemm = w4.PATH_GEMV, w4.PATH_GEMM
+    for k, n in [(2048, 2560), (2048, 16384), (8192, 2048)]:
+        assert [w4.auto_path(m, k, n) for m in (1, 2, 3, 4, 5, 512)] == [gemv] * 4 + [gemm] * 2
+    assert [w4.auto_path(m, 4096, 14336) for m in (1, 2, 3, 4)] == [gemv, gemv, gemm, gemm]
 
 
 ALIGNED = 1 << 20       # fake, suitably aligned device addresses: never dereferenced

@@ -95,6 +95,34 @@ def test_decoder_layer_full_decode_shape():
     assert err.max() <= 0, f"max excess {err.max():.3g}"
 
 
+def test_decoder_layer_one_token_unfused_shape():
+    """One token at a width whose gate/up tile cannot hold K = H in one GEMV chunk (64-column
+    tiles cover 2048 of K): the layer falls back to the nine-launch chain."""
+    h = 4096
+    host_w, dev_w = _weights(8, h, h + 512, 16384)
+    x = synth.activations(synth.rng(8, 999), 1, h).astype(np.float32)
+    got = _run_layer(x, dev_w)
+    ref = oracle.decoder_layer(x, host_w, SCALE, EPS)
+    # With 16384-wide intermediates a one-ulp fp16 difference in the normalised input can move an
+    # int8 code by one, so this shape is held to the output tolerance itself (1e-3 abs + 1e-3 rel).
+    err = np.abs(got.astype(np.float64) - ref) - (1e-3 + 1e-3 * np.abs(ref))
+    assert err.max() <= 0, f"max excess {err.max():.3g}"
+    assert np.median(np.abs(got - ref)) < 1e-4
+
+
+def test_decoder_layer_one_token_wide_workgroups():
+    """One token at hidden 6144: the fused normalising kernels of the QKV and gate/up
+    projections and the residual O projection run 8-column tiles in 512-thread workgroups."""
+    h = 6144
+    host_w, dev_w = _weights(9, h, h + 512, 2048)
+    x = synth.activations(synth.rng(9, 999), 1, h).astype(np.float32)
+    got = _run_layer(x, dev_w)
+    ref = oracle.decoder_layer(x, host_w, SCALE, EPS)
+    err = np.abs(got.astype(np.float64) - ref) - (1e-3 + 1e-3 * np.abs(ref))
+    assert err.max() <= 0, f"max excess {err.max():.3g}"
+    assert np.median(np.abs(got - ref)) < 1e-4
+
+
 def test_chain_of_layers_and_lm_head_argmax():
     """Four layers and an LM head, GPU against oracle, no teacher forcing."""
     h, n_qkv, f, vocab = 256, 320, 512, 4096
@@ -125,7 +153,8 @@ def test_chain_of_layers_and_lm_head_argmax():
     assert np.array_equal(am, tf)
 
 
-@pytest.mark.parametrize("m,h,vocab", [(1, 256, 4096), (1, 2048, 262144), (2, 256, 4096), (1, 8192, 4096)])
+@pytest.mark.parametrize("m,h,vocab", [(1, 256, 4096), (1, 2048, 262144), (2, 256, 4096), (1, 8192, 4096),
+                                        (1, 4096, 32768)])
 def test_norm_linear_argmax(m, h, vocab):
     """LM-head argmax on the fp32 residual stream (one fused launch for one row; rows normalised
     first otherwise), against the oracle and against the two-step GPU path."""

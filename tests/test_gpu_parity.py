@@ -247,6 +247,21 @@ def test_gemm_every_tile_plan(m, k, n):
     assert np.array_equal(got.astype(np.int64), oracle.block_sums(qx, qw))
 
 
+# One shape per GEMV launch plan: 64 columns in 512-thread workgroups (one chunk of K, and
+# four), 64 columns in 256-thread workgroups, 8 columns in 512-thread workgroups (one chunk,
+# two), 16 and 8 columns in 256-thread workgroups, and 32-column tiles of 4 and 8 rows.
+GEMV_PLANS = [(1, 2048, 16384), (1, 8192, 16384), (1, 2048, 32768), (1, 8192, 2048), (1, 16384, 2048),
+              (1, 2048, 8192), (1, 2048, 2560), (3, 4096, 16384), (8, 2048, 16384)]
+
+
+@pytest.mark.parametrize("m,k,n", GEMV_PLANS)
+def test_gemv_every_launch_plan(m, k, n):
+    x, qw, sw = inputs(m * 13 + k + n, m, k, n, outliers=True)
+    packed, ws = packed_on_gpu(qw, sw)
+    assert_close(host(w4.linear(dev(x), packed, ws, path=w4.PATH_GEMV)), oracle.linear(x, qw, sw),
+                 f"GEMV M={m} K={k} N={n}")
+
+
 @pytest.mark.parametrize("m", synth.WORKLOADS["wide"]["M"])
 def test_wide_linear_full(m):
     x, qw, sw = synth.workload_inputs("wide", m)["wide"]
