@@ -373,6 +373,31 @@ int w4a8_decoder_layer(float* x, int64_t M, int64_t H, const w4a8_weights* qkv, 
     W4A8_STEP(launch_gemv(da, kGemvResid, stream));
     return W4A8_OK;
   }
+  const int Nq = static_cast<int>(qkv->N);
+  if (auto_path(M, H, qkv->N) == W4A8_PATH_GEMM && auto_path(M, H, H) == W4A8_PATH_GEMM &&
+      auto_path(M, H, gate_up->N) == W4A8_PATH_GEMM && auto_path(M, F, H) == W4A8_PATH_GEMM) {
+    // Many rows: every projection is a prefill GEMM, and the glue kernels
+    // write their fp16 results straight into the next GEMM's quantised
+    // staging, so no separate quantise pre-pass runs (four launches fewer).
+    GemmStaging sg{};
+    W4A8_STEP(gemm_staging(Mi, Hi, Nq, &sg));
+    W4A8_STEP(launch_residual_norm_quant(x, nullptr, 0, 0.0f, eps, Mi, Hi, sg, stream));
+    W4A8_STEP(launch_gemm_staged(GemmArgs{nullptr, qkv->packed_w, qkv->w_scales, Mi, Hi, Nq, q, nullptr}, sg,
+                                 stream));
+    W4A8_STEP(gemm_staging(Mi, Hi, Hi, &sg));
+    W4A8_STEP(launch_cast_quant(q, qkv->N, Mi, Hi, sg, stream));
+    W4A8_STEP(launch_gemm_staged(GemmArgs{nullptr, o->packed_w, o->w_scales, Mi, Hi, Hi, ob, nullptr}, sg, stream));
+    W4A8_STEP(gemm_staging(Mi, Hi, 2 * F, &sg));
+    W4A8_STEP(launch_residual_norm_quant(x, ob, H, residual_scale, eps, Mi, Hi, sg, stream));
+    W4A8_STEP(launch_gemm_staged(GemmArgs{nullptr, gate_up->packed_w, gate_up->w_scales, Mi, Hi, 2 * F, g, nullptr},
+                                 sg, stream));
+    W4A8_STEP(gemm_staging(Mi, F, Hi, &sg));
+    W4A8_STEP(launch_gated_quant(g, Mi, F, sg, stream));
+    W4A8_STEP(launch_gemm_staged(GemmArgs{nullptr, down->packed_w, down->w_scales, Mi, F, Hi, d, nullptr}, sg,
+                                 stream));
+    W4A8_STEP(launch_residual_norm_cast(x, d, H, residual_scale, eps, Mi, Hi, nullptr, stream));
+    return W4A8_OK;
+  }
   W4A8_STEP(launch_residual_norm_cast(x, nullptr, 0, 0.0f, eps, Mi, Hi, n, stream));
   W4A8_STEP(w4a8_linear(n, qkv->packed_w, qkv->w_scales, M, H, qkv->N, q, stream));
   W4A8_STEP(launch_cast_rows(q, qkv->N, Mi, Hi, a, stream));

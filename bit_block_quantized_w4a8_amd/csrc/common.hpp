@@ -110,6 +110,23 @@ __device__ __forceinline__ uint2 quantize8_group4(const float* x, float* sx_out)
   return make_uint2(packed[0], packed[1]);
 }
 
+// Quantises group e (elements 8e .. 8e+7, held in v) of row m into the GEMM
+// staging layout (gemm.hip): codes at qxs + b * m_pad * 32, 16-byte slot
+// ((m / 32) * 2 + h) * 32 + m % 32 with h = g % 2, byte offset 8 * (g / 2), for
+// block b = e / 4 and group g = e % 4 (elements 8g .. 8g+7 of the block belong
+// at byte 8 * (0, 2, 1, 3)[g] of the row's 32 codes); the block scale goes to
+// sxs[b * m_pad + m].  Called by an aligned quad of lanes per block.
+__device__ __forceinline__ void quantize_to_staging(const float* v, int64_t m, int64_t e, int64_t m_pad,
+                                                    uint8_t* __restrict__ qxs, float* __restrict__ sxs) {
+  float scale;
+  const uint2 codes = quantize8_group4(v, &scale);
+  const int g = static_cast<int>(e & 3);
+  const int64_t b = e >> 2;
+  const int64_t row_slot = ((m >> 5) * 2 + (g & 1)) * 32 + (m & 31);
+  *reinterpret_cast<uint2*>(qxs + b * m_pad * kBlock + row_slot * 16 + 8 * (g >> 1)) = codes;
+  if (g == 0) sxs[b * m_pad + m] = scale;
+}
+
 // The eight fp16 values of a 16-byte load, widened to fp32 (exact).
 __device__ __forceinline__ void unpack_half8(uint4 v, float* x) {
   const uint32_t w[4] = {v.x, v.y, v.z, v.w};

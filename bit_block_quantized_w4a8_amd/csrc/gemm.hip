@@ -542,20 +542,26 @@ size_t gemm_scratch_bytes(int M, int K, int N) {
   return bytes;
 }
 
-int launch_gemm(const GemmArgs& a, int mode, hipStream_t stream) {
+namespace {
+
+// Partial tiles of a split-K launch follow the staging in library scratch.
+float* gemm_partials(const GemmStaging& s, int K) {
+  const size_t nb = K / kBlock;
+  return reinterpret_cast<float*>(reinterpret_cast<uint8_t*>(s.qxs) + align256(nb * s.m_pad * kBlock) +
+                                  align256(nb * s.m_pad * sizeof(float)));
+}
+
+int launch_gemm_kernel(const GemmArgs& a, int mode, const GemmStaging& s, hipStream_t stream) {
   const Plan p = plan_gemm(a.M, a.K, a.N);
   if (p.tiles_n * p.tiles_m >= kMaxTickets - 1) return hip_fail(hipErrorInvalidValue, "gemm: too many tiles");
+  if (s.m_pad != p.m_pad) return hip_fail(hipErrorInvalidValue, "gemm: staging of another shape");
   Scratch* sc = nullptr;
   int rc = scratch_for(gemm_scratch_bytes(a.M, a.K, a.N), &sc);
   if (rc != W4A8_OK) return rc;
-  const size_t nb = a.K / kBlock;
-  uint8_t* base = static_cast<uint8_t*>(sc->work);
-  uint8_t* qxs = base;
-  float* sxs = reinterpret_cast<float*>(base + align256(nb * p.m_pad * kBlock));
-  float* partials = reinterpret_cast<float*>(base + align256(nb * p.m_pad * kBlock) +
-                                             align256(nb * p.m_pad * sizeof(float)));
-  rc = launch_quantize_stage(a.x, a.M, p.m_pad, a.K, qxs, sxs, stream);
-  if (rc != W4A8_OK) return rc;
+  if (s.qxs != sc->work) return hip_fail(hipErrorInvalidValue, "gemm: staging outside library scratch");
+  const uint8_t* qxs = s.qxs;
+  const float* sxs = s.sxs;
+  float* partials = gemm_partials(s, a.K);
   const dim3 grid(p.tiles_n * p.tiles_m, p.ksplit);
   // Every thread stages scale chunks unconditionally; the block-sum export has
   // no scales (w_scales may be null), so it stages bytes of the packed weights
@@ -584,6 +590,34 @@ int launch_gemm(const GemmArgs& a, int mode, hipStream_t stream) {
 #undef W4A8_GEMM_LAUNCH
   W4A8_HIP(hipGetLastError());
   return W4A8_OK;
+}
+
+}  // namespace
+
+int gemm_staging(int M, int K, int N, GemmStaging* s) {
+  const Plan p = plan_gemm(M, K, N);
+  Scratch* sc = nullptr;
+  const int rc = scratch_for(gemm_scratch_bytes(M, K, N), &sc);
+  if (rc != W4A8_OK) return rc;
+  const size_t nb = K / kBlock;
+  uint8_t* base = static_cast<uint8_t*>(sc->work);
+  s->qxs = base;
+  s->sxs = reinterpret_cast<float*>(base + align256(nb * p.m_pad * kBlock));
+  s->m_pad = p.m_pad;
+  return W4A8_OK;
+}
+
+int launch_gemm(const GemmArgs& a, int mode, hipStream_t stream) {
+  GemmStaging s{};
+  int rc = gemm_staging(a.M, a.K, a.N, &s);
+  if (rc != W4A8_OK) return rc;
+  rc = launch_quantize_stage(a.x, a.M, s.m_pad, a.K, s.qxs, s.sxs, stream);
+  if (rc != W4A8_OK) return rc;
+  return launch_gemm_kernel(a, mode, s, stream);
+}
+
+int launch_gemm_staged(const GemmArgs& a, const GemmStaging& s, hipStream_t stream) {
+  return launch_gemm_kernel(a, 0, s, stream);
 }
 
 }  // namespace w4a8

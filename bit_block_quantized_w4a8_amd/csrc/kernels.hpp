@@ -59,6 +59,18 @@ struct GemmArgs {
 };
 int launch_gemm(const GemmArgs& a, int mode, hipStream_t stream);
 size_t gemm_scratch_bytes(int M, int K, int N);
+// Staging of one GEMM launch in library scratch (the pre-pass's output):
+// codes and scales of M_pad rows (rows M .. M_pad-1 zero) for an M x K by K x N
+// product.  gemm_staging grows the scratch if needed, so it is called before
+// anything is written into the staging.
+struct GemmStaging {
+  uint8_t* qxs;
+  float* sxs;
+  int m_pad;
+};
+int gemm_staging(int M, int K, int N, GemmStaging* s);
+// The GEMM (scaled output) on activations already quantised into `s`.
+int launch_gemm_staged(const GemmArgs& a, const GemmStaging& s, hipStream_t stream);
 
 int gemv_max_m();
 // Kernel W4A8_PATH_AUTO picks for an M x K by K x N linear.
@@ -68,6 +80,11 @@ int auto_path(int64_t M, int64_t K, int64_t N);
 int launch_residual_norm_cast(float* x, const float* d, int64_t ld_d, float alpha, float eps, int M, int H,
                               uint16_t* y, hipStream_t stream);
 int launch_cast_rows(const float* src, int64_t ld, int M, int H, uint16_t* dst, hipStream_t stream);
+// The same glue with the fp16 result quantised straight into GEMM staging.
+int launch_residual_norm_quant(float* x, const float* d, int64_t ld_d, float alpha, float eps, int M, int H,
+                               const GemmStaging& s, hipStream_t stream);
+int launch_cast_quant(const float* src, int64_t ld, int M, int H, const GemmStaging& s, hipStream_t stream);
+int launch_gated_quant(const float* g, int M, int F, const GemmStaging& s, hipStream_t stream);
 int launch_gated_cast(const float* g, int M, int F, uint16_t* u, hipStream_t stream);
 
 // Byte offsets of a decoder layer's temporaries inside the caller's workspace.

@@ -76,6 +76,97 @@ __global__ __launch_bounds__(kGlueThreads) void gated_cast_kernel(const float* _
   }
 }
 
+// The glue kernels below write the next linear's input straight into GEMM
+// staging, the bytes the quantise pre-pass would write from the fp16 result of
+// the kernels above (each fp16 value is formed the same way and quantised by
+// the same device function).  One workgroup per staging row; rows M .. M_pad-1
+// get zero codes and scales.  Thread t owns the 8-element groups
+// e = t, t + 256, ... of its row, so every aligned quad of lanes holds one
+// 32-element block (H is a multiple of 32 and 256 of 4).
+
+// Optionally x += alpha * d, then fp16(x / rms(x)) quantised into staging.
+__global__ __launch_bounds__(kGlueThreads) void residual_norm_quant_kernel(
+    float* __restrict__ x, const float* __restrict__ d, int64_t ld_d, float alpha, float eps, int M, int H,
+    int m_pad, uint8_t* __restrict__ qxs, float* __restrict__ sxs) {
+  __shared__ float red[4];
+  const int64_t m = blockIdx.x;
+  const int groups = H / 8;
+  if (m >= M) {  // padding row (uniform)
+    const float zero[8] = {0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f};
+    for (int e = threadIdx.x; e < groups; e += kGlueThreads) quantize_to_staging(zero, m, e, m_pad, qxs, sxs);
+    return;
+  }
+  float* xr = x + m * H;
+  float ss = 0.0f;
+  for (int e = threadIdx.x; e < groups; e += kGlueThreads) {
+    float4 lo = *reinterpret_cast<const float4*>(xr + 8 * e);
+    float4 hi = *reinterpret_cast<const float4*>(xr + 8 * e + 4);
+    if (d) {
+      const float* dr = d + m * ld_d + 8 * e;
+      lo.x = fmaf(alpha, dr[0], lo.x); lo.y = fmaf(alpha, dr[1], lo.y);
+      lo.z = fmaf(alpha, dr[2], lo.z); lo.w = fmaf(alpha, dr[3], lo.w);
+      hi.x = fmaf(alpha, dr[4], hi.x); hi.y = fmaf(alpha, dr[5], hi.y);
+      hi.z = fmaf(alpha, dr[6], hi.z); hi.w = fmaf(alpha, dr[7], hi.w);
+      *reinterpret_cast<float4*>(xr + 8 * e) = lo;
+      *reinterpret_cast<float4*>(xr + 8 * e + 4) = hi;
+    }
+    ss = fmaf(lo.x, lo.x, ss); ss = fmaf(lo.y, lo.y, ss); ss = fmaf(lo.z, lo.z, ss); ss = fmaf(lo.w, lo.w, ss);
+    ss = fmaf(hi.x, hi.x, ss); ss = fmaf(hi.y, hi.y, ss); ss = fmaf(hi.z, hi.z, ss); ss = fmaf(hi.w, hi.w, ss);
+  }
+  const float inv = 1.0f / sqrtf(block_sum(ss, red) / static_cast<float>(H) + eps);
+  // Each thread re-reads only the elements it wrote above.
+  for (int e = threadIdx.x; e < groups; e += kGlueThreads) {
+    const float4 lo = *reinterpret_cast<const float4*>(xr + 8 * e);
+    const float4 hi = *reinterpret_cast<const float4*>(xr + 8 * e + 4);
+    const float raw[8] = {lo.x, lo.y, lo.z, lo.w, hi.x, hi.y, hi.z, hi.w};
+    float v[8];
+#pragma unroll
+    for (int k = 0; k < 8; ++k) v[k] = half_bits_to_float(float_to_half_bits(raw[k] * inv));
+    quantize_to_staging(v, m, e, m_pad, qxs, sxs);
+  }
+}
+
+// fp16(src[m * ld + h]) for h < H, quantised into staging.
+__global__ __launch_bounds__(kGlueThreads) void cast_quant_kernel(const float* __restrict__ src, int64_t ld,
+                                                                  int M, int H, int m_pad,
+                                                                  uint8_t* __restrict__ qxs,
+                                                                  float* __restrict__ sxs) {
+  const int64_t m = blockIdx.x;
+  for (int e = threadIdx.x; e < H / 8; e += kGlueThreads) {
+    float v[8] = {0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f};
+    if (m < M) {  // uniform
+      const float4 lo = *reinterpret_cast<const float4*>(src + m * ld + 8 * e);
+      const float4 hi = *reinterpret_cast<const float4*>(src + m * ld + 8 * e + 4);
+      const float raw[8] = {lo.x, lo.y, lo.z, lo.w, hi.x, hi.y, hi.z, hi.w};
+#pragma unroll
+      for (int k = 0; k < 8; ++k) v[k] = half_bits_to_float(float_to_half_bits(raw[k]));
+    }
+    quantize_to_staging(v, m, e, m_pad, qxs, sxs);
+  }
+}
+
+// fp16(g[m][f] * g[m][F + f]) for f < F, quantised into staging.
+__global__ __launch_bounds__(kGlueThreads) void gated_quant_kernel(const float* __restrict__ g, int M, int F,
+                                                                   int m_pad, uint8_t* __restrict__ qxs,
+                                                                   float* __restrict__ sxs) {
+  const int64_t m = blockIdx.x;
+  for (int e = threadIdx.x; e < F / 8; e += kGlueThreads) {
+    float v[8] = {0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f};
+    if (m < M) {  // uniform
+      const float* row = g + m * 2 * static_cast<int64_t>(F) + 8 * e;
+      const float4 g0 = *reinterpret_cast<const float4*>(row);
+      const float4 g1 = *reinterpret_cast<const float4*>(row + 4);
+      const float4 u0 = *reinterpret_cast<const float4*>(row + F);
+      const float4 u1 = *reinterpret_cast<const float4*>(row + F + 4);
+      const float raw[8] = {g0.x * u0.x, g0.y * u0.y, g0.z * u0.z, g0.w * u0.w,
+                            g1.x * u1.x, g1.y * u1.y, g1.z * u1.z, g1.w * u1.w};
+#pragma unroll
+      for (int k = 0; k < 8; ++k) v[k] = half_bits_to_float(float_to_half_bits(raw[k]));
+    }
+    quantize_to_staging(v, m, e, m_pad, qxs, sxs);
+  }
+}
+
 size_t align256(size_t v) { return (v + 255) & ~static_cast<size_t>(255); }
 
 }  // namespace
@@ -98,6 +189,28 @@ int launch_cast_rows(const float* src, int64_t ld, int M, int H, uint16_t* dst, 
 int launch_gated_cast(const float* g, int M, int F, uint16_t* u, hipStream_t stream) {
   hipLaunchKernelGGL(gated_cast_kernel, dim3((F + kGlueThreads - 1) / kGlueThreads, M), dim3(kGlueThreads), 0,
                      stream, g, F, u);
+  W4A8_HIP(hipGetLastError());
+  return W4A8_OK;
+}
+
+int launch_residual_norm_quant(float* x, const float* d, int64_t ld_d, float alpha, float eps, int M, int H,
+                               const GemmStaging& s, hipStream_t stream) {
+  hipLaunchKernelGGL(residual_norm_quant_kernel, dim3(s.m_pad), dim3(kGlueThreads), 0, stream, x, d, ld_d, alpha,
+                     eps, M, H, s.m_pad, s.qxs, s.sxs);
+  W4A8_HIP(hipGetLastError());
+  return W4A8_OK;
+}
+
+int launch_cast_quant(const float* src, int64_t ld, int M, int H, const GemmStaging& s, hipStream_t stream) {
+  hipLaunchKernelGGL(cast_quant_kernel, dim3(s.m_pad), dim3(kGlueThreads), 0, stream, src, ld, M, H, s.m_pad,
+                     s.qxs, s.sxs);
+  W4A8_HIP(hipGetLastError());
+  return W4A8_OK;
+}
+
+int launch_gated_quant(const float* g, int M, int F, const GemmStaging& s, hipStream_t stream) {
+  hipLaunchKernelGGL(gated_quant_kernel, dim3(s.m_pad), dim3(kGlueThreads), 0, stream, g, M, F, s.m_pad, s.qxs,
+                     s.sxs);
   W4A8_HIP(hipGetLastError());
   return W4A8_OK;
 }

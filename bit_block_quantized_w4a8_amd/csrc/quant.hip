@@ -104,11 +104,7 @@ __global__ __launch_bounds__(256) void quantize_stage_kernel(const uint16_t* __r
   const int64_t e = 4 * b + g;  // 8-element group index within the row
   float v[8] = {0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f};
   if (m < M) unpack_half8(*reinterpret_cast<const uint4*>(x + m * K + 8 * e), v);
-  float scale;
-  const uint2 codes = quantize8_group4(v, &scale);
-  const int64_t row_slot = ((m >> 5) * 2 + (g & 1)) * 32 + (m & 31);
-  *reinterpret_cast<uint2*>(qxs + b * M_pad * kBlock + row_slot * 16 + 8 * (g >> 1)) = codes;
-  if (g == 0) sxs[b * M_pad + m] = scale;
+  quantize_to_staging(v, m, e, M_pad, qxs, sxs);
 }
 
 int launch_quantize_stage(const uint16_t* x, int M, int M_pad, int K, uint8_t* qxs, float* sxs,
