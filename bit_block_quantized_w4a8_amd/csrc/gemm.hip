@@ -509,15 +509,18 @@ Plan make_plan(int tn, int tm, int wn, int wm, int wk, int M, int N) {
 // problems take the widest workgroup tile that still fills the chip twice
 // over: the bytes staged per MFMA fall as the tile grows (the activation
 // codes of a block are shared by all BN weight columns).  Otherwise the four
-// waves of a workgroup split K over one small tile.  Split K across
-// workgroups only when even that leaves CUs idle.
+// waves of a workgroup split K over one 32 x 32 tile (measured on MI355X at
+// M = 512: 32 x 32 tiles beat 32 x 64 ones by 0.7-2 us on 2048 x 2560,
+// 2048 x 2048 and 8192 x 2048, fewer registers and more waves per SIMD
+// outweighing the extra staging).  Split K across workgroups only when even
+// that leaves CUs idle.
 Plan plan_gemm(int M, int K, int N) {
   constexpr int kCUs = 256;
   const int tm = M <= 32 ? 1 : 2;
   Plan p;
   if (M > 64) p = make_plan(1, 2, 4, 2, 1, M, N);       // 128 x 128, eight waves
   else p = make_plan(1, tm, 4, 1, 1, M, N);             // 128 x 32 or 128 x 64
-  if (p.tiles_n * p.tiles_m < 2 * kCUs) p = make_plan(1, tm, 1, 1, 4, M, N);
+  if (p.tiles_n * p.tiles_m < 2 * kCUs) p = make_plan(1, 1, 1, 1, 4, M, N);
   const int nb = K / kBlock;
   const int tiles = p.tiles_n * p.tiles_m;
   constexpr int kMinBlocksPerSplit = 64;
@@ -574,8 +577,7 @@ int launch_gemm_kernel(const GemmArgs& a, int mode, const GemmStaging& s, hipStr
 #define W4A8_GEMM_MODE(MODE)                                                                           \
   do {                                                                                                 \
     if (p.wk == 4) {                                                                                   \
-      if (p.tm == 2) W4A8_GEMM_LAUNCH(1, 2, 1, 1, 4, MODE);                                            \
-      else W4A8_GEMM_LAUNCH(1, 1, 1, 1, 4, MODE);                                                      \
+      W4A8_GEMM_LAUNCH(1, 1, 1, 1, 4, MODE);                                                           \
     } else if (p.wm == 2) {                                                                            \
       W4A8_GEMM_LAUNCH(1, 2, 4, 2, 1, MODE);                                                           \
     } else if (p.tm == 2) {                                                                            \

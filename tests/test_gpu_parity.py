@@ -229,7 +229,7 @@ def test_prefill_projection_sampled(proj):
 
 
 # One shape per GEMM tile plan: 128 x 32 (four waves along n), K split over four
-# waves at M <= 32, 128 x 64, K split at 32 < M <= 64 and M > 64, eight-wave
+# waves of one 32 x 32 tile (M <= 32, 32 < M <= 64 and M > 64), 128 x 64, eight-wave
 # 128 x 128, and K split across workgroups (few tiles, long K) at both M ranges.
 GEMM_PLANS = [(8, 64, 65536), (8, 96, 192), (40, 64, 65536), (40, 1024, 640), (130, 64, 32768),
               (130, 1024, 640), (8, 8192, 128), (130, 8192, 64)]
