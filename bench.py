@@ -8,7 +8,9 @@ replicas, 1.08 GB, defeats the 256 MB last-level cache).  value = algorithmic
 bytes of one layer / time of one layer, in GB/s; a step is one such layer.
 
 Also reported, each on its own keys: the prefill stage (the same projections at
-M = 512 with outlier channels, int8 TOPS against the int8 MFMA peak), the
+M = 512 with outlier channels, int8 TOPS against the int8 MFMA peak), the MX
+variant at the same prefill shapes (MXFP8 x MXFP4 on the block-scaled MFMA,
+against the fp8 peak), the
 decode-batch sweep on K = 4096, N = 14336 at M in {1, 2, 3, 4, 8, 16} for both
 kernels, the end-to-end token loop (26 layers + a 262144-entry LM head with
 the fused argmax, 512-token prefill, 128 decode steps with a host sync every
@@ -194,6 +196,38 @@ def bench_prefill(w4, torch, synth, timer, iters):
     return {"TOPS": round(tops, 1), "frac_int8_peak": round(tops / INT8_PEAK_TOPS, 4),
             "layer_us": round(tot_us, 2), "prefill_tokens_per_s_per_layer": round(512 / tot_us * 1e6, 1),
             "note": "per call: activation-quantisation pre-pass + GEMM, weights warm",
+            "per_projection": per}
+
+
+FP8_PEAK_TOPS = 5000.0         # MI355X dense fp8 MFMA (5.0 PFLOP/s)
+
+
+def bench_mx_prefill(w4, torch, synth, timer, iters):
+    """The MX variant (MXFP8 activations x MXFP4 weights, block-scaled MFMA) at the prefill
+    shapes, M = 512: pre-pass + GEMM per call, weights warm.  Weights are the fp16
+    dequantised int4 weights of the prefill workload, converted to MXFP4."""
+    inputs = synth.workload_inputs("prefill")
+    dev = torch.device("cuda:0")
+    per, tot_ops, tot_us = {}, 0, 0.0
+    for p, (x, qw, sw) in inputs.items():
+        m, k = x.shape
+        n = qw.shape[0]
+        wf = (qw.astype("float32") * sw.astype("float32").repeat(32, axis=1)).astype("float16")
+        packed, scales = w4.mx_pack_weights(torch.from_numpy(wf).to(dev))
+        xd = torch.from_numpy(x).to(dev)
+        out = torch.empty((m, n), dtype=torch.float32, device=dev)
+        for _ in range(3):
+            w4.mx_linear(xd, packed, scales, out=out)
+        us = 1000.0 * back_to_back(torch, timer, lambda i: w4.mx_linear(xd, packed, scales, out=out), iters)
+        ops = 2 * m * k * n
+        per[p] = {"M": m, "K": k, "N": n, "us": round(us, 2), "TOPS": round(ops / us / 1e6, 1),
+                  "frac_fp8_peak": round(ops / us / 1e6 / FP8_PEAK_TOPS, 4)}
+        tot_ops += ops
+        tot_us += us
+    tops = tot_ops / tot_us / 1e6
+    return {"TOPS": round(tops, 1), "frac_fp8_peak": round(tops / FP8_PEAK_TOPS, 4), "layer_us": round(tot_us, 2),
+            "note": "MX variant: MXFP8 x MXFP4 on v_mfma_scale_f32_32x32x64_f8f6f4; per call pre-pass + GEMM; "
+                    "a different numeric scheme from the headline path",
             "per_projection": per}
 
 
@@ -448,6 +482,9 @@ def main():
     pre = None if args.skip_prefill else bench_prefill(w4, torch, synth, timer, max(10, args.steps // 2))
     if pre:
         print(f"[bench] prefill done: {pre['TOPS']} TOPS", file=sys.stderr, flush=True)
+    mxp = None if args.skip_prefill else bench_mx_prefill(w4, torch, synth, timer, max(10, args.steps // 2))
+    if mxp:
+        print(f"[bench] MX prefill done: {mxp['TOPS']} TOPS", file=sys.stderr, flush=True)
     wide = None if args.skip_wide else bench_wide(w4, torch, synth, timer, max(10, args.steps // 2))
     if wide:
         print("[bench] decode-batch sweep done", file=sys.stderr, flush=True)
@@ -482,6 +519,7 @@ def main():
         "cpu_baseline": cpu,
         "decode_per_projection": dec["per_projection"],
         "prefill": pre,
+        "mx_prefill": mxp,
         "decode_batch_sweep": wide,
         "end_to_end": e2e,
     }

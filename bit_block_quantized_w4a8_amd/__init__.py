@@ -21,7 +21,7 @@ import torch
 __all__ = [
     "PATH_AUTO", "PATH_GEMV", "PATH_GEMM", "W4A8Error", "library_path", "load_library",
     "declared_functions", "init", "pack_weights", "linear", "linear_argmax",
-    "quantize_act", "block_sums", "gemv_max_m", "auto_path", "Weights", "residual_norm_cast",
+    "quantize_act", "block_sums", "gemv_max_m", "auto_path", "mx_pack_weights", "mx_quantize_act", "mx_linear", "Weights", "residual_norm_cast",
     "decoder_layer_workspace", "decoder_layer",
 ]
 
@@ -76,6 +76,9 @@ def load_library() -> ctypes.CDLL:
         "w4a8_block_sums": ([p, p, i64, i64, i64, p, i32, p], i32),
         "w4a8_gemv_max_m": ([], i32),
         "w4a8_auto_path": ([i64, i64, i64], i32),
+        "w4a8_mx_pack_weights": ([p, i64, i64, p, p, p], i32),
+        "w4a8_mx_quantize_act": ([p, i64, i64, p, p, p], i32),
+        "w4a8_mx_linear": ([p, p, p, i64, i64, i64, p, p], i32),
         "w4a8_residual_norm_cast": ([p, p, i64, ctypes.c_float, ctypes.c_float, i64, i64, p, p], i32),
         "w4a8_decoder_layer_workspace": ([i64, i64, ctypes.POINTER(_CWeights), ctypes.POINTER(_CWeights),
                                           ctypes.POINTER(ctypes.c_size_t)], i32),
@@ -252,6 +255,44 @@ def block_sums(x: torch.Tensor, packed: torch.Tensor, path: int = PATH_AUTO) -> 
 
 def gemv_max_m() -> int:
     return int(load_library().w4a8_gemv_max_m())
+
+
+def mx_pack_weights(w: torch.Tensor):
+    """MXFP4 weights from fp16 w [N][K]: (packed uint8 [K/32][N][16], scales uint8 [N][K/32])."""
+    assert w.dtype == torch.float16 and w.is_cuda and w.dim() == 2 and w.is_contiguous()
+    n, k = w.shape
+    packed = torch.empty((k // 32, n, 16), dtype=torch.uint8, device=w.device)
+    scales = torch.empty((n, k // 32), dtype=torch.uint8, device=w.device)
+    _ready(w)
+    _check("w4a8_mx_pack_weights", load_library().w4a8_mx_pack_weights(
+        w.data_ptr(), k, n, packed.data_ptr(), scales.data_ptr(), _stream(w)))
+    return packed, scales
+
+
+def mx_quantize_act(x: torch.Tensor):
+    """MXFP8 activations from fp16 x [M][K]: (codes uint8 [K/32][M][32], scales uint8 [M][K/32])."""
+    assert x.dtype == torch.float16 and x.is_cuda and x.dim() == 2 and x.is_contiguous()
+    m, k = x.shape
+    codes = torch.empty((k // 32, m, 32), dtype=torch.uint8, device=x.device)
+    scales = torch.empty((m, k // 32), dtype=torch.uint8, device=x.device)
+    _ready(x)
+    _check("w4a8_mx_quantize_act", load_library().w4a8_mx_quantize_act(
+        x.data_ptr(), m, k, codes.data_ptr(), scales.data_ptr(), _stream(x)))
+    return codes, scales
+
+
+def mx_linear(x: torch.Tensor, packed: torch.Tensor, scales: torch.Tensor, out: torch.Tensor | None = None):
+    """fp32 [M][N] = MXFP8(x) . MXFP4(W)^T (see w4a8_mx_linear)."""
+    assert x.dtype == torch.float16 and x.is_cuda and x.dim() == 2 and x.is_contiguous()
+    m, k = x.shape
+    n = packed.shape[1]
+    assert packed.shape == (k // 32, n, 16) and scales.shape == (n, k // 32)
+    if out is None:
+        out = torch.empty((m, n), dtype=torch.float32, device=x.device)
+    _ready(x)
+    _check("w4a8_mx_linear", load_library().w4a8_mx_linear(
+        x.data_ptr(), packed.data_ptr(), scales.data_ptr(), m, k, n, out.data_ptr(), _stream(x)))
+    return out
 
 
 def auto_path(m: int, k: int, n: int) -> int:

@@ -441,6 +441,48 @@ int w4a8_norm_linear_argmax(const float* x, float eps, const uint8_t* packed_w, 
   return launch_gemv(a, kGemvArgmax, stream);
 }
 
+int w4a8_mx_pack_weights(const uint16_t* w, int64_t K, int64_t N, uint8_t* packed, uint8_t* scales,
+                         hipStream_t stream) {
+  W4A8_REQUIRE(w && packed && scales, "null pointer");
+  int rc = check_shape(1, K, N, 1);
+  if (rc != W4A8_OK) return rc;
+  W4A8_REQUIRE(K % 64 == 0, "K = %lld must be a multiple of 64", static_cast<long long>(K));
+  W4A8_REQUIRE(aligned(w, 16) && aligned(packed, 16), "w and packed must be 16-byte aligned");
+  DeviceState* st = nullptr;
+  rc = current_state(&st);
+  if (rc != W4A8_OK) return rc;
+  return launch_mx_pack(w, static_cast<int>(K), static_cast<int>(N), packed, scales, stream);
+}
+
+int w4a8_mx_quantize_act(const uint16_t* x, int64_t M, int64_t K, uint8_t* codes, uint8_t* scales,
+                         hipStream_t stream) {
+  W4A8_REQUIRE(x && codes && scales, "null pointer");
+  int rc = check_shape(M, K, 64, int64_t{1} << 24);
+  if (rc != W4A8_OK) return rc;
+  W4A8_REQUIRE(K % 64 == 0, "K = %lld must be a multiple of 64", static_cast<long long>(K));
+  W4A8_REQUIRE(M * K < (int64_t{1} << 34), "M * K too large");
+  W4A8_REQUIRE(aligned(x, 16) && aligned(codes, 8), "misaligned pointer");
+  DeviceState* st = nullptr;
+  rc = current_state(&st);
+  if (rc != W4A8_OK) return rc;
+  return launch_mx_quantize_act(x, static_cast<int>(M), static_cast<int>(M), static_cast<int>(K), codes, scales,
+                                stream);
+}
+
+int w4a8_mx_linear(const uint16_t* x, const uint8_t* packed, const uint8_t* scales, int64_t M, int64_t K,
+                   int64_t N, float* out, hipStream_t stream) {
+  W4A8_REQUIRE(x && packed && scales && out, "null pointer");
+  int rc = check_shape(M, K, N, int64_t{1} << 20);
+  if (rc != W4A8_OK) return rc;
+  W4A8_REQUIRE(K % 64 == 0, "K = %lld must be a multiple of 64", static_cast<long long>(K));
+  W4A8_REQUIRE(aligned(x, 16) && aligned(packed, 16) && aligned(out, 4), "misaligned pointer");
+  DeviceState* st = nullptr;
+  rc = current_state(&st);
+  if (rc != W4A8_OK) return rc;
+  return launch_mx_linear(x, packed, scales, static_cast<int>(M), static_cast<int>(K), static_cast<int>(N), out,
+                          stream);
+}
+
 int w4a8_gemv_max_m(void) { return gemv_max_m(); }
 
 int w4a8_auto_path(int64_t M, int64_t K, int64_t N) { return auto_path(M, K, N); }

@@ -72,6 +72,16 @@ int gemm_staging(int M, int K, int N, GemmStaging* s);
 // The GEMM (scaled output) on activations already quantised into `s`.
 int launch_gemm_staged(const GemmArgs& a, const GemmStaging& s, hipStream_t stream);
 
+// MX variant (mx.hip): MXFP4 weights x MXFP8 activations on the block-scaled
+// matrix instruction.
+int mx_m_pad(int M);
+size_t mx_scratch_bytes(int M, int K);
+int launch_mx_quantize_act(const uint16_t* x, int M, int M_pad, int K, uint8_t* codes, uint8_t* scales,
+                           hipStream_t stream);
+int launch_mx_pack(const uint16_t* w, int K, int N, uint8_t* packed, uint8_t* scales, hipStream_t stream);
+int launch_mx_linear(const uint16_t* x, const uint8_t* packed, const uint8_t* wscales, int M, int K, int N,
+                     float* out, hipStream_t stream);
+
 int gemv_max_m();
 // Kernel W4A8_PATH_AUTO picks for an M x K by K x N linear.
 int auto_path(int64_t M, int64_t K, int64_t N);

@@ -209,6 +209,44 @@ W4A8_API int w4a8_gemv_max_m(void);
  */
 W4A8_API int w4a8_auto_path(int64_t M, int64_t K, int64_t N);
 
+/*
+ * MX variant (the pages' 4-bit weights in blocks of 32 -- ML Drift explainer on
+ * tech.dede.sh, section "Stage-aware optimization for large language models" --
+ * in the OCP Microscaling v1.0 formats that gfx950's block-scaled matrix
+ * instruction consumes).  Every block of 32 values along K shares an E8M0 scale
+ * byte c (value 2^(c - 127)), c = floor(log2(max |v|)) - emax + 127 (0 for an
+ * all-zero block); each value / scale is rounded to the element format, nearest
+ * with ties to even, saturating at the largest normal.  Weights use FP4 E2M1
+ * elements (emax 2, largest 6), activations FP8 E4M3 (emax 8, largest 448).
+ * A different numeric scheme from w4a8_linear: not interchangeable with it.
+ * K must be a multiple of 64, N of 64.  Errors as for w4a8_linear.
+ *
+ * w4a8_mx_pack_weights: w fp16 [N][K] (16-byte aligned, finite) ->
+ *   packed [K/32][N][16] (byte j of (block b, column n): element 32b+2j in the
+ *   low nibble, 32b+2j+1 in the high; 16-byte aligned) and
+ *   scales [N][K/32] E8M0 bytes.  Both outputs are caller-owned device memory.
+ */
+W4A8_API int w4a8_mx_pack_weights(const uint16_t* w, int64_t K, int64_t N, uint8_t* packed,
+                                  uint8_t* scales, hipStream_t stream);
+
+/*
+ * MXFP8 conversion of activations x fp16 [M][K] (16-byte aligned, finite), for
+ * verification: codes [K/32][M][32] E4M3 bytes (8-byte aligned), scales
+ * [M][K/32] E8M0 bytes -- the layout w4a8_mx_linear stages in library scratch.
+ */
+W4A8_API int w4a8_mx_quantize_act(const uint16_t* x, int64_t M, int64_t K, uint8_t* codes,
+                                  uint8_t* scales, hipStream_t stream);
+
+/*
+ * out fp32 [M][N] = MXFP8(x) . MXFP4(W)^T with both block scales:
+ *   out[m][n] = sum_b 2^(ca[m][b] + cw[n][b] - 254) * sum_{j<32} a[m][32b+j] w[n][32b+j],
+ * accumulated in fp32 by the matrix instruction.  x fp16 [M][K]; packed and
+ * scales from w4a8_mx_pack_weights.  The activations are converted into
+ * library scratch first (one pre-pass launch), then one GEMM launch.
+ */
+W4A8_API int w4a8_mx_linear(const uint16_t* x, const uint8_t* packed, const uint8_t* scales,
+                            int64_t M, int64_t K, int64_t N, float* out, hipStream_t stream);
+
 /* Message of the last failure on the calling thread ("" if none). */
 W4A8_API const char* w4a8_last_error(void);
 

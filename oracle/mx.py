@@ -162,3 +162,11 @@ def mx_linear_prequantized(qa, sa, qw, sw) -> np.ndarray:
     dots = np.einsum("mbj,nbj->mnb", va, vw)
     scale = np.exp2(sa.astype(np.float64)[:, None, :] + sw.astype(np.float64)[None, :, :] - 254.0)
     return np.sum(dots * scale, axis=2)
+
+
+def mx_abs_terms(qa, sa, qw, sw) -> np.ndarray:
+    """sum_k |a_k * w_k| of every output (fp64 [M][N]), the magnitude that bounds
+    the accumulation error of a reduced-precision dot product."""
+    va = np.abs(mx_dequantize(qa, sa, "e4m3"))
+    vw = np.abs(mx_dequantize(qw, sw, "e2m1"))
+    return va @ vw.T

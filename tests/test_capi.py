@@ -14,7 +14,7 @@ def lib():
 
 def test_exports_every_declared_symbol(lib):
     names = w4.declared_functions()
-    assert len(names) == 14, names
+    assert len(names) == 17, names
     for name in names:
         assert hasattr(lib, name), name
 

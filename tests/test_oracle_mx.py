@@ -126,3 +126,13 @@ def test_product_scales_exactly():
     x2 = (x.astype(np.float64) * 8).astype(np.float16)
     w2 = (w.astype(np.float64) / 4).astype(np.float16)
     assert np.array_equal(mx.mx_linear(x2, w2), base * 2)
+
+
+def test_abs_terms_equals_product_for_nonnegative_inputs():
+    """sum |a w| (the tolerance helper) is the product itself when every term is nonnegative."""
+    g = np.random.default_rng(6)
+    x = np.abs(g.standard_normal((3, 96))).astype(np.float16)
+    w = np.abs(g.standard_normal((5, 96)) * 0.1).astype(np.float16)
+    qa, sa = mx.mx_quantize(x, "e4m3")
+    qw, sw = mx.mx_quantize(w, "e2m1")
+    assert np.allclose(mx.mx_abs_terms(qa, sa, qw, sw), mx.mx_linear(x, w), rtol=1e-15, atol=0)
