@@ -258,11 +258,11 @@ def gemv_max_m() -> int:
 
 
 def mx_pack_weights(w: torch.Tensor):
-    """MXFP4 weights from fp16 w [N][K]: (packed uint8 [K/32][N][16], scales uint8 [N][K/32])."""
+    """MXFP4 weights from fp16 w [N][K]: (packed uint8 [K/32][N][16], scales uint8 [K/32][N])."""
     assert w.dtype == torch.float16 and w.is_cuda and w.dim() == 2 and w.is_contiguous()
     n, k = w.shape
     packed = torch.empty((k // 32, n, 16), dtype=torch.uint8, device=w.device)
-    scales = torch.empty((n, k // 32), dtype=torch.uint8, device=w.device)
+    scales = torch.empty((k // 32, n), dtype=torch.uint8, device=w.device)
     _ready(w)
     _check("w4a8_mx_pack_weights", load_library().w4a8_mx_pack_weights(
         w.data_ptr(), k, n, packed.data_ptr(), scales.data_ptr(), _stream(w)))
@@ -270,11 +270,11 @@ def mx_pack_weights(w: torch.Tensor):
 
 
 def mx_quantize_act(x: torch.Tensor):
-    """MXFP8 activations from fp16 x [M][K]: (codes uint8 [K/32][M][32], scales uint8 [M][K/32])."""
+    """MXFP8 activations from fp16 x [M][K]: (codes uint8 [K/32][M][32], scales uint8 [K/32][M])."""
     assert x.dtype == torch.float16 and x.is_cuda and x.dim() == 2 and x.is_contiguous()
     m, k = x.shape
     codes = torch.empty((k // 32, m, 32), dtype=torch.uint8, device=x.device)
-    scales = torch.empty((m, k // 32), dtype=torch.uint8, device=x.device)
+    scales = torch.empty((k // 32, m), dtype=torch.uint8, device=x.device)
     _ready(x)
     _check("w4a8_mx_quantize_act", load_library().w4a8_mx_quantize_act(
         x.data_ptr(), m, k, codes.data_ptr(), scales.data_ptr(), _stream(x)))
@@ -286,7 +286,7 @@ def mx_linear(x: torch.Tensor, packed: torch.Tensor, scales: torch.Tensor, out: 
     assert x.dtype == torch.float16 and x.is_cuda and x.dim() == 2 and x.is_contiguous()
     m, k = x.shape
     n = packed.shape[1]
-    assert packed.shape == (k // 32, n, 16) and scales.shape == (n, k // 32)
+    assert packed.shape == (k // 32, n, 16) and scales.shape == (k // 32, n)
     if out is None:
         out = torch.empty((m, n), dtype=torch.float32, device=x.device)
     _ready(x)

@@ -22,10 +22,13 @@
 // Layouts in memory (all K-block-major so that a lane's bytes are contiguous):
 //   weights  packed [K/32][N][16]: byte j of (block b, column n) holds
 //            element 32b + 2j in its low nibble and 32b + 2j + 1 in its high;
-//            scales [N][K/32] E8M0 bytes;
+//            scales [K/32][N] E8M0 bytes;
 //   activations (library staging) codes [K/32][M_pad][32] E4M3 bytes,
-//            scales [M_pad][K/32] E8M0 bytes (rows M .. M_pad-1 zero).
+//            scales [K/32][M_pad] E8M0 bytes (rows M .. M_pad-1 zero).
+// A K step (two blocks) of a 128 x 128 tile is then eight contiguous runs:
+// codes and weights of each block, and the scales of each block.
 #include "kernels.hpp"
+#include "lds_dma.hpp"
 
 namespace w4a8 {
 
@@ -122,7 +125,7 @@ __global__ __launch_bounds__(256) void mx_quantize_act_kernel(const uint16_t* __
 #pragma unroll
   for (int i = 0; i < 8; ++i) w[i >> 2] |= e4m3_code(v[i] * inv) << (8 * (i & 3));  // v * 2^-shared is exact
   *reinterpret_cast<uint2*>(codes + (b * M_pad + m) * kBlock + 8 * g) = make_uint2(w[0], w[1]);
-  if (g == 0) scales[m * nb + b] = static_cast<uint8_t>(sc);
+  if (g == 0) scales[b * M_pad + m] = static_cast<uint8_t>(sc);
 }
 
 // MXFP4 weights: one aligned quad per (column n, block b) of w [N][K].
@@ -147,7 +150,7 @@ __global__ __launch_bounds__(256) void mx_pack_kernel(const uint16_t* __restrict
 #pragma unroll
   for (int i = 0; i < 8; ++i) word |= e2m1_code(v[i] * inv) << (4 * i);
   *reinterpret_cast<uint32_t*>(packed + (b * N + n) * 16 + 4 * g) = word;
-  if (g == 0) scales[n * nb + b] = static_cast<uint8_t>(sc);
+  if (g == 0) scales[b * N + n] = static_cast<uint8_t>(sc);
 }
 
 // GEMM: four waves per workgroup, each wave a 64 x 64 output tile (2 x 2
@@ -189,7 +192,6 @@ __global__ __launch_bounds__(kMxThreads) void mx_gemm_kernel(const uint8_t* __re
   const int m_base = tm * kTileM + (WK == 1 ? (wave & 1) * 64 : 0);
   const int n_base = tn * kTileN + (WK == 1 ? (wave >> 1) * 64 : 0);
   const int wk = WK == 1 ? 0 : wave;
-  const int nb = K / kBlock;
   const int steps = K / 64;
 
   int rows[2], cols[2];
@@ -207,10 +209,10 @@ __global__ __launch_bounds__(kMxThreads) void mx_gemm_kernel(const uint8_t* __re
       const uint4 hi = *reinterpret_cast<const uint4*>(r0 + static_cast<int64_t>(M_pad) * kBlock);
       f.a[i][0] = lo.x; f.a[i][1] = lo.y; f.a[i][2] = lo.z; f.a[i][3] = lo.w;
       f.a[i][4] = hi.x; f.a[i][5] = hi.y; f.a[i][6] = hi.z; f.a[i][7] = hi.w;
-      f.sa[i] = ascale[static_cast<int64_t>(rows[i]) * nb + b0 + h];
+      f.sa[i] = ascale[static_cast<int64_t>(b0 + h) * M_pad + rows[i]];
       const uint4 wv = *reinterpret_cast<const uint4*>(packed + (static_cast<int64_t>(b0 + h) * N + cols[i]) * 16);
       f.b[i][0] = wv.x; f.b[i][1] = wv.y; f.b[i][2] = wv.z; f.b[i][3] = wv.w;
-      f.sb[i] = wscale[static_cast<int64_t>(cols[i]) * nb + b0 + h];
+      f.sb[i] = wscale[static_cast<int64_t>(b0 + h) * N + cols[i]];
     }
   };
 
@@ -287,6 +289,152 @@ __global__ __launch_bounds__(kMxThreads) void mx_gemm_kernel(const uint8_t* __re
     }
 }
 
+// GEMM with LDS staging: four waves (2 x 2, each 64 x 64) on a 128 x 128 tile.
+// A K step's operands (eight runs, 12800 bytes) are copied straight into LDS
+// with global_load_lds_dwordx4, 64 chunks of 16 bytes per instruction, into a
+// ring of three stages filled two steps ahead; each wave waits on its own
+// copies and one barrier per step publishes a stage, so every operand byte
+// crosses from L2 once per workgroup instead of once per wave.
+struct MxStage {
+  static constexpr int kA0 = 0;        // codes of block 2s, rows 0..127 (32 B each)
+  static constexpr int kA1 = 4096;     // codes of block 2s+1
+  static constexpr int kB0 = 8192;     // weights of block 2s, columns 0..127 (16 B each)
+  static constexpr int kB1 = 10240;    // weights of block 2s+1
+  static constexpr int kSA = 12288;    // activation scales, blocks 2s and 2s+1 (128 B each)
+  static constexpr int kSB = 12544;    // weight scales, blocks 2s and 2s+1
+  static constexpr int kChunks = 800;  // 12800 bytes
+  static constexpr int kGroups = 13;   // DMA instructions per stage (the last one half padding)
+  static constexpr int kBytes = kGroups * 1024;
+};
+
+__global__ __launch_bounds__(kMxThreads) void mx_gemm_lds_kernel(const uint8_t* __restrict__ codes,
+                                                                 const uint8_t* __restrict__ ascale,
+                                                                 const uint8_t* __restrict__ packed,
+                                                                 const uint8_t* __restrict__ wscale, int M,
+                                                                 int M_pad, int K, int N, int tiles_m,
+                                                                 float* __restrict__ out) {
+  __shared__ __attribute__((aligned(16))) uint8_t st0[MxStage::kBytes];
+  __shared__ __attribute__((aligned(16))) uint8_t st1[MxStage::kBytes];
+  __shared__ __attribute__((aligned(16))) uint8_t st2[MxStage::kBytes];
+  const int lane = threadIdx.x & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+  const int h = lane >> 5;
+  const int l32 = lane & 31;
+  const int tiles = gridDim.x;
+  const int id = (tiles & 7) == 0 ? (blockIdx.x & 7) * (tiles >> 3) + (blockIdx.x >> 3) : blockIdx.x;
+  const int tn = id / tiles_m;
+  const int tm = id % tiles_m;
+  const int m0 = tm * 128;
+  const int n0 = tn * 128;
+  const int steps = K / 64;
+  const int last = steps - 1;
+
+  // This lane's chunk of each of the wave's DMA instructions (groups wave,
+  // wave + 4, ...): source of step 0 and the source's advance per step.
+  constexpr int kL = (MxStage::kGroups + 3) / 4;  // 4 for wave 0, 3 for the others
+  const int my_loads = (MxStage::kGroups - wave + 3) / 4;
+  const uint8_t* src[kL];
+  uint32_t adv[kL];
+#pragma unroll
+  for (int i = 0; i < kL; ++i) {
+    const int c = min((wave + 4 * i) * 64 + lane, MxStage::kChunks - 1);  // padding lanes repeat chunk 799
+    if (c < 256) {
+      src[i] = codes + (static_cast<int64_t>(m0) * kBlock) + 16 * c;
+      adv[i] = 2u * static_cast<uint32_t>(M_pad) * kBlock;
+    } else if (c < 512) {
+      src[i] = codes + (static_cast<int64_t>(M_pad) + m0) * kBlock + 16 * (c - 256);
+      adv[i] = 2u * static_cast<uint32_t>(M_pad) * kBlock;
+    } else if (c < 768) {
+      const int blk = (c - 512) / 128;
+      const int col = min(n0 + (c - 512) % 128, N - 1);
+      src[i] = packed + (static_cast<int64_t>(blk) * N + col) * 16;
+      adv[i] = 2u * static_cast<uint32_t>(N) * 16;
+    } else if (c < 784) {
+      const int blk = (c - 768) / 8;
+      src[i] = ascale + static_cast<int64_t>(blk) * M_pad + m0 + 16 * ((c - 768) % 8);
+      adv[i] = 2u * static_cast<uint32_t>(M_pad);
+    } else {
+      const int blk = (c - 784) / 8;
+      src[i] = wscale + static_cast<int64_t>(blk) * N + min(n0 + 16 * ((c - 784) % 8), N - 16);
+      adv[i] = 2u * static_cast<uint32_t>(N);
+    }
+  }
+  auto dma = [&](uint8_t* st, int s) __attribute__((always_inline)) {
+    const uint32_t ss = static_cast<uint32_t>(min(s, last));
+#pragma unroll
+    for (int i = 0; i < kL; ++i)
+      if (i < my_loads) lds::dma16(src[i] + static_cast<uint64_t>(ss) * adv[i], st + (wave + 4 * i) * 1024);
+  };
+
+  v16f acc[2][2];
+#pragma unroll
+  for (int i = 0; i < 2; ++i)
+#pragma unroll
+    for (int j = 0; j < 2; ++j)
+#pragma unroll
+      for (int r = 0; r < 16; ++r) acc[i][j][r] = 0.0f;
+
+  const int wm = wave & 1, wn = wave >> 1;
+  auto compute = [&](const uint8_t* st) __attribute__((always_inline)) {
+    v8i a[2];
+    uint32_t sa[2];
+#pragma unroll
+    for (int i = 0; i < 2; ++i) {
+      const int r = wm * 64 + 32 * i + l32;
+      const uint4 lo = *reinterpret_cast<const uint4*>(st + MxStage::kA0 + r * 32 + 16 * h);
+      const uint4 hi = *reinterpret_cast<const uint4*>(st + MxStage::kA1 + r * 32 + 16 * h);
+      a[i][0] = lo.x; a[i][1] = lo.y; a[i][2] = lo.z; a[i][3] = lo.w;
+      a[i][4] = hi.x; a[i][5] = hi.y; a[i][6] = hi.z; a[i][7] = hi.w;
+      sa[i] = st[MxStage::kSA + 128 * h + r];
+    }
+#pragma unroll
+    for (int j = 0; j < 2; ++j) {
+      const int c = wn * 64 + 32 * j + l32;
+      const uint4 wv = *reinterpret_cast<const uint4*>(st + MxStage::kB0 + h * 2048 + c * 16);
+      const v8i bv = {static_cast<int>(wv.x), static_cast<int>(wv.y), static_cast<int>(wv.z), static_cast<int>(wv.w),
+                      0, 0, 0, 0};
+      const uint32_t sb = st[MxStage::kSB + 128 * h + c];
+#pragma unroll
+      for (int i = 0; i < 2; ++i)
+        acc[i][j] = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(a[i], bv, acc[i][j], kE4M3, kE2M1, 0, sa[i], 0,
+                                                                    sb);
+    }
+  };
+
+  // Step s: wait for this wave's copies of step s, publish the stage, refill
+  // the stage read last step with step s + 2, multiply step s.  At most two
+  // steps' copies are in flight, so vmcnt(my_loads) leaves exactly step s + 1's.
+#define W4A8_MX_STEP(CUR, REFILL, S)                                 \
+  do {                                                               \
+    if (my_loads == kL) lds::wait_vmcnt<kL>();                       \
+    else lds::wait_vmcnt<kL - 1>();                                  \
+    lds::stage_barrier();                                            \
+    dma((REFILL), (S) + 2);                                          \
+    if ((S) < steps) compute(CUR);                                   \
+  } while (0)
+  dma(st0, 0);
+  dma(st1, 1);
+  for (int s = 0; s < steps; s += 3) {
+    W4A8_MX_STEP(st0, st2, s + 0);
+    W4A8_MX_STEP(st1, st0, s + 1);
+    W4A8_MX_STEP(st2, st1, s + 2);
+  }
+#undef W4A8_MX_STEP
+  lds::wait_vmcnt<0>();  // copies past the end are still in flight
+
+#pragma unroll
+  for (int i = 0; i < 2; ++i)
+#pragma unroll
+    for (int j = 0; j < 2; ++j) {
+      const int n = n0 + wn * 64 + 32 * j + l32;
+#pragma unroll
+      for (int r = 0; r < 16; ++r) {
+        const int m = m0 + wm * 64 + 32 * i + 8 * (r / 4) + 4 * h + r % 4;
+        if (m < M && n < N) out[static_cast<int64_t>(m) * N + n] = acc[i][j][r];
+      }
+    }
+}
+
 size_t align256(size_t v) { return (v + 255) & ~static_cast<size_t>(255); }
 
 }  // namespace
@@ -295,7 +443,7 @@ int mx_m_pad(int M) { return (M + kMxRowPad - 1) / kMxRowPad * kMxRowPad; }
 
 size_t mx_scratch_bytes(int M, int K) {
   const size_t m_pad = mx_m_pad(M);
-  return align256(m_pad * K) + align256(m_pad * (K / kBlock));
+  return align256(m_pad * K) + align256(m_pad * (K / kBlock));  // codes, then scales [K/32][M_pad]
 }
 
 int launch_mx_quantize_act(const uint16_t* x, int M, int M_pad, int K, uint8_t* codes, uint8_t* scales,
@@ -330,7 +478,7 @@ int launch_mx_linear(const uint16_t* x, const uint8_t* packed, const uint8_t* ws
   constexpr int kCUs = 256;
   const int big = (m_pad / 128) * ((N + 127) / 128);
   if (big >= 2 * kCUs) {
-    hipLaunchKernelGGL(mx_gemm_kernel<1>, dim3(big), dim3(kMxThreads), 0, stream, codes, ascale, packed, wscales, M,
+    hipLaunchKernelGGL(mx_gemm_lds_kernel, dim3(big), dim3(kMxThreads), 0, stream, codes, ascale, packed, wscales, M,
                        m_pad, K, N, m_pad / 128, out);
   } else {
     const int tiles_m = m_pad / 64;

@@ -224,7 +224,7 @@ W4A8_API int w4a8_auto_path(int64_t M, int64_t K, int64_t N);
  * w4a8_mx_pack_weights: w fp16 [N][K] (16-byte aligned, finite) ->
  *   packed [K/32][N][16] (byte j of (block b, column n): element 32b+2j in the
  *   low nibble, 32b+2j+1 in the high; 16-byte aligned) and
- *   scales [N][K/32] E8M0 bytes.  Both outputs are caller-owned device memory.
+ *   scales [K/32][N] E8M0 bytes.  Both outputs are caller-owned device memory.
  */
 W4A8_API int w4a8_mx_pack_weights(const uint16_t* w, int64_t K, int64_t N, uint8_t* packed,
                                   uint8_t* scales, hipStream_t stream);
@@ -232,7 +232,7 @@ W4A8_API int w4a8_mx_pack_weights(const uint16_t* w, int64_t K, int64_t N, uint8
 /*
  * MXFP8 conversion of activations x fp16 [M][K] (16-byte aligned, finite), for
  * verification: codes [K/32][M][32] E4M3 bytes (8-byte aligned), scales
- * [M][K/32] E8M0 bytes -- the layout w4a8_mx_linear stages in library scratch.
+ * [K/32][M] E8M0 bytes -- the layout w4a8_mx_linear stages in library scratch.
  */
 W4A8_API int w4a8_mx_quantize_act(const uint16_t* x, int64_t M, int64_t K, uint8_t* codes,
                                   uint8_t* scales, hipStream_t stream);
