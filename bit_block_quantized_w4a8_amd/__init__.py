@@ -259,7 +259,7 @@ def gemv_max_m() -> int:
 
 def mx_pack_weights(w: torch.Tensor):
     """MXFP4 weights from fp16 w [N][K]: (packed uint8 [K/32][N][16], scales uint8 [K/32][N])."""
-    assert w.dtype == torch.float16 and w.is_cuda and w.dim() == 2 and w.is_contiguous()
+    _need(w, "w", torch.float16, 2)
     n, k = w.shape
     packed = torch.empty((k // 32, n, 16), dtype=torch.uint8, device=w.device)
     scales = torch.empty((k // 32, n), dtype=torch.uint8, device=w.device)
@@ -271,7 +271,7 @@ def mx_pack_weights(w: torch.Tensor):
 
 def mx_quantize_act(x: torch.Tensor):
     """MXFP8 activations from fp16 x [M][K]: (codes uint8 [K/32][M][32], scales uint8 [K/32][M])."""
-    assert x.dtype == torch.float16 and x.is_cuda and x.dim() == 2 and x.is_contiguous()
+    _need(x, "x", torch.float16, 2)
     m, k = x.shape
     codes = torch.empty((k // 32, m, 32), dtype=torch.uint8, device=x.device)
     scales = torch.empty((k // 32, m), dtype=torch.uint8, device=x.device)
@@ -283,10 +283,13 @@ def mx_quantize_act(x: torch.Tensor):
 
 def mx_linear(x: torch.Tensor, packed: torch.Tensor, scales: torch.Tensor, out: torch.Tensor | None = None):
     """fp32 [M][N] = MXFP8(x) . MXFP4(W)^T (see w4a8_mx_linear)."""
-    assert x.dtype == torch.float16 and x.is_cuda and x.dim() == 2 and x.is_contiguous()
+    _need(x, "x", torch.float16, 2)
+    _need(packed, "packed", torch.uint8, 3)
+    _need(scales, "scales", torch.uint8, 2)
     m, k = x.shape
     n = packed.shape[1]
-    assert packed.shape == (k // 32, n, 16) and scales.shape == (k // 32, n)
+    if packed.shape != (k // 32, n, 16) or scales.shape != (k // 32, n):
+        raise ValueError(f"MX weights of shape {tuple(packed.shape)} / {tuple(scales.shape)} do not match K = {k}")
     if out is None:
         out = torch.empty((m, n), dtype=torch.float32, device=x.device)
     _ready(x)

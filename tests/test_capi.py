@@ -90,3 +90,22 @@ def test_python_binding_rejects_cpu_tensors():
     with pytest.raises(TypeError):
         w4.linear(torch.zeros(1, 32, dtype=torch.float16), torch.zeros(1, 64, 16, dtype=torch.uint8),
                   torch.zeros(1, 64, dtype=torch.float16))
+
+
+def test_mx_entry_points_validate(lib):
+    """MX entry points reject null pointers, K not a multiple of 64, N not a multiple of 64
+    and misaligned operands before any HIP call; valid arguments then need w4a8_init."""
+    A = ALIGNED
+    assert lib.w4a8_mx_linear(P(A), P(A), P(A), 4, 96, 128, P(A), None) == w4.W4A8_EINVAL
+    assert lib.w4a8_mx_linear(P(A), P(A), P(A), 4, 128, 96, P(A), None) == w4.W4A8_EINVAL
+    assert lib.w4a8_mx_linear(P(0), P(A), P(A), 4, 128, 128, P(A), None) == w4.W4A8_EINVAL
+    assert lib.w4a8_mx_linear(P(A), P(A), P(0), 4, 128, 128, P(A), None) == w4.W4A8_EINVAL
+    assert lib.w4a8_mx_linear(P(A + 8), P(A), P(A), 4, 128, 128, P(A), None) == w4.W4A8_EINVAL
+    assert lib.w4a8_mx_linear(P(A), P(A), P(A), 0, 128, 128, P(A), None) == w4.W4A8_EINVAL
+    assert lib.w4a8_mx_linear(P(A), P(A), P(A), 4, 128, 128, P(A), None) == w4.W4A8_ENOINIT
+    assert lib.w4a8_mx_pack_weights(P(A), 32, 128, P(A), P(A), None) == w4.W4A8_EINVAL
+    assert lib.w4a8_mx_pack_weights(P(A), 64, 128, P(A + 4), P(A), None) == w4.W4A8_EINVAL
+    assert lib.w4a8_mx_pack_weights(P(A), 64, 128, P(A), P(A), None) == w4.W4A8_ENOINIT
+    assert lib.w4a8_mx_quantize_act(P(A), 3, 96, P(A), P(A), None) == w4.W4A8_EINVAL
+    assert lib.w4a8_mx_quantize_act(P(A), 3, 128, P(A + 4), P(A), None) == w4.W4A8_EINVAL
+    assert lib.w4a8_mx_quantize_act(P(A), 3, 128, P(A), P(A), None) == w4.W4A8_ENOINIT
