@@ -137,3 +137,26 @@ def e2e_prompt() -> np.ndarray:
     k = LM_HEAD_SHAPE[0]
     ch = outlier_channels(rng(seed, 2_000_001), k)
     return activations(rng(seed, 2_000_000), PREFILL_TOKENS, k, ch)
+
+
+# Decode attention of the synthetic layer: the QKV projection's 2560 outputs read as
+# 8 query heads of 256, one key head and one value head (2048 + 256 + 256), over an
+# fp16 KV cache of the pages' context of 640 positions (512 prefill + 128 decode).
+ATTN_HEADS = 8
+ATTN_KV_HEADS = 1
+ATTN_HEAD_DIM = 256
+CONTEXT = PREFILL_TOKENS + DECODE_TOKENS
+ATTN_Q_GAIN = 2.0   # query scale: scores about N(0, 4), so weight spreads over tens of positions
+WORKLOADS["attention"] = {"seed": 5, "M": [1], "shapes": {}, "outliers": False}
+
+
+def attention_inputs(seed: int, hq: int, hkv: int, d: int, length: int, q_gain: float = ATTN_Q_GAIN):
+    """Inputs of one decode-attention step over `length` positions (the newest included):
+    q fp32 [hq][d] = q_gain * N(0,1); k_new, v_new fp32 [hkv][d] = N(0,1);
+    k_past, v_past fp16 [hkv][length-1][d] = N(0,1) rounded once.  Tensor ids 0 .. 4."""
+    q = (rng(seed, 0).standard_normal((hq, d)) * q_gain).astype(np.float32)
+    k_new = rng(seed, 1).standard_normal((hkv, d)).astype(np.float32)
+    v_new = rng(seed, 2).standard_normal((hkv, d)).astype(np.float32)
+    k_past = rng(seed, 3).standard_normal((hkv, length - 1, d)).astype(np.float16)
+    v_past = rng(seed, 4).standard_normal((hkv, length - 1, d)).astype(np.float16)
+    return q, k_new, v_new, k_past, v_past
