@@ -21,7 +21,7 @@ import torch
 __all__ = [
     "PATH_AUTO", "PATH_GEMV", "PATH_GEMM", "W4A8Error", "library_path", "load_library",
     "declared_functions", "init", "pack_weights", "linear", "linear_argmax",
-    "quantize_act", "block_sums", "gemv_max_m", "auto_path", "mx_pack_weights", "mx_quantize_act", "mx_linear", "Weights", "residual_norm_cast",
+    "quantize_act", "block_sums", "gemv_max_m", "auto_path", "mx_pack_weights", "mx_quantize_act", "mx_linear", "kv_cache", "decode_attention", "Weights", "residual_norm_cast",
     "decoder_layer_workspace", "decoder_layer",
 ]
 
@@ -79,6 +79,7 @@ def load_library() -> ctypes.CDLL:
         "w4a8_mx_pack_weights": ([p, i64, i64, p, p, p], i32),
         "w4a8_mx_quantize_act": ([p, i64, i64, p, p, p], i32),
         "w4a8_mx_linear": ([p, p, p, i64, i64, i64, p, p], i32),
+        "w4a8_decode_attention": ([p, p, p, p, p, i64, i64, i64, i64, i64, p, p], i32),
         "w4a8_residual_norm_cast": ([p, p, i64, ctypes.c_float, ctypes.c_float, i64, i64, p, p], i32),
         "w4a8_decoder_layer_workspace": ([i64, i64, ctypes.POINTER(_CWeights), ctypes.POINTER(_CWeights),
                                           ctypes.POINTER(ctypes.c_size_t)], i32),
@@ -295,6 +296,39 @@ def mx_linear(x: torch.Tensor, packed: torch.Tensor, scales: torch.Tensor, out: 
     _ready(x)
     _check("w4a8_mx_linear", load_library().w4a8_mx_linear(
         x.data_ptr(), packed.data_ptr(), scales.data_ptr(), m, k, n, out.data_ptr(), _stream(x)))
+    return out
+
+
+def kv_cache(n_kv_heads: int, head_dim: int, capacity: int, device=None):
+    """Zeroed fp16 (k_cache [n_kv_heads][capacity][head_dim], v_cache [n_kv_heads][head_dim][capacity])
+    in the storage order w4a8_decode_attention reads."""
+    dev = torch.device("cuda", torch.cuda.current_device()) if device is None else torch.device(device)
+    return (torch.zeros((n_kv_heads, capacity, head_dim), dtype=torch.float16, device=dev),
+            torch.zeros((n_kv_heads, head_dim, capacity), dtype=torch.float16, device=dev))
+
+
+def decode_attention(q: torch.Tensor, k_new: torch.Tensor, v_new: torch.Tensor, k_cache: torch.Tensor,
+                     v_cache: torch.Tensor, length: int, out: torch.Tensor | None = None) -> torch.Tensor:
+    """fp16 [Hq][D] attention of the newest token (position length - 1, whose key and value
+    this call writes into the caches) over positions 0 .. length - 1 (see w4a8_decode_attention)."""
+    _need(q, "q", torch.float32, 2)
+    _need(k_new, "k_new", torch.float32, 2)
+    _need(v_new, "v_new", torch.float32, 2)
+    _need(k_cache, "k_cache", torch.float16, 3)
+    _need(v_cache, "v_cache", torch.float16, 3)
+    hq, d = q.shape
+    hkv, cap = k_new.shape[0], k_cache.shape[1]
+    if k_new.shape != (hkv, d) or v_new.shape != (hkv, d):
+        raise ValueError(f"k_new / v_new must be [{hkv}][{d}]")
+    if k_cache.shape != (hkv, cap, d) or v_cache.shape != (hkv, d, cap):
+        raise ValueError(f"caches of shape {tuple(k_cache.shape)} / {tuple(v_cache.shape)} do not match "
+                         f"[{hkv}][capacity][{d}] / [{hkv}][{d}][capacity]")
+    if out is None:
+        out = torch.empty((hq, d), dtype=torch.float16, device=q.device)
+    _ready(q)
+    _check("w4a8_decode_attention", load_library().w4a8_decode_attention(
+        q.data_ptr(), k_new.data_ptr(), v_new.data_ptr(), k_cache.data_ptr(), v_cache.data_ptr(),
+        hq, hkv, d, length, cap, out.data_ptr(), _stream(q)))
     return out
 
 

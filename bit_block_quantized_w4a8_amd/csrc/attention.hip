@@ -1,0 +1,329 @@
+// Decode attention: the newest token's query heads over an fp16 KV cache, the
+// step between a decoder layer's QKV and O projections.  The pages decode
+// with an fp16 KV cache at context 640 and store that cache in a layout
+// chosen for the GPU (ML Drift explainer on tech.dede.sh, section
+// "Stage-aware optimization for large language models").
+//
+// Computed: scaled dot-product attention with grouped query heads (query head
+// h reads KV head h / G, G = Hq / Hkv), softmax over the L cached positions,
+// the newest (position L - 1) included after its key and value are rounded to
+// fp16 and written into the cache by this same launch.
+//
+// Cache storage, chosen so that both products run on the fp16 matrix
+// instruction with operands read as contiguous runs:
+//   k_cache [Hkv][capacity][D]  -- scores S = Q K^T: a lane's B operand is a
+//                                  run of one position's dimensions
+//   v_cache [Hkv][D][capacity]  -- output O = P V: a lane's B operand is a run
+//                                  of one dimension's positions
+//
+// One workgroup (four waves) per 64-position chunk and KV head:
+//   1. loads its chunk of K and V and the group's fp32 queries in one round;
+//   2. S = [Q_hi; Q_lo] K^T on v_mfma_f32_16x16x16_f16, the 16 matrix rows
+//      holding the fp16 high parts of up to 8 query heads and, scaled by 2^12,
+//      their low parts (q = hi + lo / 2^12 to about 22 bits), so the fp32
+//      queries keep their precision on fp16 inputs at no extra instruction;
+//   3. a chunk-local softmax in base 2 (running max m, weight sum l);
+//   4. O = [P_hi; P_lo] V, the weights split the same way;
+//   5. writes (m, l, O) as a partial; the last workgroup of the KV head to
+//      finish (an atomic ticket) merges the partials in chunk order, so the
+//      result does not depend on which workgroup finishes when, and writes the
+//      fp16 output.
+#include <cmath>
+
+#include "kernels.hpp"
+
+namespace w4a8 {
+
+namespace {
+
+constexpr int kChunk = 64;          // positions per workgroup
+constexpr int kThreads = 256;       // four waves
+constexpr int kRows = 16;           // matrix rows: hi parts of 8 heads, then lo parts
+constexpr int kMaxGroup = 8;        // query heads per KV head
+constexpr float kLo = 4096.0f;      // lo parts are stored times 2^12
+constexpr float kInvLo = 1.0f / 4096.0f;
+
+typedef _Float16 h4 __attribute__((ext_vector_type(4)));
+typedef float f4 __attribute__((ext_vector_type(4)));
+
+struct AttnArgs {
+  const float* q;        // fp32 [Hkv * G][D]
+  const float* k_new;    // fp32 [Hkv][D]
+  const float* v_new;    // fp32 [Hkv][D]
+  uint16_t* k_cache;     // fp16 [Hkv][capacity][D]
+  uint16_t* v_cache;     // fp16 [Hkv][D][capacity]
+  uint16_t* out;         // fp16 [Hkv * G][D]
+  float* part;           // [Hkv][chunks][G][D] unnormalised chunk outputs
+  float* stats;          // [Hkv][chunks][G][2]: chunk max (base-2 units), weight sum
+  uint32_t* tickets;     // [Hkv], zero between launches
+  int group, length, capacity;
+  float scale2;          // log2(e) / sqrt(D)
+};
+
+__device__ __forceinline__ uint32_t pack2(_Float16 a, _Float16 b) {
+  return static_cast<uint32_t>(__builtin_bit_cast(unsigned short, a)) |
+         (static_cast<uint32_t>(__builtin_bit_cast(unsigned short, b)) << 16);
+}
+
+// The four fp16 values at half offset 4 * i of a run held as 16-byte words.
+__device__ __forceinline__ h4 half4_at(const uint4* run, int i) {
+  const uint4 w = run[i >> 1];
+  const uint2 v = (i & 1) ? make_uint2(w.z, w.w) : make_uint2(w.x, w.y);
+  return __builtin_bit_cast(h4, v);
+}
+
+// Sixteen positions of one dimension (two 16-byte words): positions at or past
+// `valid` become 0 (cache slots not yet written may hold any bits, and 0 * NaN
+// would reach the sum), and position `at` (if in 0 .. 15) becomes `fresh`.
+__device__ __forceinline__ void fix_run(uint4* run, int valid, int at, uint32_t fresh) {
+  uint32_t w[8] = {run[0].x, run[0].y, run[0].z, run[0].w, run[1].x, run[1].y, run[1].z, run[1].w};
+#pragma unroll
+  for (int i = 0; i < 16; ++i) {
+    const int sh = 16 * (i & 1);
+    uint32_t v = (w[i >> 1] >> sh) & 0xFFFFu;
+    v = i >= valid ? 0u : v;
+    v = i == at ? fresh : v;
+    w[i >> 1] = (w[i >> 1] & ~(0xFFFFu << sh)) | (v << sh);
+  }
+  run[0] = make_uint4(w[0], w[1], w[2], w[3]);
+  run[1] = make_uint4(w[4], w[5], w[6], w[7]);
+}
+
+template <int D>
+__global__ __launch_bounds__(kThreads) void decode_attention_kernel(AttnArgs a) {
+  constexpr int kSeg = D / 4;        // dimensions of a lane group's share of one key
+  constexpr int kSteps = D / 16;     // score MFMAs per wave
+  constexpr int kTiles = D / 64;     // 16-dimension output tiles per wave
+  constexpr int kQS = D + 8;         // LDS row strides (padded against bank conflicts)
+  constexpr int kSS = kChunk + 4;
+  constexpr int kPS = kChunk + 8;
+  __shared__ __align__(16) _Float16 q_hl[kRows * kQS];
+  __shared__ __align__(16) float s_raw[kRows * kSS];
+  __shared__ __align__(16) _Float16 p_hl[kRows * kPS];
+  __shared__ int last;
+
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const int col = lane & 15, lg = lane >> 4;
+  const int c = blockIdx.x, g = blockIdx.y, chunks = gridDim.x;
+  const int G = a.group, L = a.length, cap = a.capacity;
+  const int t0 = c * kChunk;
+  const int newest = L - 1;
+
+  // 1. Loads.  Key: this lane's position (column `col` of the wave's 16) and
+  // its lane group's quarter of the dimensions.  Value: sixteen positions of
+  // each of the wave's output dimensions.  Every address lies below the
+  // capacity, which is a multiple of the chunk.
+  const int tk = t0 + 16 * wave + col;
+  uint16_t* krow = a.k_cache + (static_cast<int64_t>(g) * cap + tk) * D + lg * kSeg;
+  uint4 kr[kSeg / 8];
+#pragma unroll
+  for (int i = 0; i < kSeg / 8; ++i) kr[i] = reinterpret_cast<const uint4*>(krow)[i];
+  uint4 vr[kTiles][2];
+#pragma unroll
+  for (int nt = 0; nt < kTiles; ++nt) {
+    const int d = wave * (D / 4) + 16 * nt + col;
+    const uint4* vrow =
+        reinterpret_cast<const uint4*>(a.v_cache + (static_cast<int64_t>(g) * D + d) * cap + t0 + 16 * lg);
+    vr[nt][0] = vrow[0];
+    vr[nt][1] = vrow[1];
+  }
+  // Queries of the group -> hi / lo rows of the A operand.
+  for (int it = tid; it < kMaxGroup * (D / 8); it += kThreads) {
+    const int h = it / (D / 8), d0 = (it % (D / 8)) * 8;
+    float v[8] = {0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f};
+    if (h < G) {
+      const float4* src = reinterpret_cast<const float4*>(a.q + (static_cast<int64_t>(g) * G + h) * D + d0);
+      const float4 x0 = src[0], x1 = src[1];
+      v[0] = x0.x; v[1] = x0.y; v[2] = x0.z; v[3] = x0.w;
+      v[4] = x1.x; v[5] = x1.y; v[6] = x1.z; v[7] = x1.w;
+    }
+    uint32_t hi[4], lo[4];
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      const _Float16 h0 = static_cast<_Float16>(v[2 * i]), h1 = static_cast<_Float16>(v[2 * i + 1]);
+      hi[i] = pack2(h0, h1);
+      lo[i] = pack2(static_cast<_Float16>((v[2 * i] - static_cast<float>(h0)) * kLo),
+                    static_cast<_Float16>((v[2 * i + 1] - static_cast<float>(h1)) * kLo));
+    }
+    *reinterpret_cast<uint4*>(q_hl + h * kQS + d0) = make_uint4(hi[0], hi[1], hi[2], hi[3]);
+    *reinterpret_cast<uint4*>(q_hl + (h + kMaxGroup) * kQS + d0) = make_uint4(lo[0], lo[1], lo[2], lo[3]);
+  }
+  // The newest token: its key and value enter the cache as fp16 here and are
+  // used in that form; no other workgroup reads position L - 1.
+  if (tk == newest) {
+    const float4* src = reinterpret_cast<const float4*>(a.k_new + static_cast<int64_t>(g) * D + lg * kSeg);
+#pragma unroll
+    for (int i = 0; i < kSeg / 8; ++i) {
+      const float4 x0 = src[2 * i], x1 = src[2 * i + 1];
+      kr[i] = make_uint4(pack2(static_cast<_Float16>(x0.x), static_cast<_Float16>(x0.y)),
+                         pack2(static_cast<_Float16>(x0.z), static_cast<_Float16>(x0.w)),
+                         pack2(static_cast<_Float16>(x1.x), static_cast<_Float16>(x1.y)),
+                         pack2(static_cast<_Float16>(x1.z), static_cast<_Float16>(x1.w)));
+      reinterpret_cast<uint4*>(krow)[i] = kr[i];
+    }
+  }
+  {
+    const int first = t0 + 16 * lg;   // position of element 0 of this lane's value runs
+    const int at = newest - first;
+#pragma unroll
+    for (int nt = 0; nt < kTiles; ++nt) {
+      const int d = wave * (D / 4) + 16 * nt + col;
+      uint32_t fresh = 0u;
+      if (at >= 0 && at < 16) {
+        const _Float16 v = static_cast<_Float16>(a.v_new[static_cast<int64_t>(g) * D + d]);
+        fresh = __builtin_bit_cast(unsigned short, v);
+        a.v_cache[(static_cast<int64_t>(g) * D + d) * cap + newest] = static_cast<uint16_t>(fresh);
+      }
+      fix_run(vr[nt], L - first, at, fresh);
+    }
+  }
+  __syncthreads();
+
+  // 2. Scores of the wave's 16 positions: row r of the result is head r's hi
+  // part (r < 8) or head r - 8's lo part; lane l holds rows 4 * (l / 16) + j
+  // of column l % 16.  The contraction index k = 4 * lg + j of step `ks` is
+  // dimension lg * D / 4 + 4 * ks + j, for the A and the B operand alike.
+  {
+    f4 acc = {0.f, 0.f, 0.f, 0.f};
+    const _Float16* qa = q_hl + col * kQS + lg * kSeg;
+#pragma unroll
+    for (int ks = 0; ks < kSteps; ++ks) {
+      const h4 av = *reinterpret_cast<const h4*>(qa + 4 * ks);
+      acc = __builtin_amdgcn_mfma_f32_16x16x16f16(av, half4_at(kr, ks), acc, 0, 0, 0);
+    }
+#pragma unroll
+    for (int j = 0; j < 4; ++j) s_raw[(4 * lg + j) * kSS + 16 * wave + col] = acc[j];
+  }
+  __syncthreads();
+
+  // 3. Chunk softmax: thread -> head tid / 32, positions 2 * (tid % 32) + {0, 1};
+  // the 32 threads of a head are one half of a wave.
+  {
+    const int h = tid >> 5, tt = 2 * (tid & 31);
+    float s[2];
+#pragma unroll
+    for (int e = 0; e < 2; ++e) {
+      const float v = (s_raw[h * kSS + tt + e] + s_raw[(h + kMaxGroup) * kSS + tt + e] * kInvLo) * a.scale2;
+      s[e] = t0 + tt + e < L ? v : -INFINITY;
+    }
+    float m = fmaxf(s[0], s[1]);
+#pragma unroll
+    for (int o = 1; o < 32; o <<= 1) m = fmaxf(m, __shfl_xor(m, o));
+    const float p0 = exp2f(s[0] - m), p1 = exp2f(s[1] - m);
+    float l = p0 + p1;
+#pragma unroll
+    for (int o = 1; o < 32; o <<= 1) l += __shfl_xor(l, o);
+    uint32_t hi = 0u, lo = 0u;
+    if (h < G) {
+      const _Float16 h0 = static_cast<_Float16>(p0), h1 = static_cast<_Float16>(p1);
+      hi = pack2(h0, h1);
+      lo = pack2(static_cast<_Float16>((p0 - static_cast<float>(h0)) * kLo),
+                 static_cast<_Float16>((p1 - static_cast<float>(h1)) * kLo));
+      if ((tid & 31) == 0) {
+        float* st = a.stats + ((static_cast<int64_t>(g) * chunks + c) * G + h) * 2;
+        store_agent(st, m);
+        store_agent(st + 1, l);
+      }
+    }
+    *reinterpret_cast<uint32_t*>(p_hl + h * kPS + tt) = hi;
+    *reinterpret_cast<uint32_t*>(p_hl + (h + kMaxGroup) * kPS + tt) = lo;
+  }
+  __syncthreads();
+
+  // 4. Chunk output of the wave's D / 4 dimensions: the contraction index of
+  // step `ks` is position 16 * lg + 4 * ks + j, matching the value runs.  Rows
+  // 0 .. 7 of the result sit in lanes 0 .. 31 and their lo rows 32 lanes up.
+  {
+    h4 pa[4];
+#pragma unroll
+    for (int ks = 0; ks < 4; ++ks) pa[ks] = *reinterpret_cast<const h4*>(p_hl + col * kPS + 16 * lg + 4 * ks);
+#pragma unroll
+    for (int nt = 0; nt < kTiles; ++nt) {
+      f4 acc = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+      for (int ks = 0; ks < 4; ++ks) acc = __builtin_amdgcn_mfma_f32_16x16x16f16(pa[ks], half4_at(vr[nt], ks), acc, 0, 0, 0);
+      const int d = wave * (D / 4) + 16 * nt + col;
+#pragma unroll
+      for (int j = 0; j < 4; ++j) {
+        const float up = __shfl_down(acc[j], 32);
+        const int h = 4 * lg + j;
+        if (lane < 32 && h < G)
+          store_agent(a.part + ((static_cast<int64_t>(g) * chunks + c) * G + h) * D + d, acc[j] + up * kInvLo);
+      }
+    }
+  }
+
+  // 5. Ticket; the last workgroup of this KV head merges every chunk in order.
+  __builtin_amdgcn_s_waitcnt(0);
+  __syncthreads();
+  if (tid == 0)
+    last = __hip_atomic_fetch_add(&a.tickets[g], 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) ==
+           static_cast<uint32_t>(chunks - 1);
+  __syncthreads();
+  if (!last) return;
+  const float* st = a.stats + static_cast<int64_t>(g) * chunks * G * 2;
+  const float* pp = a.part + static_cast<int64_t>(g) * chunks * G * D;
+  for (int it = tid; it < G * (D / 8); it += kThreads) {
+    const int h = it / (D / 8), d0 = (it % (D / 8)) * 8;
+    float mx = -INFINITY;
+    for (int cc = 0; cc < chunks; ++cc) mx = fmaxf(mx, load_agent(st + (cc * G + h) * 2));
+    float lsum = 0.f, acc[8] = {0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f};
+    for (int cc = 0; cc < chunks; ++cc) {
+      const float w = exp2f(load_agent(st + (cc * G + h) * 2) - mx);
+      lsum += w * load_agent(st + (cc * G + h) * 2 + 1);
+      const float* src = pp + (static_cast<int64_t>(cc) * G + h) * D + d0;
+#pragma unroll
+      for (int k = 0; k < 8; ++k) acc[k] += w * load_agent(src + k);
+    }
+    uint32_t o[4];
+#pragma unroll
+    for (int i = 0; i < 4; ++i)
+      o[i] = pack2(static_cast<_Float16>(acc[2 * i] / lsum), static_cast<_Float16>(acc[2 * i + 1] / lsum));
+    *reinterpret_cast<uint4*>(a.out + (static_cast<int64_t>(g) * G + h) * D + d0) = make_uint4(o[0], o[1], o[2], o[3]);
+  }
+  if (tid == 0) __hip_atomic_store(&a.tickets[g], 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+}
+
+}  // namespace
+
+int attention_chunks(int length) { return (length + kChunk - 1) / kChunk; }
+
+size_t attention_scratch_bytes(int n_kv_heads, int group, int head_dim, int length) {
+  return static_cast<size_t>(n_kv_heads) * attention_chunks(length) * group * (head_dim + 2) * sizeof(float);
+}
+
+int launch_decode_attention(const float* q, const float* k_new, const float* v_new, uint16_t* k_cache,
+                            uint16_t* v_cache, int n_heads, int n_kv_heads, int head_dim, int length, int capacity,
+                            uint16_t* out, Scratch* sc, hipStream_t stream) {
+  if (n_heads % n_kv_heads != 0 || n_heads / n_kv_heads > kMaxGroup || capacity % kChunk != 0 ||
+      length < 1 || length > capacity || n_kv_heads >= kMaxTickets - 1 ||
+      attention_scratch_bytes(n_kv_heads, n_heads / n_kv_heads, head_dim, length) > sc->work_bytes)
+    return hip_fail(hipErrorInvalidValue, "decode attention: shape outside the kernel's limits");
+  const int chunks = attention_chunks(length);
+  const int group = n_heads / n_kv_heads;
+  AttnArgs a{};
+  a.q = q;
+  a.k_new = k_new;
+  a.v_new = v_new;
+  a.k_cache = k_cache;
+  a.v_cache = v_cache;
+  a.out = out;
+  a.part = static_cast<float*>(sc->work);
+  a.stats = a.part + static_cast<size_t>(n_kv_heads) * chunks * group * head_dim;
+  a.tickets = sc->tickets + 1;
+  a.group = group;
+  a.length = length;
+  a.capacity = capacity;
+  a.scale2 = static_cast<float>(1.4426950408889634 / std::sqrt(static_cast<double>(head_dim)));
+  const dim3 grid(chunks, n_kv_heads);
+  switch (head_dim) {
+    case 64: hipLaunchKernelGGL(decode_attention_kernel<64>, grid, dim3(kThreads), 0, stream, a); break;
+    case 128: hipLaunchKernelGGL(decode_attention_kernel<128>, grid, dim3(kThreads), 0, stream, a); break;
+    case 256: hipLaunchKernelGGL(decode_attention_kernel<256>, grid, dim3(kThreads), 0, stream, a); break;
+    default: return hip_fail(hipErrorInvalidValue, "decode attention: head_dim must be 64, 128 or 256");
+  }
+  W4A8_HIP(hipGetLastError());
+  return W4A8_OK;
+}
+
+}  // namespace w4a8

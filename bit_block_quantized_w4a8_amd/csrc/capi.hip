@@ -483,6 +483,33 @@ int w4a8_mx_linear(const uint16_t* x, const uint8_t* packed, const uint8_t* scal
                           stream);
 }
 
+int w4a8_decode_attention(const float* q, const float* k_new, const float* v_new, uint16_t* k_cache,
+                          uint16_t* v_cache, int64_t n_heads, int64_t n_kv_heads, int64_t head_dim, int64_t length,
+                          int64_t capacity, uint16_t* out, hipStream_t stream) {
+  W4A8_REQUIRE(q && k_new && v_new && k_cache && v_cache && out, "null pointer");
+  W4A8_REQUIRE(head_dim == 64 || head_dim == 128 || head_dim == 256, "head_dim = %lld must be 64, 128 or 256",
+               static_cast<long long>(head_dim));
+  W4A8_REQUIRE(n_kv_heads >= 1 && n_kv_heads <= 4096, "n_kv_heads = %lld out of range [1, 4096]",
+               static_cast<long long>(n_kv_heads));
+  W4A8_REQUIRE(n_heads >= n_kv_heads && n_heads % n_kv_heads == 0 && n_heads / n_kv_heads <= 8,
+               "n_heads = %lld must be 1 to 8 times n_kv_heads = %lld", static_cast<long long>(n_heads),
+               static_cast<long long>(n_kv_heads));
+  W4A8_REQUIRE(capacity >= 64 && capacity % 64 == 0 && capacity <= (int64_t{1} << 24),
+               "capacity = %lld must be a multiple of 64 in [64, 2^24]", static_cast<long long>(capacity));
+  W4A8_REQUIRE(length >= 1 && length <= capacity, "length = %lld out of range [1, capacity = %lld]",
+               static_cast<long long>(length), static_cast<long long>(capacity));
+  W4A8_REQUIRE(n_kv_heads * capacity * head_dim < (int64_t{1} << 38), "KV cache too large");
+  W4A8_REQUIRE(aligned(q, 16) && aligned(k_new, 16) && aligned(v_new, 16) && aligned(out, 16) &&
+                   aligned(k_cache, 16) && aligned(v_cache, 16),
+               "every pointer must be 16-byte aligned");
+  const int Hq = static_cast<int>(n_heads), Hkv = static_cast<int>(n_kv_heads), D = static_cast<int>(head_dim);
+  const int Li = static_cast<int>(length), cap = static_cast<int>(capacity);
+  Scratch* sc = nullptr;
+  int rc = scratch_for(attention_scratch_bytes(Hkv, Hq / Hkv, D, Li), &sc);
+  if (rc != W4A8_OK) return rc;
+  return launch_decode_attention(q, k_new, v_new, k_cache, v_cache, Hq, Hkv, D, Li, cap, out, sc, stream);
+}
+
 int w4a8_gemv_max_m(void) { return gemv_max_m(); }
 
 int w4a8_auto_path(int64_t M, int64_t K, int64_t N) { return auto_path(M, K, N); }

@@ -142,6 +142,17 @@ __device__ __forceinline__ void unpack_half8(uint4 v, float* x) {
 __device__ __forceinline__ uint32_t low_nibbles_x16(uint32_t w) { return (w << 4) & kNibbleMask; }
 __device__ __forceinline__ uint32_t high_nibbles_x16(uint32_t w) { return w & kNibbleMask; }
 
+// Partial results handed between workgroups of one launch: agent-scope
+// accesses go to the device-coherent level, past the issuing CU's L1.
+__device__ __forceinline__ void store_agent(float* p, float v) {
+  __hip_atomic_store(reinterpret_cast<uint32_t*>(p), __float_as_uint(v), __ATOMIC_RELAXED,
+                     __HIP_MEMORY_SCOPE_AGENT);
+}
+__device__ __forceinline__ float load_agent(const float* p) {
+  return __uint_as_float(__hip_atomic_load(reinterpret_cast<uint32_t*>(const_cast<float*>(p)),
+                                           __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT));
+}
+
 // Total order on finite floats as unsigned keys, -0.0 mapped to +0.0.
 __device__ __forceinline__ uint32_t orderable_key(float v) {
   uint32_t b = __float_as_uint(v);

@@ -85,15 +85,6 @@ struct Stage {
   static_assert(2 * kMaxLoads <= 63, "vmcnt range");
 };
 
-__device__ __forceinline__ void store_agent(float* p, float v) {
-  __hip_atomic_store(reinterpret_cast<uint32_t*>(p), __float_as_uint(v), __ATOMIC_RELAXED,
-                     __HIP_MEMORY_SCOPE_AGENT);
-}
-__device__ __forceinline__ float load_agent(const float* p) {
-  return __uint_as_float(__hip_atomic_load(reinterpret_cast<uint32_t*>(const_cast<float*>(p)),
-                                           __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT));
-}
-
 // Source of one lane's DMA chunk: global address of its bytes in K block 0
 // of the region, the region's stride per K block, and which of the step's
 // WK blocks it belongs to.  Columns are clamped into range, so every lane of

@@ -82,6 +82,13 @@ int launch_mx_pack(const uint16_t* w, int K, int N, uint8_t* packed, uint8_t* sc
 int launch_mx_linear(const uint16_t* x, const uint8_t* packed, const uint8_t* wscales, int M, int K, int N,
                      float* out, hipStream_t stream);
 
+// Decode attention over an fp16 KV cache (attention.hip).
+int attention_chunks(int length);
+size_t attention_scratch_bytes(int n_kv_heads, int group, int head_dim, int length);
+int launch_decode_attention(const float* q, const float* k_new, const float* v_new, uint16_t* k_cache,
+                            uint16_t* v_cache, int n_heads, int n_kv_heads, int head_dim, int length, int capacity,
+                            uint16_t* out, Scratch* sc, hipStream_t stream);
+
 int gemv_max_m();
 // Kernel W4A8_PATH_AUTO picks for an M x K by K x N linear.
 int auto_path(int64_t M, int64_t K, int64_t N);

@@ -247,6 +247,41 @@ W4A8_API int w4a8_mx_quantize_act(const uint16_t* x, int64_t M, int64_t K, uint8
 W4A8_API int w4a8_mx_linear(const uint16_t* x, const uint8_t* packed, const uint8_t* scales,
                             int64_t M, int64_t K, int64_t N, float* out, hipStream_t stream);
 
+/*
+ * Decode attention of one new token over an fp16 KV cache: the step between
+ * a decoder layer's QKV and O projections.  The pages decode with an fp16 KV
+ * cache at context 640, kept in a layout chosen for the GPU (ML Drift
+ * explainer on tech.dede.sh, section "Stage-aware optimization for large
+ * language models"); the operation is scaled dot-product attention with
+ * grouped query heads (query head h reads KV head h / (n_heads / n_kv_heads)):
+ *
+ *   K_t, V_t = cache position t for t < length - 1; position length - 1 is the
+ *              new token, fp16(k_new), fp16(v_new), which this call writes into
+ *              both caches before attending to it
+ *   out[h]   = fp16( sum_t softmax_t(q[h] . K_t / sqrt(head_dim)) V_t ),
+ *              t = 0 .. length - 1, accumulated in fp32.
+ *
+ * q fp32 [n_heads][head_dim]; k_new, v_new fp32 [n_kv_heads][head_dim] (a QKV
+ * projection's output row, sliced, fits as is); out fp16 [n_heads][head_dim].
+ * Cache storage (fp16, caller-owned, positions 0 .. length - 2 written by
+ * earlier calls or by the caller):
+ *   k_cache [n_kv_heads][capacity][head_dim]  one contiguous vector per position
+ *   v_cache [n_kv_heads][head_dim][capacity]  one contiguous run of positions per
+ *                                             dimension (the order the output
+ *                                             product reads)
+ * Slots past length - 1 are read but never used, whatever they hold.
+ * Limits: head_dim 64, 128 or 256; 1 <= n_kv_heads <= 4096; n_heads a multiple
+ * of n_kv_heads, at most 8 times it; capacity a multiple of 64 in [64, 2^24];
+ * 1 <= length <= capacity; every pointer 16-byte aligned; |q|, |k_new|, |v_new|
+ * within fp16 range.  Uses library scratch (about n_kv_heads * length / 64 *
+ * n_heads / n_kv_heads * (head_dim + 2) * 4 bytes).  Errors: W4A8_EINVAL for
+ * arguments outside these limits, W4A8_ENOINIT, W4A8_EHIP.
+ */
+W4A8_API int w4a8_decode_attention(const float* q, const float* k_new, const float* v_new,
+                                   uint16_t* k_cache, uint16_t* v_cache, int64_t n_heads,
+                                   int64_t n_kv_heads, int64_t head_dim, int64_t length,
+                                   int64_t capacity, uint16_t* out, hipStream_t stream);
+
 /* Message of the last failure on the calling thread ("" if none). */
 W4A8_API const char* w4a8_last_error(void);
 

@@ -14,7 +14,7 @@ def lib():
 
 def test_exports_every_declared_symbol(lib):
     names = w4.declared_functions()
-    assert len(names) == 17, names
+    assert len(names) == 18, names
     for name in names:
         assert hasattr(lib, name), name
 
@@ -109,3 +109,28 @@ def test_mx_entry_points_validate(lib):
     assert lib.w4a8_mx_quantize_act(P(A), 3, 96, P(A), P(A), None) == w4.W4A8_EINVAL
     assert lib.w4a8_mx_quantize_act(P(A), 3, 128, P(A + 4), P(A), None) == w4.W4A8_EINVAL
     assert lib.w4a8_mx_quantize_act(P(A), 3, 128, P(A), P(A), None) == w4.W4A8_ENOINIT
+
+
+def test_decode_attention_validates(lib):
+    """w4a8_decode_attention rejects null or misaligned pointers, unsupported head sizes,
+    group sizes above 8, a capacity that is not a multiple of 64 and a length outside
+    [1, capacity] before any HIP call; valid arguments then need w4a8_init."""
+    A = ALIGNED
+    f = lib.w4a8_decode_attention
+
+    def call(q=A, kn=A, vn=A, kc=A, vc=A, hq=8, hkv=1, d=256, length=640, cap=640, out=A):
+        return f(P(q), P(kn), P(vn), P(kc), P(vc), hq, hkv, d, length, cap, P(out), None)
+
+    assert call(q=0) == w4.W4A8_EINVAL
+    assert call(vc=0) == w4.W4A8_EINVAL
+    assert call(out=A + 8) == w4.W4A8_EINVAL
+    assert call(kc=A + 2) == w4.W4A8_EINVAL
+    assert call(d=96) == w4.W4A8_EINVAL
+    assert call(hq=9, hkv=1) == w4.W4A8_EINVAL
+    assert call(hq=6, hkv=4) == w4.W4A8_EINVAL
+    assert call(hkv=0) == w4.W4A8_EINVAL
+    assert call(cap=600, length=600) == w4.W4A8_EINVAL
+    assert call(length=0) == w4.W4A8_EINVAL
+    assert call(length=641) == w4.W4A8_EINVAL
+    assert call() == w4.W4A8_ENOINIT
+    assert call(hq=16, hkv=2, d=64, length=1, cap=64) == w4.W4A8_ENOINIT
