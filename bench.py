@@ -12,7 +12,8 @@ M = 512 with outlier channels, int8 TOPS against the int8 MFMA peak), the MX
 variant at the same prefill shapes (MXFP8 x MXFP4 on the block-scaled MFMA,
 against the fp8 peak), the
 decode-batch sweep on K = 4096, N = 14336 at M in {1, 2, 3, 4, 8, 16} for both
-kernels, the end-to-end token loop (26 layers + a 262144-entry LM head with
+kernels, decode attention over an fp16 KV cache (8 query heads of 256 over one
+KV head, at context 640 and 32768), the end-to-end token loop (26 layers + a 262144-entry LM head with
 the fused argmax, 512-token prefill, 128 decode steps with a host sync every
 token; stream-ordered and replayed from a HIP graph), the roofline of the
 dominant kernel (the gate_up GEMV) and the CPU oracle timed on the host.
@@ -80,6 +81,7 @@ def parse():
     ap.add_argument("--skip-wide", action="store_true")
     ap.add_argument("--skip-cpu", action="store_true")
     ap.add_argument("--skip-e2e", action="store_true")
+    ap.add_argument("--skip-attention", action="store_true")
     ap.add_argument("--decode-steps", type=int, default=128)
     ap.add_argument("--profile-gemv", action="store_true",
                     help="only run the gate_up GEMV (cold weights) and a 256 MiB copy, for counter runs")
@@ -253,6 +255,44 @@ def bench_wide(w4, torch, synth, timer, iters):
         row["auto"] = "gemv" if w4.auto_path(m, k, n) == w4.PATH_GEMV else "gemm"
         res[f"M={m}"] = row
     return {"K": k, "N": n, "replicas": r, "results": res}
+
+
+def bench_attention(w4, torch, synth, timer, iters):
+    """Decode attention of the layer's 8 x 256 query heads over one fp16 KV head: at the
+    pages' context of 640 (cache warm: 655 KB) and at 32768 positions (cache cold through a
+    rotation of copies).  Bytes = the K and V cache read once + q, the new key and value, the
+    output and the two cache slots written."""
+    import numpy as np
+
+    dev = torch.device("cuda:0")
+    hq, hkv, d = synth.ATTN_HEADS, synth.ATTN_KV_HEADS, synth.ATTN_HEAD_DIM
+    res = {}
+    for length, cold in ((synth.CONTEXT, False), (32768, True)):
+        q, k_new, v_new, k_past, v_past = synth.attention_inputs(5, hq, hkv, d, length)
+        kc = np.zeros((hkv, length, d), np.float16)
+        vc = np.zeros((hkv, d, length), np.float16)
+        kc[:, :length - 1] = k_past
+        vc[:, :, :length - 1] = np.transpose(v_past, (0, 2, 1))
+        qd, knd, vnd = (torch.from_numpy(a).to(dev) for a in (q, k_new, v_new))
+        cache_bytes = 2 * kc.nbytes
+        r = max(1, -(-REPLICA_BYTES_MIN // cache_bytes)) if cold else 1
+        kd, vd = torch.from_numpy(kc).to(dev), torch.from_numpy(vc).to(dev)
+        caches = [(kd, vd)] + [(kd.clone(), vd.clone()) for _ in range(r - 1)]
+        out = torch.empty((hq, d), dtype=torch.float16, device=dev)
+        torch.cuda.synchronize()
+
+        def call(i):
+            kk, vv = caches[i % r]
+            w4.decode_attention(qd, knd, vnd, kk, vv, length, out=out)
+
+        for i in range(3):
+            call(i)
+        us = 1000.0 * back_to_back(torch, timer, call, iters)
+        b = cache_bytes + q.nbytes + k_new.nbytes + v_new.nbytes + hq * d * 2 + 2 * hkv * d * 2
+        res[f"L={length}"] = {"us": round(us, 2), "bytes": b, "GB_s": round(b / us / 1e3, 1),
+                              "frac_hbm": round(b / us / 1e3 / HBM_PEAK_GBS, 4),
+                              "cache": f"cold (rotation over {r} copies)" if cold else "warm"}
+    return {"heads": hq, "kv_heads": hkv, "head_dim": d, "results": res}
 
 
 E2E_EPS = 1e-6
@@ -488,6 +528,9 @@ def main():
     wide = None if args.skip_wide else bench_wide(w4, torch, synth, timer, max(10, args.steps // 2))
     if wide:
         print("[bench] decode-batch sweep done", file=sys.stderr, flush=True)
+    att = None if args.skip_attention else bench_attention(w4, torch, synth, timer, max(20, args.steps))
+    if att:
+        print(f"[bench] decode attention done: {att['results']}", file=sys.stderr, flush=True)
     e2e = None if args.skip_e2e else bench_e2e(w4, torch, synth, timer, args.decode_steps)
     if e2e:
         print(f"[bench] end-to-end done: {e2e['decode_tok_s_graph']} tok/s", file=sys.stderr, flush=True)
@@ -521,6 +564,7 @@ def main():
         "prefill": pre,
         "mx_prefill": mxp,
         "decode_batch_sweep": wide,
+        "decode_attention": att,
         "end_to_end": e2e,
     }
     print(json.dumps(line), flush=True)

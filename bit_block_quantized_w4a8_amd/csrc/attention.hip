@@ -24,10 +24,15 @@
 //      queries keep their precision on fp16 inputs at no extra instruction;
 //   3. a chunk-local softmax in base 2 (running max m, weight sum l);
 //   4. O = [P_hi; P_lo] V, the weights split the same way;
-//   5. writes (m, l, O) as a partial; the last workgroup of the KV head to
-//      finish (an atomic ticket) merges the partials in chunk order, so the
-//      result does not depend on which workgroup finishes when, and writes the
-//      fp16 output.
+//   5. writes (m, l, O) as a partial.  Chunks form at most kMaxGroups merge
+//      groups of consecutive chunks; the last workgroup of a group to finish
+//      (an atomic ticket) merges the group's partials in chunk order, and with
+//      more than one group the last group merger merges the group results in
+//      group order, so the result does not depend on which workgroup finishes
+//      when.  The final merge writes the fp16 output.  A merge keeps a running
+//      maximum (online softmax) and fetches eight partials per round, so its
+//      memory round trips grow with chunks / 8, not with chunks.
+#include <algorithm>
 #include <cmath>
 
 #include "kernels.hpp"
@@ -42,6 +47,9 @@ constexpr int kRows = 16;           // matrix rows: hi parts of 8 heads, then lo
 constexpr int kMaxGroup = 8;        // query heads per KV head
 constexpr float kLo = 4096.0f;      // lo parts are stored times 2^12
 constexpr float kInvLo = 1.0f / 4096.0f;
+constexpr int kMaxGroups = 8;       // merge groups per KV head
+constexpr int kGroupChunks = 64;    // chunks per merge group, at least
+constexpr int kMergeUnroll = 8;     // partials fetched per merge round
 
 typedef _Float16 h4 __attribute__((ext_vector_type(4)));
 typedef float f4 __attribute__((ext_vector_type(4)));
@@ -55,8 +63,11 @@ struct AttnArgs {
   uint16_t* out;         // fp16 [Hkv * G][D]
   float* part;           // [Hkv][chunks][G][D] unnormalised chunk outputs
   float* stats;          // [Hkv][chunks][G][2]: chunk max (base-2 units), weight sum
-  uint32_t* tickets;     // [Hkv], zero between launches
+  float* part2;          // [Hkv][kMaxGroups][G][D] unnormalised merge-group outputs
+  float* stats2;         // [Hkv][kMaxGroups][G][2]
+  uint32_t* tickets;     // [Hkv][kMaxGroups + 1], zero between launches
   int group, length, capacity;
+  int group_chunks;      // chunks per merge group
   float scale2;          // log2(e) / sqrt(D)
 };
 
@@ -87,6 +98,51 @@ __device__ __forceinline__ void fix_run(uint4* run, int valid, int at, uint32_t 
   }
   run[0] = make_uint4(w[0], w[1], w[2], w[3]);
   run[1] = make_uint4(w[4], w[5], w[6], w[7]);
+}
+
+__device__ __forceinline__ float2 load_agent2(const float* p) {
+  const uint64_t v = __hip_atomic_load(reinterpret_cast<uint64_t*>(const_cast<float*>(p)), __ATOMIC_RELAXED,
+                                       __HIP_MEMORY_SCOPE_AGENT);
+  return make_float2(__uint_as_float(static_cast<uint32_t>(v)), __uint_as_float(static_cast<uint32_t>(v >> 32)));
+}
+
+// Online-softmax merge of partials [cb, ce) of one query head h, dimensions
+// d0 .. d0 + 7: stats (max in base-2 units, weight sum) at st[(c * G + h) * 2],
+// unnormalised outputs at pp[(c * G + h) * D + d0 ..].  Returns the merged max
+// m, weight sum l and unnormalised output acc, taking the partials in index
+// order.  Each round fetches kMergeUnroll partials before using any.
+__device__ __forceinline__ void merge_range(const float* st, const float* pp, int G, int D, int h, int d0, int cb,
+                                            int ce, float& m, float& l, float acc[8]) {
+  m = -INFINITY;
+  l = 0.f;
+#pragma unroll
+  for (int k = 0; k < 8; ++k) acc[k] = 0.f;
+  for (int c0 = cb; c0 < ce; c0 += kMergeUnroll) {
+    float2 sv[kMergeUnroll], pv[kMergeUnroll][4];
+#pragma unroll
+    for (int u = 0; u < kMergeUnroll; ++u) {
+      const int cc = min(c0 + u, ce - 1);
+      sv[u] = load_agent2(st + (static_cast<int64_t>(cc) * G + h) * 2);
+      const float* src = pp + (static_cast<int64_t>(cc) * G + h) * D + d0;
+#pragma unroll
+      for (int k = 0; k < 4; ++k) pv[u][k] = load_agent2(src + 2 * k);
+    }
+#pragma unroll
+    for (int u = 0; u < kMergeUnroll; ++u) {
+      if (c0 + u < ce) {
+        const float mn = fmaxf(m, sv[u].x);   // every partial's max is finite
+        const float sc = exp2f(m - mn);       // 0 on the first partial (m = -inf)
+        const float w = exp2f(sv[u].x - mn);
+        l = l * sc + w * sv[u].y;
+#pragma unroll
+        for (int k = 0; k < 4; ++k) {
+          acc[2 * k] = acc[2 * k] * sc + w * pv[u][k].x;
+          acc[2 * k + 1] = acc[2 * k + 1] * sc + w * pv[u][k].y;
+        }
+        m = mn;
+      }
+    }
+  }
 }
 
 template <int D>
@@ -253,35 +309,58 @@ __global__ __launch_bounds__(kThreads) void decode_attention_kernel(AttnArgs a) 
     }
   }
 
-  // 5. Ticket; the last workgroup of this KV head merges every chunk in order.
+  // 5. Merge.  The last workgroup of this chunk's merge group to finish
+  // merges the group; with several groups, the last group merger merges the
+  // group results.  Tickets reset themselves once every member has arrived.
+  const int gsz = a.group_chunks;
+  const int ngroups = (chunks + gsz - 1) / gsz;
+  const int grp = c / gsz;
+  const int cb = grp * gsz, ce = min(chunks, cb + gsz);
+  uint32_t* tix = a.tickets + g * (kMaxGroups + 1);
   __builtin_amdgcn_s_waitcnt(0);
   __syncthreads();
   if (tid == 0)
-    last = __hip_atomic_fetch_add(&a.tickets[g], 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) ==
-           static_cast<uint32_t>(chunks - 1);
+    last = __hip_atomic_fetch_add(&tix[grp], 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) ==
+           static_cast<uint32_t>(ce - cb - 1);
   __syncthreads();
   if (!last) return;
+  if (tid == 0) __hip_atomic_store(&tix[grp], 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
   const float* st = a.stats + static_cast<int64_t>(g) * chunks * G * 2;
   const float* pp = a.part + static_cast<int64_t>(g) * chunks * G * D;
+  float* st2 = a.stats2 + static_cast<int64_t>(g) * kMaxGroups * G * 2;
+  float* pp2 = a.part2 + static_cast<int64_t>(g) * kMaxGroups * G * D;
+  if (ngroups > 1) {
+    for (int it = tid; it < G * (D / 8); it += kThreads) {
+      const int h = it / (D / 8), d0 = (it % (D / 8)) * 8;
+      float m, l, acc[8];
+      merge_range(st, pp, G, D, h, d0, cb, ce, m, l, acc);
+      if (d0 == 0) {
+        store_agent(st2 + (grp * G + h) * 2, m);
+        store_agent(st2 + (grp * G + h) * 2 + 1, l);
+      }
+#pragma unroll
+      for (int k = 0; k < 8; ++k) store_agent(pp2 + (static_cast<int64_t>(grp) * G + h) * D + d0 + k, acc[k]);
+    }
+    __builtin_amdgcn_s_waitcnt(0);
+    __syncthreads();
+    if (tid == 0)
+      last = __hip_atomic_fetch_add(&tix[kMaxGroups], 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) ==
+             static_cast<uint32_t>(ngroups - 1);
+    __syncthreads();
+    if (!last) return;
+    if (tid == 0) __hip_atomic_store(&tix[kMaxGroups], 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+  }
   for (int it = tid; it < G * (D / 8); it += kThreads) {
     const int h = it / (D / 8), d0 = (it % (D / 8)) * 8;
-    float mx = -INFINITY;
-    for (int cc = 0; cc < chunks; ++cc) mx = fmaxf(mx, load_agent(st + (cc * G + h) * 2));
-    float lsum = 0.f, acc[8] = {0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f};
-    for (int cc = 0; cc < chunks; ++cc) {
-      const float w = exp2f(load_agent(st + (cc * G + h) * 2) - mx);
-      lsum += w * load_agent(st + (cc * G + h) * 2 + 1);
-      const float* src = pp + (static_cast<int64_t>(cc) * G + h) * D + d0;
-#pragma unroll
-      for (int k = 0; k < 8; ++k) acc[k] += w * load_agent(src + k);
-    }
+    float m, l, acc[8];
+    if (ngroups > 1) merge_range(st2, pp2, G, D, h, d0, 0, ngroups, m, l, acc);
+    else merge_range(st, pp, G, D, h, d0, cb, ce, m, l, acc);
     uint32_t o[4];
 #pragma unroll
     for (int i = 0; i < 4; ++i)
-      o[i] = pack2(static_cast<_Float16>(acc[2 * i] / lsum), static_cast<_Float16>(acc[2 * i + 1] / lsum));
+      o[i] = pack2(static_cast<_Float16>(acc[2 * i] / l), static_cast<_Float16>(acc[2 * i + 1] / l));
     *reinterpret_cast<uint4*>(a.out + (static_cast<int64_t>(g) * G + h) * D + d0) = make_uint4(o[0], o[1], o[2], o[3]);
   }
-  if (tid == 0) __hip_atomic_store(&a.tickets[g], 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
 }
 
 }  // namespace
@@ -289,14 +368,15 @@ __global__ __launch_bounds__(kThreads) void decode_attention_kernel(AttnArgs a) 
 int attention_chunks(int length) { return (length + kChunk - 1) / kChunk; }
 
 size_t attention_scratch_bytes(int n_kv_heads, int group, int head_dim, int length) {
-  return static_cast<size_t>(n_kv_heads) * attention_chunks(length) * group * (head_dim + 2) * sizeof(float);
+  return static_cast<size_t>(n_kv_heads) * (attention_chunks(length) + kMaxGroups) * group * (head_dim + 2) *
+         sizeof(float);
 }
 
 int launch_decode_attention(const float* q, const float* k_new, const float* v_new, uint16_t* k_cache,
                             uint16_t* v_cache, int n_heads, int n_kv_heads, int head_dim, int length, int capacity,
                             uint16_t* out, Scratch* sc, hipStream_t stream) {
   if (n_heads % n_kv_heads != 0 || n_heads / n_kv_heads > kMaxGroup || capacity % kChunk != 0 ||
-      length < 1 || length > capacity || n_kv_heads >= kMaxTickets - 1 ||
+      length < 1 || length > capacity || n_kv_heads * (kMaxGroups + 1) >= kMaxTickets - 1 ||
       attention_scratch_bytes(n_kv_heads, n_heads / n_kv_heads, head_dim, length) > sc->work_bytes)
     return hip_fail(hipErrorInvalidValue, "decode attention: shape outside the kernel's limits");
   const int chunks = attention_chunks(length);
@@ -310,7 +390,10 @@ int launch_decode_attention(const float* q, const float* k_new, const float* v_n
   a.out = out;
   a.part = static_cast<float*>(sc->work);
   a.stats = a.part + static_cast<size_t>(n_kv_heads) * chunks * group * head_dim;
+  a.part2 = a.stats + static_cast<size_t>(n_kv_heads) * chunks * group * 2;
+  a.stats2 = a.part2 + static_cast<size_t>(n_kv_heads) * kMaxGroups * group * head_dim;
   a.tickets = sc->tickets + 1;
+  a.group_chunks = std::max(kGroupChunks, (chunks + kMaxGroups - 1) / kMaxGroups);
   a.group = group;
   a.length = length;
   a.capacity = capacity;
