@@ -21,8 +21,11 @@ dominant kernel (the gate_up GEMV) and the CPU oracle timed on the host.
 Timing: launches are queued behind a GPU sleep so the device runs them back to
 back, and two HIP events (torch.cuda.Event, recorded on the stream every
 kernel is launched on) bracket each timed batch: the K steps of the layer, and
-for every projection a batch of 4K launches of that projection alone, whose
-average is the per-launch duration used for the roofline.
+for every projection nine batches of K launches of that projection alone; the
+median batch mean is the per-launch duration used for the roofline (p10 and
+p90 of the batch means are reported beside it).  A background thread samples
+the GPU's clocks, power and temperature with amd-smi (a child process) while
+the bench runs and reports the busy samples under "device".
 """
 from __future__ import annotations
 
@@ -146,6 +149,75 @@ def back_to_back(torch, timer, launch, count):
     return t0.elapsed_time(t1) / count
 
 
+BATCHES = 9
+
+
+def percentile(sorted_vals, q):
+    """Nearest-rank percentile of an ascending list."""
+    k = max(0, min(len(sorted_vals) - 1, int(round(q / 100.0 * (len(sorted_vals) - 1)))))
+    return sorted_vals[k]
+
+
+class DeviceMonitor:
+    """Samples the GPU's clocks, power and temperature with `amd-smi metric` (a child process)
+    in a background thread while the bench runs; busy samples (graphics clock above 1 GHz)
+    are summarised, so that throttling shows up next to the figures it would distort."""
+
+    def __init__(self):
+        import threading
+        self.samples, self.error = [], None
+        self._stop = threading.Event()
+        self._thread = threading.Thread(target=self._run, daemon=True)
+
+    @staticmethod
+    def _value(d, *keys):
+        for k in keys:
+            if not isinstance(d, dict) or k not in d:
+                return None
+            d = d[k]
+        return float(d["value"]) if isinstance(d, dict) and isinstance(d.get("value"), (int, float)) else None
+
+    def _sample(self):
+        import subprocess
+        res = subprocess.run(["amd-smi", "metric", "-g", "0", "-c", "-p", "-t", "--json"], capture_output=True,
+                             text=True, timeout=20)
+        data = json.loads(res.stdout[res.stdout.index("{"):])
+        gpu = data["gpu_data"][0] if "gpu_data" in data else data[0]
+        clocks = gpu.get("clock", {})
+        gfx = [self._value(v, "clk") for k, v in clocks.items() if k.startswith("gfx")]
+        gfx = [g for g in gfx if g is not None]
+        return {"gfx_clk_MHz": sum(gfx) / len(gfx) if gfx else None,
+                "mem_clk_MHz": self._value(clocks, "mem_0", "clk"),
+                "power_W": self._value(gpu.get("power", {}), "socket_power"),
+                "hotspot_C": self._value(gpu.get("temperature", {}), "hotspot")}
+
+    def _run(self):
+        while not self._stop.is_set():
+            try:
+                self.samples.append(self._sample())
+            except Exception as e:  # the monitor never stops the bench
+                self.error = f"{type(e).__name__}: {e}"[:200]
+                return
+            self._stop.wait(0.5)
+
+    def start(self):
+        self._thread.start()
+        return self
+
+    def summary(self):
+        self._stop.set()
+        self._thread.join(timeout=30)
+        busy = [x for x in self.samples if (x["gfx_clk_MHz"] or 0) > 1000]
+        out = {"tool": "amd-smi metric -g 0 -c -p -t", "samples": len(self.samples), "busy_samples": len(busy)}
+        for key in ("gfx_clk_MHz", "mem_clk_MHz", "power_W", "hotspot_C"):
+            vals = sorted(x[key] for x in busy if x[key] is not None)
+            if vals:
+                out[key] = {"min": vals[0], "median": vals[len(vals) // 2], "max": vals[-1]}
+        if self.error:
+            out["error"] = self.error
+        return out
+
+
 def bench_decode(w4, torch, synth, timer, steps, warmup):
     inputs = synth.workload_inputs("decode")
     shapes = {p: (x.shape[0], x.shape[1], qw.shape[0]) for p, (x, qw, _) in inputs.items()}
@@ -168,10 +240,15 @@ def bench_decode(w4, torch, synth, timer, steps, warmup):
     ms_per_step = back_to_back(torch, timer, lambda i: step(warmup + i), steps)
     per = {}
     for p in names:
-        us = 1000.0 * back_to_back(torch, timer, lambda i, p=p: one(p, i), 4 * steps)
+        # BATCHES back-to-back batches of `steps` launches: the median batch mean is the
+        # per-launch time; p10 / p90 over the batches show the spread.
+        means = sorted(1000.0 * back_to_back(torch, timer, lambda i, p=p: one(p, i), steps)
+                       for _ in range(BATCHES))
+        us = means[len(means) // 2]
         b = algorithmic_bytes(*shapes[p])
         per[p] = {"M": shapes[p][0], "K": shapes[p][1], "N": shapes[p][2], "bytes": b,
-                  "us": round(us, 3), "GB_s": round(b / us / 1e3, 1),
+                  "us": round(us, 3), "us_p10": round(percentile(means, 10), 3),
+                  "us_p90": round(percentile(means, 90), 3), "GB_s": round(b / us / 1e3, 1),
                   "frac_hbm": round(b / us / 1e3 / HBM_PEAK_GBS, 4)}
     return {"layer_bytes": layer_bytes, "ms_per_step": ms_per_step, "replicas": r,
             "rotation_bytes": r * layer_bytes, "per_projection": per}
@@ -517,6 +594,7 @@ def main():
         profile_gemv(w4, torch, synth)
         return
     timer = Timer(torch)
+    monitor = DeviceMonitor().start()
     dec = bench_decode(w4, torch, synth, timer, args.steps, args.warmup)
     print(f"[bench] decode done: {dec['ms_per_step'] * 1e3:.2f} us per layer", file=sys.stderr, flush=True)
     pre = None if args.skip_prefill else bench_prefill(w4, torch, synth, timer, max(10, args.steps // 2))
@@ -534,6 +612,7 @@ def main():
     e2e = None if args.skip_e2e else bench_e2e(w4, torch, synth, timer, args.decode_steps)
     if e2e:
         print(f"[bench] end-to-end done: {e2e['decode_tok_s_graph']} tok/s", file=sys.stderr, flush=True)
+    device = monitor.summary()
     cpu = None if args.skip_cpu else cpu_baseline(synth, args.cpu_seconds)
 
     value = dec["layer_bytes"] / (dec["ms_per_step"] * 1e-3) / 1e9
@@ -558,7 +637,9 @@ def main():
         "roofline": {"bound": "hbm", "kernel": GATE_UP_KERNEL + " (gate_up 2048x16384, M=1)",
                      "achieved": gu["GB_s"], "peak": HBM_PEAK_GBS, "unit": "GB/s",
                      "frac": round(gu["GB_s"] / HBM_PEAK_GBS, 4), "traffic": measured_traffic(),
-                     "bytes_per_launch": gu["bytes"], "us_per_launch": gu["us"]},
+                     "bytes_per_launch": gu["bytes"], "us_per_launch": gu["us"],
+                     "us_per_launch_p10_p90": [gu["us_p10"], gu["us_p90"]]},
+        "device": device,
         "cpu_baseline": cpu,
         "decode_per_projection": dec["per_projection"],
         "prefill": pre,
