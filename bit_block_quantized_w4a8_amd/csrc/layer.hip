@@ -22,6 +22,9 @@ namespace w4a8 {
 namespace {
 
 constexpr int kGlueThreads = 256;
+// Rows of up to kRegGroups * kGlueThreads 8-element groups stay in registers
+// between the sum of squares and the quantisation.
+constexpr int kRegGroups = 2;
 
 // Fixed-order workgroup sum: wave shuffles, then the 4 wave totals in order.
 __device__ __forceinline__ float block_sum(float v, float* red) {
@@ -55,6 +58,24 @@ __global__ __launch_bounds__(kGlueThreads) void residual_norm_cast_kernel(
   const float inv = 1.0f / sqrtf(block_sum(ss, red) / static_cast<float>(H) + eps);
   if (y)
     for (int h = threadIdx.x; h < H; h += kGlueThreads) y[m * H + h] = float_to_half_bits(xr[h] * inv);
+}
+
+// x += alpha * d with no normalised output: elementwise, four floats per
+// thread over the whole [M][H] block (H and ld_d multiples of 4, 16-byte
+// aligned rows); the same one fma per element as the kernel above.
+__global__ __launch_bounds__(kGlueThreads) void residual_add_kernel(float* __restrict__ x, const float* __restrict__ d,
+                                                                    int64_t ld_d, float alpha, int H, int64_t total4) {
+  const int64_t t = static_cast<int64_t>(blockIdx.x) * kGlueThreads + threadIdx.x;
+  if (t >= total4) return;
+  const int64_t m = (4 * t) / H;
+  const int64_t h = 4 * t - m * H;
+  float4 v = *reinterpret_cast<const float4*>(x + m * H + h);
+  const float4 dv = *reinterpret_cast<const float4*>(d + m * ld_d + h);
+  v.x = fmaf(alpha, dv.x, v.x);
+  v.y = fmaf(alpha, dv.y, v.y);
+  v.z = fmaf(alpha, dv.z, v.z);
+  v.w = fmaf(alpha, dv.w, v.w);
+  *reinterpret_cast<float4*>(x + m * H + h) = v;
 }
 
 // dst[m][h] = fp16(src[m * ld + h]) for h < H.
@@ -98,6 +119,44 @@ __global__ __launch_bounds__(kGlueThreads) void residual_norm_quant_kernel(
   }
   float* xr = x + m * H;
   float ss = 0.0f;
+  if (groups <= kRegGroups * kGlueThreads) {  // uniform: the row stays in registers
+    float4 lo[kRegGroups], hi[kRegGroups];
+#pragma unroll
+    for (int i = 0; i < kRegGroups; ++i) {
+      const int e = threadIdx.x + i * kGlueThreads;
+      if (e < groups) {
+        lo[i] = *reinterpret_cast<const float4*>(xr + 8 * e);
+        hi[i] = *reinterpret_cast<const float4*>(xr + 8 * e + 4);
+        if (d) {
+          const float4 d0 = *reinterpret_cast<const float4*>(d + m * ld_d + 8 * e);
+          const float4 d1 = *reinterpret_cast<const float4*>(d + m * ld_d + 8 * e + 4);
+          lo[i].x = fmaf(alpha, d0.x, lo[i].x); lo[i].y = fmaf(alpha, d0.y, lo[i].y);
+          lo[i].z = fmaf(alpha, d0.z, lo[i].z); lo[i].w = fmaf(alpha, d0.w, lo[i].w);
+          hi[i].x = fmaf(alpha, d1.x, hi[i].x); hi[i].y = fmaf(alpha, d1.y, hi[i].y);
+          hi[i].z = fmaf(alpha, d1.z, hi[i].z); hi[i].w = fmaf(alpha, d1.w, hi[i].w);
+          *reinterpret_cast<float4*>(xr + 8 * e) = lo[i];
+          *reinterpret_cast<float4*>(xr + 8 * e + 4) = hi[i];
+        }
+        ss = fmaf(lo[i].x, lo[i].x, ss); ss = fmaf(lo[i].y, lo[i].y, ss);
+        ss = fmaf(lo[i].z, lo[i].z, ss); ss = fmaf(lo[i].w, lo[i].w, ss);
+        ss = fmaf(hi[i].x, hi[i].x, ss); ss = fmaf(hi[i].y, hi[i].y, ss);
+        ss = fmaf(hi[i].z, hi[i].z, ss); ss = fmaf(hi[i].w, hi[i].w, ss);
+      }
+    }
+    const float inv = 1.0f / sqrtf(block_sum(ss, red) / static_cast<float>(H) + eps);
+#pragma unroll
+    for (int i = 0; i < kRegGroups; ++i) {
+      const int e = threadIdx.x + i * kGlueThreads;
+      if (e < groups) {
+        const float raw[8] = {lo[i].x, lo[i].y, lo[i].z, lo[i].w, hi[i].x, hi[i].y, hi[i].z, hi[i].w};
+        float v[8];
+#pragma unroll
+        for (int k = 0; k < 8; ++k) v[k] = half_bits_to_float(float_to_half_bits(raw[k] * inv));
+        quantize_to_staging(v, m, e, m_pad, qxs, sxs);
+      }
+    }
+    return;
+  }
   for (int e = threadIdx.x; e < groups; e += kGlueThreads) {
     float4 lo = *reinterpret_cast<const float4*>(xr + 8 * e);
     float4 hi = *reinterpret_cast<const float4*>(xr + 8 * e + 4);
@@ -146,11 +205,14 @@ __global__ __launch_bounds__(kGlueThreads) void cast_quant_kernel(const float* _
 }
 
 // fp16(g[m][f] * g[m][F + f]) for f < F, quantised into staging.
+// Rows are split over gridDim.x workgroups, one 8-element group per thread
+// (F / 8 is a multiple of 4, so quads of lanes are whole blocks, in range or not).
 __global__ __launch_bounds__(kGlueThreads) void gated_quant_kernel(const float* __restrict__ g, int M, int F,
                                                                    int m_pad, uint8_t* __restrict__ qxs,
                                                                    float* __restrict__ sxs) {
-  const int64_t m = blockIdx.x;
-  for (int e = threadIdx.x; e < F / 8; e += kGlueThreads) {
+  const int64_t m = blockIdx.y;
+  const int e = blockIdx.x * kGlueThreads + threadIdx.x;
+  if (e < F / 8) {
     float v[8] = {0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f};
     if (m < M) {  // uniform
       const float* row = g + m * 2 * static_cast<int64_t>(F) + 8 * e;
@@ -173,6 +235,15 @@ size_t align256(size_t v) { return (v + 255) & ~static_cast<size_t>(255); }
 
 int launch_residual_norm_cast(float* x, const float* d, int64_t ld_d, float alpha, float eps, int M, int H,
                               uint16_t* y, hipStream_t stream) {
+  const bool vec = d && !y && H % 4 == 0 && ld_d % 4 == 0 && reinterpret_cast<uintptr_t>(x) % 16 == 0 &&
+                   reinterpret_cast<uintptr_t>(d) % 16 == 0;
+  if (vec) {
+    const int64_t total4 = static_cast<int64_t>(M) * H / 4;
+    hipLaunchKernelGGL(residual_add_kernel, dim3(static_cast<unsigned>((total4 + kGlueThreads - 1) / kGlueThreads)),
+                       dim3(kGlueThreads), 0, stream, x, d, ld_d, alpha, H, total4);
+    W4A8_HIP(hipGetLastError());
+    return W4A8_OK;
+  }
   hipLaunchKernelGGL(residual_norm_cast_kernel, dim3(M), dim3(kGlueThreads), 0, stream, x, d, ld_d, alpha,
                      eps, H, y);
   W4A8_HIP(hipGetLastError());
@@ -209,8 +280,8 @@ int launch_cast_quant(const float* src, int64_t ld, int M, int H, const GemmStag
 }
 
 int launch_gated_quant(const float* g, int M, int F, const GemmStaging& s, hipStream_t stream) {
-  hipLaunchKernelGGL(gated_quant_kernel, dim3(s.m_pad), dim3(kGlueThreads), 0, stream, g, M, F, s.m_pad, s.qxs,
-                     s.sxs);
+  hipLaunchKernelGGL(gated_quant_kernel, dim3((F / 8 + kGlueThreads - 1) / kGlueThreads, s.m_pad), dim3(kGlueThreads),
+                     0, stream, g, M, F, s.m_pad, s.qxs, s.sxs);
   W4A8_HIP(hipGetLastError());
   return W4A8_OK;
 }
