@@ -206,7 +206,8 @@ class DeviceMonitor:
 
     def summary(self):
         self._stop.set()
-        self._thread.join(timeout=30)
+        if self._thread.is_alive():
+            self._thread.join(timeout=30)
         busy = [x for x in self.samples if (x["gfx_clk_MHz"] or 0) > 1000]
         out = {"tool": "amd-smi metric -g 0 -c -p -t", "samples": len(self.samples), "busy_samples": len(busy)}
         for key in ("gfx_clk_MHz", "mem_clk_MHz", "power_W", "hotspot_C"):
