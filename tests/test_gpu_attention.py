@@ -73,7 +73,8 @@ def run(q, k_new, v_new, k_past, v_past, capacity, seed=0):
 
 # (Hq, Hkv, D, length, capacity): the layer's 8 x 256 heads over one KV head at the pages'
 # context of 640 and at the first decode step after the 512-token prefill; one chunk,
-# one position, a chunk plus one; grouped, multi-head and odd group sizes; long context.
+# one position, a chunk plus one; grouped, multi-head and odd group sizes; long contexts
+# whose chunk partials are merged in two levels.
 CASES = [
     (ATTN_HEADS, ATTN_KV_HEADS, ATTN_HEAD_DIM, CONTEXT, CONTEXT),
     (ATTN_HEADS, ATTN_KV_HEADS, ATTN_HEAD_DIM, PREFILL_TOKENS + 1, CONTEXT),
@@ -86,7 +87,8 @@ CASES = [
     (8, 8, 128, 200, 256),
     (5, 1, 64, 1000, 1024),
     (16, 2, 256, 2048, 2112),
-    (8, 1, 256, 32768, 32768),
+    (4, 2, 128, 5000, 5056),      # two merge groups of unequal size (64 + 15 chunks)
+    (8, 1, 256, 32768, 32768),    # eight merge groups of 64 chunks
 ]
 
 
