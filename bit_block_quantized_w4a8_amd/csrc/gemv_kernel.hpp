@@ -40,11 +40,21 @@ constexpr int kRowsMax = 8;        // token rows per launch
 constexpr int kMaxLoadsPerLane = 16;
 constexpr int kMaxChunkBlocks = 256;
 
+// Task g of a chunk (8 activations) -> row m and 8-element group e of the
+// chunk: m = g / (4 nbc), e = g % (4 nbc).  One-row kernels (MR = 1) only see
+// g < 4 nbc, so they skip the integer division (about 40 instructions ahead
+// of the first load).
+template <int MR>
+__device__ __forceinline__ int task_row(int g, int nbc) { return MR == 1 ? 0 : g / (nbc * 4); }
+template <int MR>
+__device__ __forceinline__ int task_group(int g, int nbc) { return MR == 1 ? g : g % (nbc * 4); }
+
 // 16 bytes (8 fp16) of activations for quantisation task g of a chunk:
-// task g = (row m, block e / 4, quarter e % 4) with m = g / (4 nbc), e = g % (4 nbc).
+// task g = (row m, block e / 4, quarter e % 4).
+template <int MR>
 __device__ __forceinline__ uint4 load_x16(const uint16_t* __restrict__ x, int K, int kb0, int nbc, int g) {
-  const int m = g / (nbc * 4);
-  const int e = g % (nbc * 4);
+  const int m = task_row<MR>(g, nbc);
+  const int e = task_group<MR>(g, nbc);
   return *reinterpret_cast<const uint4*>(x + static_cast<int64_t>(m) * K +
                                          static_cast<int64_t>(kb0) * kBlock + 8 * e);
 }
@@ -153,15 +163,15 @@ __global__ __launch_bounds__(T) void gemv_kernel(GemvArgs a, uint32_t* __restric
 #pragma unroll
       for (int j = 0; j < XQ; ++j) {
         const int g = min(j * T + tid, tasks - 1);
-        const int m = g / (nbc * 4);
-        const int e = g % (nbc * 4);
+        const int m = task_row<MR>(g, nbc);
+        const int e = task_group<MR>(g, nbc);
         const float* p = a.xf + static_cast<int64_t>(m) * K + static_cast<int64_t>(kb0) * kBlock + 8 * e;
         xa[j] = *reinterpret_cast<const float4*>(p);
         xb[j] = *reinterpret_cast<const float4*>(p + 4);
       }
     } else {
 #pragma unroll
-      for (int j = 0; j < XQ; ++j) xv[j] = load_x16(x, K, kb0, nbc, min(j * T + tid, tasks - 1));
+      for (int j = 0; j < XQ; ++j) xv[j] = load_x16<MR>(x, K, kb0, nbc, min(j * T + tid, tasks - 1));
     }
     __builtin_amdgcn_sched_barrier(0);  // keep the activation loads ahead of the weights
     uint4 w[R];
@@ -180,8 +190,8 @@ __global__ __launch_bounds__(T) void gemv_kernel(GemvArgs a, uint32_t* __restric
       float scale;
       const uint2 codes = quantize8_group4(v, &scale);
       if (g < tasks) {
-        const int m = g / (nbc * 4);
-        const int e = g % (nbc * 4);
+        const int m = task_row<MR>(g, nbc);
+        const int e = task_group<MR>(g, nbc);
         *reinterpret_cast<uint2*>(&q_lds[m][e >> 2][2 * (e & 3)]) = codes;
         if ((e & 3) == 0) s_lds[m][e >> 2] = scale * 0.0625f;
       }
@@ -196,7 +206,7 @@ __global__ __launch_bounds__(T) void gemv_kernel(GemvArgs a, uint32_t* __restric
       for (int j = 0; j < XQ; ++j) {
         const int g = j * T + tid;
         if (g < tasks) {
-          const int m = g / (nbc * 4);
+          const int m = task_row<MR>(g, nbc);
           float q = xa[j].x * xa[j].x;
           q = fmaf(xa[j].y, xa[j].y, q);
           q = fmaf(xa[j].z, xa[j].z, q);
@@ -230,7 +240,7 @@ __global__ __launch_bounds__(T) void gemv_kernel(GemvArgs a, uint32_t* __restric
       for (int j = 0; j < XQ; ++j) {
         if (j * T < tasks) {  // uniform
           const int g = j * T + tid;
-          const int m = min(g, tasks - 1) / (nbc * 4);
+          const int m = task_row<MR>(min(g, tasks - 1), nbc);
           float im = inv[0];
 #pragma unroll
           for (int mm = 1; mm < MR; ++mm)
@@ -263,7 +273,7 @@ __global__ __launch_bounds__(T) void gemv_kernel(GemvArgs a, uint32_t* __restric
       for (int j = 0; j < XQ; ++j) keep ^= xv[j].x;
       for (int t0 = XQ * T; t0 < tasks; t0 += XQ * T) {
 #pragma unroll
-        for (int j = 0; j < XQ; ++j) xv[j] = load_x16(x, K, kb0, nbc, min(t0 + j * T + tid, tasks - 1));
+        for (int j = 0; j < XQ; ++j) xv[j] = load_x16<MR>(x, K, kb0, nbc, min(t0 + j * T + tid, tasks - 1));
         quantize_batch(t0);
       }
     }
