@@ -61,37 +61,37 @@ __global__ __launch_bounds__(kGlueThreads) void residual_norm_cast_kernel(
 }
 
 // x += alpha * d with no normalised output: elementwise, four floats per
-// thread over the whole [M][H] block (H and ld_d multiples of 4, 16-byte
-// aligned rows); the same one fma per element as the kernel above.
+// thread (H and ld_d multiples of 4, 16-byte aligned rows), the grid's y
+// dimension walking the rows; the same one fma per element as the kernel above.
 __global__ __launch_bounds__(kGlueThreads) void residual_add_kernel(float* __restrict__ x, const float* __restrict__ d,
-                                                                    int64_t ld_d, float alpha, int H, int64_t total4) {
-  const int64_t t = static_cast<int64_t>(blockIdx.x) * kGlueThreads + threadIdx.x;
-  if (t >= total4) return;
-  const int64_t m = (4 * t) / H;
-  const int64_t h = 4 * t - m * H;
-  float4 v = *reinterpret_cast<const float4*>(x + m * H + h);
-  const float4 dv = *reinterpret_cast<const float4*>(d + m * ld_d + h);
-  v.x = fmaf(alpha, dv.x, v.x);
-  v.y = fmaf(alpha, dv.y, v.y);
-  v.z = fmaf(alpha, dv.z, v.z);
-  v.w = fmaf(alpha, dv.w, v.w);
-  *reinterpret_cast<float4*>(x + m * H + h) = v;
+                                                                    int64_t ld_d, float alpha, int M, int H) {
+  const int h = 4 * (blockIdx.x * kGlueThreads + threadIdx.x);
+  if (h >= H) return;
+  for (int64_t m = blockIdx.y; m < M; m += gridDim.y) {  // grid y: rows
+    float4 v = *reinterpret_cast<const float4*>(x + m * H + h);
+    const float4 dv = *reinterpret_cast<const float4*>(d + m * ld_d + h);
+    v.x = fmaf(alpha, dv.x, v.x);
+    v.y = fmaf(alpha, dv.y, v.y);
+    v.z = fmaf(alpha, dv.z, v.z);
+    v.w = fmaf(alpha, dv.w, v.w);
+    *reinterpret_cast<float4*>(x + m * H + h) = v;
+  }
 }
 
 // dst[m][h] = fp16(src[m * ld + h]) for h < H.
 __global__ __launch_bounds__(kGlueThreads) void cast_rows_kernel(const float* __restrict__ src, int64_t ld,
-                                                                 int H, uint16_t* __restrict__ dst) {
-  const int64_t m = blockIdx.y;
+                                                                 int M, int H, uint16_t* __restrict__ dst) {
   const int h = blockIdx.x * kGlueThreads + threadIdx.x;
-  if (h < H) dst[m * H + h] = float_to_half_bits(src[m * ld + h]);
+  if (h >= H) return;
+  for (int64_t m = blockIdx.y; m < M; m += gridDim.y) dst[m * H + h] = float_to_half_bits(src[m * ld + h]);
 }
 
 // u[m][f] = fp16(fp32(g[m][f] * g[m][F + f])) for f < F (rows of g hold 2F values).
-__global__ __launch_bounds__(kGlueThreads) void gated_cast_kernel(const float* __restrict__ g, int F,
+__global__ __launch_bounds__(kGlueThreads) void gated_cast_kernel(const float* __restrict__ g, int M, int F,
                                                                   uint16_t* __restrict__ u) {
-  const int64_t m = blockIdx.y;
   const int f = blockIdx.x * kGlueThreads + threadIdx.x;
-  if (f < F) {
+  if (f >= F) return;
+  for (int64_t m = blockIdx.y; m < M; m += gridDim.y) {
     const float* row = g + m * 2 * static_cast<int64_t>(F);
     u[m * F + f] = float_to_half_bits(row[f] * row[F + f]);
   }
@@ -210,9 +210,9 @@ __global__ __launch_bounds__(kGlueThreads) void cast_quant_kernel(const float* _
 __global__ __launch_bounds__(kGlueThreads) void gated_quant_kernel(const float* __restrict__ g, int M, int F,
                                                                    int m_pad, uint8_t* __restrict__ qxs,
                                                                    float* __restrict__ sxs) {
-  const int64_t m = blockIdx.y;
   const int e = blockIdx.x * kGlueThreads + threadIdx.x;
-  if (e < F / 8) {
+  if (e >= F / 8) return;
+  for (int64_t m = blockIdx.y; m < m_pad; m += gridDim.y) {  // grid y: staging rows
     float v[8] = {0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f};
     if (m < M) {  // uniform
       const float* row = g + m * 2 * static_cast<int64_t>(F) + 8 * e;
@@ -238,9 +238,8 @@ int launch_residual_norm_cast(float* x, const float* d, int64_t ld_d, float alph
   const bool vec = d && !y && H % 4 == 0 && ld_d % 4 == 0 && reinterpret_cast<uintptr_t>(x) % 16 == 0 &&
                    reinterpret_cast<uintptr_t>(d) % 16 == 0;
   if (vec) {
-    const int64_t total4 = static_cast<int64_t>(M) * H / 4;
-    hipLaunchKernelGGL(residual_add_kernel, dim3(static_cast<unsigned>((total4 + kGlueThreads - 1) / kGlueThreads)),
-                       dim3(kGlueThreads), 0, stream, x, d, ld_d, alpha, H, total4);
+    const dim3 grid((H / 4 + kGlueThreads - 1) / kGlueThreads, M < 65535 ? M : 65535);
+    hipLaunchKernelGGL(residual_add_kernel, grid, dim3(kGlueThreads), 0, stream, x, d, ld_d, alpha, M, H);
     W4A8_HIP(hipGetLastError());
     return W4A8_OK;
   }
@@ -251,15 +250,15 @@ int launch_residual_norm_cast(float* x, const float* d, int64_t ld_d, float alph
 }
 
 int launch_cast_rows(const float* src, int64_t ld, int M, int H, uint16_t* dst, hipStream_t stream) {
-  hipLaunchKernelGGL(cast_rows_kernel, dim3((H + kGlueThreads - 1) / kGlueThreads, M), dim3(kGlueThreads), 0,
-                     stream, src, ld, H, dst);
+  hipLaunchKernelGGL(cast_rows_kernel, dim3((H + kGlueThreads - 1) / kGlueThreads, M < 65535 ? M : 65535),
+                     dim3(kGlueThreads), 0, stream, src, ld, M, H, dst);
   W4A8_HIP(hipGetLastError());
   return W4A8_OK;
 }
 
 int launch_gated_cast(const float* g, int M, int F, uint16_t* u, hipStream_t stream) {
-  hipLaunchKernelGGL(gated_cast_kernel, dim3((F + kGlueThreads - 1) / kGlueThreads, M), dim3(kGlueThreads), 0,
-                     stream, g, F, u);
+  hipLaunchKernelGGL(gated_cast_kernel, dim3((F + kGlueThreads - 1) / kGlueThreads, M < 65535 ? M : 65535),
+                     dim3(kGlueThreads), 0, stream, g, M, F, u);
   W4A8_HIP(hipGetLastError());
   return W4A8_OK;
 }
@@ -280,8 +279,9 @@ int launch_cast_quant(const float* src, int64_t ld, int M, int H, const GemmStag
 }
 
 int launch_gated_quant(const float* g, int M, int F, const GemmStaging& s, hipStream_t stream) {
-  hipLaunchKernelGGL(gated_quant_kernel, dim3((F / 8 + kGlueThreads - 1) / kGlueThreads, s.m_pad), dim3(kGlueThreads),
-                     0, stream, g, M, F, s.m_pad, s.qxs, s.sxs);
+  hipLaunchKernelGGL(gated_quant_kernel,
+                     dim3((F / 8 + kGlueThreads - 1) / kGlueThreads, s.m_pad < 65535 ? s.m_pad : 65535),
+                     dim3(kGlueThreads), 0, stream, g, M, F, s.m_pad, s.qxs, s.sxs);
   W4A8_HIP(hipGetLastError());
   return W4A8_OK;
 }

@@ -106,26 +106,27 @@ __device__ __forceinline__ uint32_t block_scale(float amax, float* inv_scale) {
 __global__ __launch_bounds__(256) void mx_quantize_act_kernel(const uint16_t* __restrict__ x, int M, int M_pad,
                                                               int K, uint8_t* __restrict__ codes,
                                                               uint8_t* __restrict__ scales) {
-  const int64_t t = static_cast<int64_t>(blockIdx.x) * blockDim.x + threadIdx.x;
+  // x of the grid: rows (four lanes each); y: blocks (no runtime division).
+  const int tx = blockIdx.x * blockDim.x + threadIdx.x;
+  if (tx >= 4 * M_pad) return;  // whole quads in or out (4 | 256)
   const int nb = K / kBlock;
-  if (t >= static_cast<int64_t>(M_pad) * nb * 4) return;  // whole quads in or out (4 | 256)
-  const int g = static_cast<int>(t & 3);
-  const int64_t q = t >> 2;
-  const int64_t m = q % M_pad;
-  const int64_t b = q / M_pad;
-  float v[8] = {0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f};
-  if (m < M) unpack_half8(*reinterpret_cast<const uint4*>(x + m * K + b * kBlock + 8 * g), v);
-  float amax = 0.0f;
+  const int g = tx & 3;
+  const int64_t m = tx >> 2;
+  for (int64_t b = blockIdx.y; b < nb; b += gridDim.y) {
+    float v[8] = {0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f};
+    if (m < M) unpack_half8(*reinterpret_cast<const uint4*>(x + m * K + b * kBlock + 8 * g), v);
+    float amax = 0.0f;
 #pragma unroll
-  for (int i = 0; i < 8; ++i) amax = fmaxf(amax, fabsf(v[i]));
-  amax = quad_amax(amax);
-  float inv;
-  const uint32_t sc = block_scale<8>(amax, &inv);
-  uint32_t w[2] = {0u, 0u};
+    for (int i = 0; i < 8; ++i) amax = fmaxf(amax, fabsf(v[i]));
+    amax = quad_amax(amax);
+    float inv;
+    const uint32_t sc = block_scale<8>(amax, &inv);
+    uint32_t w[2] = {0u, 0u};
 #pragma unroll
-  for (int i = 0; i < 8; ++i) w[i >> 2] |= e4m3_code(v[i] * inv) << (8 * (i & 3));  // v * 2^-shared is exact
-  *reinterpret_cast<uint2*>(codes + (b * M_pad + m) * kBlock + 8 * g) = make_uint2(w[0], w[1]);
-  if (g == 0) scales[b * M_pad + m] = static_cast<uint8_t>(sc);
+    for (int i = 0; i < 8; ++i) w[i >> 2] |= e4m3_code(v[i] * inv) << (8 * (i & 3));  // v * 2^-shared is exact
+    *reinterpret_cast<uint2*>(codes + (b * M_pad + m) * kBlock + 8 * g) = make_uint2(w[0], w[1]);
+    if (g == 0) scales[b * M_pad + m] = static_cast<uint8_t>(sc);
+  }
 }
 
 // MXFP4 weights: one aligned quad per (column n, block b) of w [N][K].
@@ -448,9 +449,9 @@ size_t mx_scratch_bytes(int M, int K) {
 
 int launch_mx_quantize_act(const uint16_t* x, int M, int M_pad, int K, uint8_t* codes, uint8_t* scales,
                            hipStream_t stream) {
-  const int64_t threads = static_cast<int64_t>(M_pad) * (K / kBlock) * 4;
-  hipLaunchKernelGGL(mx_quantize_act_kernel, dim3(static_cast<unsigned>((threads + 255) / 256)), dim3(256), 0,
-                     stream, x, M, M_pad, K, codes, scales);
+  const int nb = K / kBlock;
+  const dim3 grid((4 * M_pad + 255) / 256, nb < 65535 ? nb : 65535);
+  hipLaunchKernelGGL(mx_quantize_act_kernel, grid, dim3(256), 0, stream, x, M, M_pad, K, codes, scales);
   W4A8_HIP(hipGetLastError());
   return W4A8_OK;
 }

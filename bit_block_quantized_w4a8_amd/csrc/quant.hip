@@ -90,29 +90,31 @@ int launch_quantize_export(const uint16_t* x, int M, int K, int8_t* qx, float* s
 // consecutive rows of the same block, so a wave writes whole runs of the
 // staging layout.  Group lane g holds elements 8g .. 8g+7, which belong at
 // byte 8 * (0, 2, 1, 3)[g] of the row's 32 codes: half (0, 1, 0, 1)[g],
-// offset (0, 0, 8, 8)[g].
+// offset (0, 0, 8, 8)[g].  The grid's x dimension covers the rows (four
+// lanes each) and its y dimension the blocks, so no lane divides by a
+// runtime size to find its (row, block).
 __global__ __launch_bounds__(256) void quantize_stage_kernel(const uint16_t* __restrict__ x, int M,
                                                              int M_pad, int K,
                                                              uint8_t* __restrict__ qxs,
                                                              float* __restrict__ sxs) {
-  const int64_t t = static_cast<int64_t>(blockIdx.x) * blockDim.x + threadIdx.x;
-  if (t >= static_cast<int64_t>(K / 8) * M_pad) return;
-  const int g = static_cast<int>(t & 3);
-  const int64_t q = t >> 2;
-  const int64_t m = q % M_pad;
-  const int64_t b = q / M_pad;
-  const int64_t e = 4 * b + g;  // 8-element group index within the row
-  float v[8] = {0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f};
-  if (m < M) unpack_half8(*reinterpret_cast<const uint4*>(x + m * K + 8 * e), v);
-  quantize_to_staging(v, m, e, M_pad, qxs, sxs);
+  const int tx = blockIdx.x * blockDim.x + threadIdx.x;
+  if (tx >= 4 * M_pad) return;  // whole quads (4 | 256)
+  const int g = tx & 3;
+  const int64_t m = tx >> 2;
+  const int nb = K / kBlock;
+  for (int b = blockIdx.y; b < nb; b += gridDim.y) {
+    const int64_t e = 4 * static_cast<int64_t>(b) + g;  // 8-element group index within the row
+    float v[8] = {0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f};
+    if (m < M) unpack_half8(*reinterpret_cast<const uint4*>(x + m * K + 8 * e), v);
+    quantize_to_staging(v, m, e, M_pad, qxs, sxs);
+  }
 }
 
 int launch_quantize_stage(const uint16_t* x, int M, int M_pad, int K, uint8_t* qxs, float* sxs,
                           hipStream_t stream) {
-  const int64_t total = static_cast<int64_t>(M_pad) * (K / 8);
-  const int64_t grid = (total + 255) / 256;
-  hipLaunchKernelGGL(quantize_stage_kernel, dim3(static_cast<unsigned>(grid)), dim3(256), 0, stream,
-                     x, M, M_pad, K, qxs, sxs);
+  const int nb = K / kBlock;
+  const dim3 grid((4 * M_pad + 255) / 256, nb < 65535 ? nb : 65535);
+  hipLaunchKernelGGL(quantize_stage_kernel, grid, dim3(256), 0, stream, x, M, M_pad, K, qxs, sxs);
   W4A8_HIP(hipGetLastError());
   return W4A8_OK;
 }
