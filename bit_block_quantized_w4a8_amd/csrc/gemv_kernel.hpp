@@ -41,13 +41,19 @@ constexpr int kMaxLoadsPerLane = 16;
 constexpr int kMaxChunkBlocks = 256;
 
 // Task g of a chunk (8 activations) -> row m and 8-element group e of the
-// chunk: m = g / (4 nbc), e = g % (4 nbc).  One-row kernels (MR = 1) only see
-// g < 4 nbc, so they skip the integer division (about 40 instructions ahead
-// of the first load).
+// chunk: m = g / (4 nbc), e = g % (4 nbc).  Tasks never reach row MR, so m is
+// counted with MR - 1 comparisons instead of an integer division by a runtime
+// size (about 40 instructions ahead of the first load); one-row kernels
+// (MR = 1) use g directly.
 template <int MR>
-__device__ __forceinline__ int task_row(int g, int nbc) { return MR == 1 ? 0 : g / (nbc * 4); }
+__device__ __forceinline__ int task_row(int g, int nbc) {
+  int m = 0;
+#pragma unroll
+  for (int i = 1; i < MR; ++i) m += g >= i * (nbc * 4) ? 1 : 0;
+  return m;
+}
 template <int MR>
-__device__ __forceinline__ int task_group(int g, int nbc) { return MR == 1 ? g : g % (nbc * 4); }
+__device__ __forceinline__ int task_group(int g, int nbc) { return g - task_row<MR>(g, nbc) * (nbc * 4); }
 
 // 16 bytes (8 fp16) of activations for quantisation task g of a chunk:
 // task g = (row m, block e / 4, quarter e % 4).
