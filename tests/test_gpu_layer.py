@@ -225,3 +225,27 @@ def test_graph_replay_matches_eager():
         assert int(host(am_fused)[0]) == eager_fused[i], f"replay {i}"
         scratch = w4.linear(dev(np.ones((2, h), np.float16)), head.packed, head.w_scales)  # eager work between
         host(scratch)
+
+
+def test_residual_add_more_rows_than_a_grid_dimension():
+    """The residual-only add walks rows with the grid's y stride: 70000 rows (more than the 65535
+    a grid dimension holds), bit for bit against the oracle."""
+    g = np.random.default_rng(11)
+    x = (g.standard_normal((70000, 64)) * 3).astype(np.float32)
+    d = (g.standard_normal((70000, 96)) * 50).astype(np.float32)
+    xd = dev(x)
+    w4.residual_norm_cast(xd, dev(d), alpha=SCALE, want_y=False)
+    assert np.array_equal(host(xd), oracle.residual_add(x, d[:, :64], SCALE))
+
+
+def test_decoder_layer_at_the_row_limit():
+    """65536 rows (the layer's limit) through the prefill GEMMs and the glue kernels that quantise
+    into GEMM staging, whose row loops cover more rows than one grid dimension holds."""
+    h, n_qkv, f, m = 64, 128, 64, 65536
+    host_w, dev_w = _weights(90, h, n_qkv, f)
+    x = (np.random.default_rng(3).standard_normal((m, h)) * 2).astype(np.float32)
+    assert w4.auto_path(m, h, 2 * f) == w4.PATH_GEMM
+    got = _run_layer(x, dev_w)
+    ref = oracle.decoder_layer(x, host_w, SCALE, EPS)
+    err = np.abs(got.astype(np.float64) - ref) - (1e-4 + 1e-4 * np.abs(ref))
+    assert err.max() <= 0, f"max excess {err.max():.3g}"
