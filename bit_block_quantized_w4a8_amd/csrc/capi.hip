@@ -393,9 +393,12 @@ int w4a8_decoder_layer(float* x, int64_t M, int64_t H, const w4a8_weights* qkv, 
                                  sg, stream));
     W4A8_STEP(gemm_staging(Mi, F, Hi, &sg));
     W4A8_STEP(launch_gated_quant(g, Mi, F, sg, stream));
-    W4A8_STEP(launch_gemm_staged(GemmArgs{nullptr, down->packed_w, down->w_scales, Mi, F, Hi, d, nullptr}, sg,
-                                 stream));
-    W4A8_STEP(launch_residual_norm_cast(x, d, H, residual_scale, eps, Mi, Hi, nullptr, stream));
+    // The down projection adds 0.01 * d straight into the residual stream in
+    // its epilogue (the same fma per element as a separate residual add).
+    GemmArgs da{nullptr, down->packed_w, down->w_scales, Mi, F, Hi, nullptr, nullptr};
+    da.resid = x;
+    da.alpha = residual_scale;
+    W4A8_STEP(launch_gemm_staged_resid(da, sg, stream));
     return W4A8_OK;
   }
   W4A8_STEP(launch_residual_norm_cast(x, nullptr, 0, 0.0f, eps, Mi, Hi, n, stream));

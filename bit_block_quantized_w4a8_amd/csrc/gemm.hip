@@ -113,12 +113,12 @@ __device__ __forceinline__ void chunk_source(int c, const uint8_t* pw, const uin
 }
 
 template <int TN, int TM, int WN, int WM, int WK, int MODE>
-__global__ __launch_bounds__(64 * WN * WM * WK) __attribute__((amdgpu_waves_per_eu(MODE == 0 && WK == 1 ? 4 : 1)))
+__global__ __launch_bounds__(64 * WN * WM * WK) __attribute__((amdgpu_waves_per_eu(MODE != 1 && WK == 1 ? 4 : 1)))
 void gemm_kernel(
     const uint8_t* __restrict__ pw, const uint16_t* __restrict__ ws, const uint8_t* __restrict__ qxs,
     const float* __restrict__ sxs, int M, int M_pad, int K, int N, int tiles_n, int tiles_m, int bps,
     float* __restrict__ out, int32_t* __restrict__ sums, float* __restrict__ partials,
-    uint32_t* __restrict__ tickets) {
+    uint32_t* __restrict__ tickets, float alpha) {
   constexpr int NW = WN * WM * WK;  // waves per workgroup
   static_assert(NW == 4 || NW == 8, "four or eight waves");
   static_assert(WK == 1 || (WK == 4 && WN * WM == 1), "K split only over four waves of one position");
@@ -133,7 +133,9 @@ void gemm_kernel(
   // into a full-rate v_fma_f32 but leaves each stage one step less time to
   // arrive.  The K-split tiles are short on latency hiding, so they keep the
   // fp16 scales and the three-step lead.
-  constexpr bool kWiden = MODE == 0 && WK == 1;
+  // MODE 0 writes the scaled output; MODE 2 adds alpha times it into `out`
+  // (the residual stream); MODE 1 exports the integer block sums.
+  constexpr bool kWiden = MODE != 1 && WK == 1;
   static_assert(!kWiden || BN == 128, "one wave widens the scales of a stage, two per lane");
   // Ring of four stages: blocks are fetched three steps ahead.
   __shared__ __attribute__((aligned(16))) uint8_t st0[St::kBytes];
@@ -433,9 +435,15 @@ void gemm_kernel(
 #pragma unroll
       for (int q = 0; q < 4; ++q) {
         const int n = n_base + 32 * i + 8 * q + 4 * h;
-        if (m < M && n < N)
-          *reinterpret_cast<float4*>(out + static_cast<int64_t>(m) * N + n) =
-              make_float4(acc[i][j][4 * q], acc[i][j][4 * q + 1], acc[i][j][4 * q + 2], acc[i][j][4 * q + 3]);
+        if (m < M && n < N) {
+          float4* dst = reinterpret_cast<float4*>(out + static_cast<int64_t>(m) * N + n);
+          float4 y = make_float4(acc[i][j][4 * q], acc[i][j][4 * q + 1], acc[i][j][4 * q + 2], acc[i][j][4 * q + 3]);
+          if (MODE == 2) {
+            const float4 r = *dst;
+            y = make_float4(fmaf(alpha, y.x, r.x), fmaf(alpha, y.y, r.y), fmaf(alpha, y.z, r.z), fmaf(alpha, y.w, r.w));
+          }
+          *dst = y;
+        }
       }
     }
 }
@@ -530,7 +538,7 @@ int launch_gemm_kernel(const GemmArgs& a, int mode, const GemmStaging& s, hipStr
 #define W4A8_GEMM_LAUNCH(TN, TM, WN, WM, WK, MODE)                                                     \
   hipLaunchKernelGGL((gemm_kernel<TN, TM, WN, WM, WK, MODE>), grid, dim3(64 * WN * WM * WK), 0,     \
                      stream, a.packed_w, ws, qxs, sxs, a.M, p.m_pad, a.K, a.N, p.tiles_n, p.tiles_m,       \
-                     p.bps, a.out, a.sums, partials, sc->tickets)
+                     p.bps, mode == 2 ? a.resid : a.out, a.sums, partials, sc->tickets, a.alpha)
 #define W4A8_GEMM_MODE(MODE)                                                                           \
   do {                                                                                                 \
     if (p.wk == 4) {                                                                                   \
@@ -544,6 +552,7 @@ int launch_gemm_kernel(const GemmArgs& a, int mode, const GemmStaging& s, hipStr
     }                                                                                                  \
   } while (0)
   if (mode == 1) W4A8_GEMM_MODE(1);
+  else if (mode == 2) W4A8_GEMM_MODE(2);
   else W4A8_GEMM_MODE(0);
 #undef W4A8_GEMM_MODE
 #undef W4A8_GEMM_LAUNCH
@@ -577,6 +586,10 @@ int launch_gemm(const GemmArgs& a, int mode, hipStream_t stream) {
 
 int launch_gemm_staged(const GemmArgs& a, const GemmStaging& s, hipStream_t stream) {
   return launch_gemm_kernel(a, 0, s, stream);
+}
+
+int launch_gemm_staged_resid(const GemmArgs& a, const GemmStaging& s, hipStream_t stream) {
+  return launch_gemm_kernel(a, 2, s, stream);
 }
 
 }  // namespace w4a8

@@ -56,6 +56,8 @@ struct GemmArgs {
   int M, K, N;
   float* out;            // mode 0
   int32_t* sums;         // mode 1
+  float* resid = nullptr;  // residual epilogue: resid[m][n] = fma(alpha, y[m][n], resid[m][n])
+  float alpha = 0.0f;
 };
 int launch_gemm(const GemmArgs& a, int mode, hipStream_t stream);
 size_t gemm_scratch_bytes(int M, int K, int N);
@@ -71,6 +73,9 @@ struct GemmStaging {
 int gemm_staging(int M, int K, int N, GemmStaging* s);
 // The GEMM (scaled output) on activations already quantised into `s`.
 int launch_gemm_staged(const GemmArgs& a, const GemmStaging& s, hipStream_t stream);
+// The same, adding alpha times the result into a.resid (fp32 [M][N]) instead
+// of writing a.out: one fma per element, as a separate residual add would.
+int launch_gemm_staged_resid(const GemmArgs& a, const GemmStaging& s, hipStream_t stream);
 
 // MX variant (mx.hip): MXFP4 weights x MXFP8 activations on the block-scaled
 // matrix instruction.
