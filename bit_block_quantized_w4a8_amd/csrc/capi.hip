@@ -389,16 +389,23 @@ int w4a8_decoder_layer(float* x, int64_t M, int64_t H, const w4a8_weights* qkv, 
     W4A8_STEP(launch_gemm_staged(GemmArgs{nullptr, o->packed_w, o->w_scales, Mi, Hi, Hi, ob, nullptr}, sg, stream));
     W4A8_STEP(gemm_staging(Mi, Hi, 2 * F, &sg));
     W4A8_STEP(launch_residual_norm_quant(x, ob, H, residual_scale, eps, Mi, Hi, sg, stream));
-    W4A8_STEP(launch_gemm_staged(GemmArgs{nullptr, gate_up->packed_w, gate_up->w_scales, Mi, Hi, 2 * F, g, nullptr},
-                                 sg, stream));
-    W4A8_STEP(gemm_staging(Mi, F, Hi, &sg));
-    W4A8_STEP(launch_gated_quant(g, Mi, F, sg, stream));
+    const GemmArgs gua{nullptr, gate_up->packed_w, gate_up->w_scales, Mi, Hi, 2 * F, g, nullptr};
+    GemmStaging sd = gemm_staging_at(g, Mi, F, Hi);
+    if (gemm_gated_supported(Mi, Hi, 2 * F, sd.m_pad)) {
+      // The gate/up GEMM forms fp16(gate * up) and quantises it into the down
+      // projection's staging (in the workspace, in place of g) itself.
+      W4A8_STEP(launch_gemm_staged_gated(gua, sg, sd, stream));
+    } else {
+      W4A8_STEP(launch_gemm_staged(gua, sg, stream));
+      W4A8_STEP(gemm_staging(Mi, F, Hi, &sd));
+      W4A8_STEP(launch_gated_quant(g, Mi, F, sd, stream));
+    }
     // The down projection adds 0.01 * d straight into the residual stream in
     // its epilogue (the same fma per element as a separate residual add).
     GemmArgs da{nullptr, down->packed_w, down->w_scales, Mi, F, Hi, nullptr, nullptr};
     da.resid = x;
     da.alpha = residual_scale;
-    W4A8_STEP(launch_gemm_staged_resid(da, sg, stream));
+    W4A8_STEP(launch_gemm_staged_resid(da, sd, stream));
     return W4A8_OK;
   }
   W4A8_STEP(launch_residual_norm_cast(x, nullptr, 0, 0.0f, eps, Mi, Hi, n, stream));

@@ -77,13 +77,9 @@ __device__ __forceinline__ float quad_max(float a) {
   return a;
 }
 
-__device__ __forceinline__ uint2 quantize8_group4(const float* x, float* sx_out) {
-  float a = 0.0f;
-#pragma unroll
-  for (int i = 0; i < 8; ++i) a = fmaxf(a, fabsf(x[i]));
-  a = quad_max(a);
-  const float sx = a / 127.0f;
-  *sx_out = sx;
+// The codes of eight elements of a block whose max-abs is `a` and whose scale
+// is sx = fp32(a / 127), by the method above.
+__device__ __forceinline__ uint2 quantize8_codes(const float* x, float a, float sx) {
   if (!(a > 0.0f)) return make_uint2(0u, 0u);
   const float r = __builtin_amdgcn_rcpf(sx);
   float q[8];
@@ -108,6 +104,16 @@ __device__ __forceinline__ uint2 quantize8_group4(const float* x, float* sx_out)
     packed[i >> 2] |= (static_cast<uint32_t>(static_cast<int>(c)) & 0xFFu) << (8 * (i & 3));
   }
   return make_uint2(packed[0], packed[1]);
+}
+
+__device__ __forceinline__ uint2 quantize8_group4(const float* x, float* sx_out) {
+  float a = 0.0f;
+#pragma unroll
+  for (int i = 0; i < 8; ++i) a = fmaxf(a, fabsf(x[i]));
+  a = quad_max(a);
+  const float sx = a / 127.0f;
+  *sx_out = sx;
+  return quantize8_codes(x, a, sx);
 }
 
 // Quantises group e (elements 8e .. 8e+7, held in v) of row m into the GEMM

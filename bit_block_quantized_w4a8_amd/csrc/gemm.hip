@@ -88,8 +88,10 @@ struct Stage {
 // Source of one lane's DMA chunk: global address of its bytes in K block 0
 // of the region, the region's stride per K block, and which of the step's
 // WK blocks it belongs to.  Columns are clamped into range, so every lane of
-// every DMA instruction reads valid memory.
-template <int BN, int BM, int WK, int NW>
+// every DMA instruction reads valid memory.  With GATED the tile's columns
+// are BN/2 gate columns and their partners N/2 further on (tile t covers
+// gate columns t*BN/2 .. t*BN/2 + BN/2 - 1).
+template <int BN, int BM, int WK, int NW, bool GATED>
 __device__ __forceinline__ void chunk_source(int c, const uint8_t* pw, const uint16_t* ws, const uint8_t* qxs,
                                              const float* sxs, int N, int M_pad, int n0, int m0,
                                              const uint8_t** base, uint32_t* stride, int* kk) {
@@ -97,11 +99,12 @@ __device__ __forceinline__ void chunk_source(int c, const uint8_t* pw, const uin
   c = min(c, St::kChunks - 1);  // padding lanes repeat the last chunk into the pad
   *kk = c / St::kBlockChunks;
   const int cc = c - *kk * St::kBlockChunks;
+  auto column = [&](int lc) { return !GATED ? n0 + lc : lc < BN / 2 ? n0 / 2 + lc : N / 2 + n0 / 2 + lc - BN / 2; };
   if (cc < BN) {
-    *base = pw + static_cast<int64_t>(min(n0 + cc, N - 1)) * kPackedBytes;
+    *base = pw + static_cast<int64_t>(min(column(cc), N - 1)) * kPackedBytes;
     *stride = static_cast<uint32_t>(N) * kPackedBytes;
   } else if (cc < BN + BN / 8) {
-    *base = reinterpret_cast<const uint8_t*>(ws + min(n0 + 8 * (cc - BN), N - 8));
+    *base = reinterpret_cast<const uint8_t*>(ws + min(column(8 * (cc - BN)), N - 8));
     *stride = static_cast<uint32_t>(N) * 2;
   } else if (cc < BN + BN / 8 + BM / 4) {
     *base = reinterpret_cast<const uint8_t*>(sxs + m0 + 4 * (cc - BN - BN / 8));
@@ -118,7 +121,8 @@ void gemm_kernel(
     const uint8_t* __restrict__ pw, const uint16_t* __restrict__ ws, const uint8_t* __restrict__ qxs,
     const float* __restrict__ sxs, int M, int M_pad, int K, int N, int tiles_n, int tiles_m, int bps,
     float* __restrict__ out, int32_t* __restrict__ sums, float* __restrict__ partials,
-    uint32_t* __restrict__ tickets, float alpha) {
+    uint32_t* __restrict__ tickets, float alpha, uint8_t* __restrict__ qout, float* __restrict__ sout,
+    int m_pad_out) {
   constexpr int NW = WN * WM * WK;  // waves per workgroup
   static_assert(NW == 4 || NW == 8, "four or eight waves");
   static_assert(WK == 1 || (WK == 4 && WN * WM == 1), "K split only over four waves of one position");
@@ -134,7 +138,11 @@ void gemm_kernel(
   // arrive.  The K-split tiles are short on latency hiding, so they keep the
   // fp16 scales and the three-step lead.
   // MODE 0 writes the scaled output; MODE 2 adds alpha times it into `out`
-  // (the residual stream); MODE 1 exports the integer block sums.
+  // (the residual stream); MODE 1 exports the integer block sums; MODE 3
+  // (gated) forms fp16(gate * up) of the tile's column pairs and quantises it
+  // into the staging of the next GEMM (qout, sout) instead of writing out.
+  constexpr bool kGated = MODE == 3;
+  static_assert(!kGated || (TN == 1 && WN == 4 && WK == 1), "gated tiles: four 32-column waves along n");
   constexpr bool kWiden = MODE != 1 && WK == 1;
   static_assert(!kWiden || BN == 128, "one wave widens the scales of a stage, two per lane");
   // Ring of four stages: blocks are fetched three steps ahead.
@@ -271,9 +279,9 @@ void gemm_kernel(
     uint32_t str0, str1, str2;
     int kk0, kk1, kk2;
     static_assert(kL <= 3, "three DMA instructions per wave and stage at most");
-    chunk_source<BN, BM, WK, NW>((wave + 0 * NW) * 64 + lane, pw, ws, qxs, sxs, N, M_pad, n0, m0, &src0, &str0, &kk0);
-    chunk_source<BN, BM, WK, NW>((wave + 1 * NW) * 64 + lane, pw, ws, qxs, sxs, N, M_pad, n0, m0, &src1, &str1, &kk1);
-    chunk_source<BN, BM, WK, NW>((wave + 2 * NW) * 64 + lane, pw, ws, qxs, sxs, N, M_pad, n0, m0, &src2, &str2, &kk2);
+    chunk_source<BN, BM, WK, NW, kGated>((wave + 0 * NW) * 64 + lane, pw, ws, qxs, sxs, N, M_pad, n0, m0, &src0, &str0, &kk0);
+    chunk_source<BN, BM, WK, NW, kGated>((wave + 1 * NW) * 64 + lane, pw, ws, qxs, sxs, N, M_pad, n0, m0, &src1, &str1, &kk1);
+    chunk_source<BN, BM, WK, NW, kGated>((wave + 2 * NW) * 64 + lane, pw, ws, qxs, sxs, N, M_pad, n0, m0, &src2, &str2, &kk2);
 
     // Stage `st` <- the WK blocks of step s (clamped to the last block, so
     // the steps past the end re-read it and every wave issues the same
@@ -348,6 +356,53 @@ void gemm_kernel(
   }
 
   if (MODE == 1) return;
+
+  if (kGated) {
+    // Waves wn = 2, 3 hold the partners of the gate columns of waves wn - 2.
+    // Each hands its accumulators to its gate wave through one LDS stage, one
+    // 32-row tile j at a time; the gate wave forms v = fp16(g * u) and
+    // quantises each row's 32 values (one block of the next GEMM's K: lane l
+    // holds 16 of them, lane l ^ 32 the other 16) exactly as the activation
+    // pre-pass does, into the staging layout.  Rows from M up to m_pad_out
+    // get zero codes and scales, as the pre-pass writes for padding rows.
+    const int pair = (wn & 1) + 2 * wm;
+    float* xch = reinterpret_cast<float*>(pair == 0 ? st0 : pair == 1 ? st1 : pair == 2 ? st2 : st3);
+    const int bo = (n0 >> 6) + wn;  // output block: gate columns 32 * bo .. 32 * bo + 31
+#pragma unroll
+    for (int j = 0; j < TM; ++j) {
+      __syncthreads();
+      if (wn >= 2) {
+#pragma unroll
+        for (int r = 0; r < 16; ++r) xch[r * 64 + lane] = acc[0][j][r];
+      }
+      __syncthreads();
+      if (wn < 2) {
+        const int m = m_base + 32 * j + l32;
+        float v[16];
+        float a = 0.0f;
+#pragma unroll
+        for (int r = 0; r < 16; ++r) {
+          v[r] = m < M ? half_bits_to_float(float_to_half_bits(acc[0][j][r] * xch[r * 64 + lane])) : 0.0f;
+          a = fmaxf(a, fabsf(v[r]));
+        }
+        a = fmaxf(a, __shfl_xor(a, 32));
+        const float sx = a / 127.0f;
+        const uint2 c0 = quantize8_codes(v, a, sx);
+        const uint2 c1 = quantize8_codes(v + 8, a, sx);
+        if (m < m_pad_out) {
+          // Elements 8q + 4h .. 8q + 4h + 3 of the block (registers 4q .. 4q + 3).
+          uint8_t* row = qout + static_cast<int64_t>(bo) * m_pad_out * kBlock + (m & 31) * 16 + 4 * h;
+          const int64_t s0 = static_cast<int64_t>((m >> 5) * 2) * 32 * 16;
+          *reinterpret_cast<uint32_t*>(row + s0) = c0.x;                 // q = 0: slot h' = 0, bytes 0..7
+          *reinterpret_cast<uint32_t*>(row + s0 + 32 * 16) = c0.y;       // q = 1: slot h' = 1
+          *reinterpret_cast<uint32_t*>(row + s0 + 8) = c1.x;             // q = 2: slot h' = 0, bytes 8..15
+          *reinterpret_cast<uint32_t*>(row + s0 + 32 * 16 + 8) = c1.y;   // q = 3: slot h' = 1
+          if (h == 0) sout[static_cast<int64_t>(bo) * m_pad_out + m] = sx;
+        }
+      }
+    }
+    return;
+  }
 
   // Waves wk > 0 hand their accumulators to wave wk = 0 of their (n, m)
   // position through LDS; that wave adds them in wk order.
@@ -502,6 +557,28 @@ size_t align256(size_t v) { return (v + 255) & ~static_cast<size_t>(255); }
 
 }  // namespace
 
+bool gemm_gated_supported(int M, int K, int N, int m_pad_out) {
+  const Plan p = plan_gemm(M, K, N);
+  return p.wm == 2 && p.wk == 1 && p.ksplit == 1 && N % 128 == 0 && m_pad_out >= M && m_pad_out <= p.m_pad &&
+         m_pad_out % 32 == 0;
+}
+
+size_t gemm_staging_bytes(int M, int K, int N) {
+  const Plan p = plan_gemm(M, K, N);
+  const size_t nb = K / kBlock;
+  return align256(nb * p.m_pad * kBlock) + align256(nb * p.m_pad * sizeof(float));
+}
+
+GemmStaging gemm_staging_at(void* base, int M, int K, int N) {
+  const Plan p = plan_gemm(M, K, N);
+  const size_t nb = K / kBlock;
+  GemmStaging s{};
+  s.qxs = static_cast<uint8_t*>(base);
+  s.sxs = reinterpret_cast<float*>(static_cast<uint8_t*>(base) + align256(nb * p.m_pad * kBlock));
+  s.m_pad = p.m_pad;
+  return s;
+}
+
 size_t gemm_scratch_bytes(int M, int K, int N) {
   const Plan p = plan_gemm(M, K, N);
   const size_t nb = K / kBlock;
@@ -512,10 +589,11 @@ size_t gemm_scratch_bytes(int M, int K, int N) {
 
 namespace {
 
-// Partial tiles of a split-K launch follow the staging in library scratch.
-float* gemm_partials(const GemmStaging& s, int K) {
+// Partial tiles of a split-K launch follow the room for a staging in library
+// scratch (whether or not the staging in use lies there).
+float* gemm_partials(void* work, const GemmStaging& s, int K) {
   const size_t nb = K / kBlock;
-  return reinterpret_cast<float*>(reinterpret_cast<uint8_t*>(s.qxs) + align256(nb * s.m_pad * kBlock) +
+  return reinterpret_cast<float*>(static_cast<uint8_t*>(work) + align256(nb * s.m_pad * kBlock) +
                                   align256(nb * s.m_pad * sizeof(float)));
 }
 
@@ -526,10 +604,9 @@ int launch_gemm_kernel(const GemmArgs& a, int mode, const GemmStaging& s, hipStr
   Scratch* sc = nullptr;
   int rc = scratch_for(gemm_scratch_bytes(a.M, a.K, a.N), &sc);
   if (rc != W4A8_OK) return rc;
-  if (s.qxs != sc->work) return hip_fail(hipErrorInvalidValue, "gemm: staging outside library scratch");
   const uint8_t* qxs = s.qxs;
   const float* sxs = s.sxs;
-  float* partials = gemm_partials(s, a.K);
+  float* partials = gemm_partials(sc->work, s, a.K);
   const dim3 grid(p.tiles_n * p.tiles_m, p.ksplit);
   // Every thread stages scale chunks unconditionally; the block-sum export has
   // no scales (w_scales may be null), so it stages bytes of the packed weights
@@ -538,7 +615,8 @@ int launch_gemm_kernel(const GemmArgs& a, int mode, const GemmStaging& s, hipStr
 #define W4A8_GEMM_LAUNCH(TN, TM, WN, WM, WK, MODE)                                                     \
   hipLaunchKernelGGL((gemm_kernel<TN, TM, WN, WM, WK, MODE>), grid, dim3(64 * WN * WM * WK), 0,     \
                      stream, a.packed_w, ws, qxs, sxs, a.M, p.m_pad, a.K, a.N, p.tiles_n, p.tiles_m,       \
-                     p.bps, mode == 2 ? a.resid : a.out, a.sums, partials, sc->tickets, a.alpha)
+                     p.bps, mode == 2 ? a.resid : a.out, a.sums, partials, sc->tickets, a.alpha, a.q_out,        \
+                     a.s_out, a.m_pad_out)
 #define W4A8_GEMM_MODE(MODE)                                                                           \
   do {                                                                                                 \
     if (p.wk == 4) {                                                                                   \
@@ -551,7 +629,11 @@ int launch_gemm_kernel(const GemmArgs& a, int mode, const GemmStaging& s, hipStr
       W4A8_GEMM_LAUNCH(1, 1, 4, 1, 1, MODE);                                                           \
     }                                                                                                  \
   } while (0)
-  if (mode == 1) W4A8_GEMM_MODE(1);
+  if (mode == 3) {
+    if (!gemm_gated_supported(a.M, a.K, a.N, a.m_pad_out) || !a.q_out || !a.s_out)
+      return hip_fail(hipErrorInvalidValue, "gemm: gated epilogue needs 128 x 128 tiles, N % 128 == 0 and a staging within the tile rows");
+    W4A8_GEMM_LAUNCH(1, 2, 4, 2, 1, 3);
+  } else if (mode == 1) W4A8_GEMM_MODE(1);
   else if (mode == 2) W4A8_GEMM_MODE(2);
   else W4A8_GEMM_MODE(0);
 #undef W4A8_GEMM_MODE
@@ -590,6 +672,14 @@ int launch_gemm_staged(const GemmArgs& a, const GemmStaging& s, hipStream_t stre
 
 int launch_gemm_staged_resid(const GemmArgs& a, const GemmStaging& s, hipStream_t stream) {
   return launch_gemm_kernel(a, 2, s, stream);
+}
+
+int launch_gemm_staged_gated(const GemmArgs& a, const GemmStaging& s, const GemmStaging& out, hipStream_t stream) {
+  GemmArgs g = a;
+  g.q_out = out.qxs;
+  g.s_out = out.sxs;
+  g.m_pad_out = out.m_pad;
+  return launch_gemm_kernel(g, 3, s, stream);
 }
 
 }  // namespace w4a8

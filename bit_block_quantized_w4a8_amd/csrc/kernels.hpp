@@ -58,6 +58,9 @@ struct GemmArgs {
   int32_t* sums;         // mode 1
   float* resid = nullptr;  // residual epilogue: resid[m][n] = fma(alpha, y[m][n], resid[m][n])
   float alpha = 0.0f;
+  uint8_t* q_out = nullptr;  // gated epilogue: staging of the next GEMM (codes, scales, rows)
+  float* s_out = nullptr;
+  int m_pad_out = 0;
 };
 int launch_gemm(const GemmArgs& a, int mode, hipStream_t stream);
 size_t gemm_scratch_bytes(int M, int K, int N);
@@ -76,6 +79,18 @@ int launch_gemm_staged(const GemmArgs& a, const GemmStaging& s, hipStream_t stre
 // The same, adding alpha times the result into a.resid (fp32 [M][N]) instead
 // of writing a.out: one fma per element, as a separate residual add would.
 int launch_gemm_staged_resid(const GemmArgs& a, const GemmStaging& s, hipStream_t stream);
+// Staging in caller memory (gemm_staging_bytes(M, K, N) bytes, 256-byte
+// aligned) for a GEMM of that shape.
+size_t gemm_staging_bytes(int M, int K, int N);
+GemmStaging gemm_staging_at(void* base, int M, int K, int N);
+// A gate/up GEMM (columns [gate F | up F], N = 2F) whose epilogue forms
+// fp16(gate * up) and quantises it into `out`, the staging of a GEMM with
+// K = F, instead of writing a.out; the codes and scales equal those that the
+// gated glue kernel and the activation pre-pass write.  Only for shapes that
+// run 128 x 128 tiles without a K split, and a staging of at most as many
+// rows as the tiles cover.
+bool gemm_gated_supported(int M, int K, int N, int m_pad_out);
+int launch_gemm_staged_gated(const GemmArgs& a, const GemmStaging& s, const GemmStaging& out, hipStream_t stream);
 
 // MX variant (mx.hip): MXFP4 weights x MXFP8 activations on the block-scaled
 // matrix instruction.

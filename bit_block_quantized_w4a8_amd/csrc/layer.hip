@@ -299,7 +299,11 @@ LayerWorkspace layer_workspace(int M, int H, int n_qkv, int n_gu) {
   w.a = take(static_cast<size_t>(M) * H * 2);
   w.o = take(static_cast<size_t>(M) * H * 4);
   w.n = take(static_cast<size_t>(M) * H * 2);
-  w.g = take(static_cast<size_t>(M) * n_gu * 4);
+  // g: the gate/up output, or (when the gate/up GEMM quantises its gated
+  // product itself) the staging of the down projection.
+  const size_t g_bytes = static_cast<size_t>(M) * n_gu * 4;
+  const size_t sd_bytes = gemm_staging_bytes(M, n_gu / 2, H);
+  w.g = take(g_bytes > sd_bytes ? g_bytes : sd_bytes);
   w.u = take(static_cast<size_t>(M) * (n_gu / 2) * 2);
   w.d = take(static_cast<size_t>(M) * H * 4);
   w.bytes = off;

@@ -84,6 +84,26 @@ def test_decoder_layer_small(m):
     assert not np.array_equal(got, x)
 
 
+@pytest.mark.parametrize("m", [200, 256])
+def test_decoder_layer_gated_gemm_epilogue(m):
+    """A gate/up GEMM wide enough for 128 x 128 tiles (2F = 32768) quantises fp16(gate * up)
+    into the down projection's staging in its epilogue. At 200 rows the down projection's
+    staging covers 224 rows (zero codes past row 200) against the gate/up tiles' 256, and the
+    down projection splits K across workgroups with its staging outside library scratch."""
+    h, n_qkv, f = 128, 192, 16384
+    host_w, dev_w = _weights(21, h, n_qkv, f)
+    x = (np.random.default_rng(m + 5).standard_normal((m, h)) * 2).astype(np.float32)
+    assert w4.auto_path(m, h, 2 * f) == w4.PATH_GEMM and w4.auto_path(m, f, h) == w4.PATH_GEMM
+    got = _run_layer(x, dev_w)
+    ref = oracle.decoder_layer(x, host_w, SCALE, EPS)
+    # 16384-wide intermediates: a one-ulp fp16 difference in a normalised input can move an
+    # int8 code by one, so the output tolerance itself applies (1e-3 abs + 1e-3 rel).
+    err = np.abs(got.astype(np.float64) - ref) - (1e-3 + 1e-3 * np.abs(ref))
+    assert err.max() <= 0, f"max excess {err.max():.3g}"
+    assert np.median(np.abs(got - ref)) < 1e-4
+    assert not np.array_equal(got, x)
+
+
 def test_decoder_layer_full_decode_shape():
     """One layer at the end-to-end shapes (hidden 2048), M = 1."""
     h = 2048
