@@ -382,13 +382,25 @@ int w4a8_decoder_layer(float* x, int64_t M, int64_t H, const w4a8_weights* qkv, 
     GemmStaging sg{};
     W4A8_STEP(gemm_staging(Mi, Hi, Nq, &sg));
     W4A8_STEP(launch_residual_norm_quant(x, nullptr, 0, 0.0f, eps, Mi, Hi, sg, stream));
-    W4A8_STEP(launch_gemm_staged(GemmArgs{nullptr, qkv->packed_w, qkv->w_scales, Mi, Hi, Nq, q, nullptr}, sg,
-                                 stream));
-    W4A8_STEP(gemm_staging(Mi, Hi, Hi, &sg));
-    W4A8_STEP(launch_cast_quant(q, qkv->N, Mi, Hi, sg, stream));
-    W4A8_STEP(launch_gemm_staged(GemmArgs{nullptr, o->packed_w, o->w_scales, Mi, Hi, Hi, ob, nullptr}, sg, stream));
+    const GemmArgs qa{nullptr, qkv->packed_w, qkv->w_scales, Mi, Hi, Nq, q, nullptr};
+    GemmStaging so = gemm_staging_at(a, Mi, Hi, Hi);
+    if (gemm_cast_supported(Mi, Hi, Nq, Hi, so.m_pad)) {
+      // The qkv GEMM quantises fp16 of its query slice into the o
+      // projection's staging (in the workspace, in place of a) itself.
+      W4A8_STEP(launch_gemm_staged_cast(qa, Hi, sg, so, stream));
+    } else {
+      W4A8_STEP(launch_gemm_staged(qa, sg, stream));
+      W4A8_STEP(gemm_staging(Mi, Hi, Hi, &so));
+      W4A8_STEP(launch_cast_quant(q, qkv->N, Mi, Hi, so, stream));
+    }
+    // The o projection adds 0.01 * o into the residual stream in its
+    // epilogue; the normalisation then reads x alone.
+    GemmArgs oa{nullptr, o->packed_w, o->w_scales, Mi, Hi, Hi, nullptr, nullptr};
+    oa.resid = x;
+    oa.alpha = residual_scale;
+    W4A8_STEP(launch_gemm_staged_resid(oa, so, stream));
     W4A8_STEP(gemm_staging(Mi, Hi, 2 * F, &sg));
-    W4A8_STEP(launch_residual_norm_quant(x, ob, H, residual_scale, eps, Mi, Hi, sg, stream));
+    W4A8_STEP(launch_residual_norm_quant(x, nullptr, 0, 0.0f, eps, Mi, Hi, sg, stream));
     const GemmArgs gua{nullptr, gate_up->packed_w, gate_up->w_scales, Mi, Hi, 2 * F, g, nullptr};
     GemmStaging sd = gemm_staging_at(g, Mi, F, Hi);
     if (gemm_gated_supported(Mi, Hi, 2 * F, sd.m_pad)) {

@@ -115,6 +115,33 @@ __device__ __forceinline__ void chunk_source(int c, const uint8_t* pw, const uin
   }
 }
 
+// One activation block of the next GEMM from a 32 x 32 result tile: lane l
+// holds row m's values at block positions 8q + 4h + i in v[4q + i] (h = l / 32)
+// and lane l ^ 32 the other 16.  Quantised as the activation pre-pass does
+// (same max-abs, scale and code routine) into the staging layout: codes of
+// block bo at qout + bo * m_pad_out * 32, 16-byte slot ((m / 32) * 2 + q % 2)
+// * 32 + m % 32, byte 8 * (q / 2) + 4h; scale at sout[bo * m_pad_out + m].
+// Rows at or past m_pad_out are not stored.  Every lane of the wave calls it.
+__device__ __forceinline__ void quantize_pair_to_staging(const float* v, int m, int h, int bo, int m_pad_out,
+                                                         uint8_t* __restrict__ qout, float* __restrict__ sout) {
+  float a = 0.0f;
+#pragma unroll
+  for (int r = 0; r < 16; ++r) a = fmaxf(a, fabsf(v[r]));
+  a = fmaxf(a, __shfl_xor(a, 32));
+  const float sx = a / 127.0f;
+  const uint2 c0 = quantize8_codes(v, a, sx);
+  const uint2 c1 = quantize8_codes(v + 8, a, sx);
+  if (m < m_pad_out) {
+    uint8_t* row = qout + static_cast<int64_t>(bo) * m_pad_out * kBlock + (m & 31) * 16 + 4 * h;
+    const int64_t s0 = static_cast<int64_t>((m >> 5) * 2) * 32 * 16;
+    *reinterpret_cast<uint32_t*>(row + s0) = c0.x;                // q = 0
+    *reinterpret_cast<uint32_t*>(row + s0 + 32 * 16) = c0.y;      // q = 1
+    *reinterpret_cast<uint32_t*>(row + s0 + 8) = c1.x;            // q = 2
+    *reinterpret_cast<uint32_t*>(row + s0 + 32 * 16 + 8) = c1.y;  // q = 3
+    if (h == 0) sout[static_cast<int64_t>(bo) * m_pad_out + m] = sx;
+  }
+}
+
 template <int TN, int TM, int WN, int WM, int WK, int MODE>
 __global__ __launch_bounds__(64 * WN * WM * WK) __attribute__((amdgpu_waves_per_eu(MODE != 1 && WK == 1 ? 4 : 1)))
 void gemm_kernel(
@@ -122,7 +149,7 @@ void gemm_kernel(
     const float* __restrict__ sxs, int M, int M_pad, int K, int N, int tiles_n, int tiles_m, int bps,
     float* __restrict__ out, int32_t* __restrict__ sums, float* __restrict__ partials,
     uint32_t* __restrict__ tickets, float alpha, uint8_t* __restrict__ qout, float* __restrict__ sout,
-    int m_pad_out) {
+    int m_pad_out, int n_cast) {
   constexpr int NW = WN * WM * WK;  // waves per workgroup
   static_assert(NW == 4 || NW == 8, "four or eight waves");
   static_assert(WK == 1 || (WK == 4 && WN * WM == 1), "K split only over four waves of one position");
@@ -140,7 +167,9 @@ void gemm_kernel(
   // MODE 0 writes the scaled output; MODE 2 adds alpha times it into `out`
   // (the residual stream); MODE 1 exports the integer block sums; MODE 3
   // (gated) forms fp16(gate * up) of the tile's column pairs and quantises it
-  // into the staging of the next GEMM (qout, sout) instead of writing out.
+  // into the staging of the next GEMM (qout, sout) instead of writing out;
+  // MODE 4 does the same with fp16(y) of the leading n_cast columns and
+  // writes the others out as MODE 0.
   constexpr bool kGated = MODE == 3;
   static_assert(!kGated || (TN == 1 && WN == 4 && WK == 1), "gated tiles: four 32-column waves along n");
   constexpr bool kWiden = MODE != 1 && WK == 1;
@@ -379,26 +408,10 @@ void gemm_kernel(
       if (wn < 2) {
         const int m = m_base + 32 * j + l32;
         float v[16];
-        float a = 0.0f;
 #pragma unroll
-        for (int r = 0; r < 16; ++r) {
+        for (int r = 0; r < 16; ++r)
           v[r] = m < M ? half_bits_to_float(float_to_half_bits(acc[0][j][r] * xch[r * 64 + lane])) : 0.0f;
-          a = fmaxf(a, fabsf(v[r]));
-        }
-        a = fmaxf(a, __shfl_xor(a, 32));
-        const float sx = a / 127.0f;
-        const uint2 c0 = quantize8_codes(v, a, sx);
-        const uint2 c1 = quantize8_codes(v + 8, a, sx);
-        if (m < m_pad_out) {
-          // Elements 8q + 4h .. 8q + 4h + 3 of the block (registers 4q .. 4q + 3).
-          uint8_t* row = qout + static_cast<int64_t>(bo) * m_pad_out * kBlock + (m & 31) * 16 + 4 * h;
-          const int64_t s0 = static_cast<int64_t>((m >> 5) * 2) * 32 * 16;
-          *reinterpret_cast<uint32_t*>(row + s0) = c0.x;                 // q = 0: slot h' = 0, bytes 0..7
-          *reinterpret_cast<uint32_t*>(row + s0 + 32 * 16) = c0.y;       // q = 1: slot h' = 1
-          *reinterpret_cast<uint32_t*>(row + s0 + 8) = c1.x;             // q = 2: slot h' = 0, bytes 8..15
-          *reinterpret_cast<uint32_t*>(row + s0 + 32 * 16 + 8) = c1.y;   // q = 3: slot h' = 1
-          if (h == 0) sout[static_cast<int64_t>(bo) * m_pad_out + m] = sx;
-        }
+        quantize_pair_to_staging(v, m, h, bo, m_pad_out, qout, sout);
       }
     }
     return;
@@ -487,6 +500,15 @@ void gemm_kernel(
 #pragma unroll
     for (int j = 0; j < TM; ++j) {
       const int m = m_base + 32 * j + l32;
+      if (MODE == 4 && n_base + 32 * i < n_cast) {
+        // A block of the leading n_cast columns: fp16(y) quantised into the
+        // next GEMM's staging instead of written out.
+        float v[16];
+#pragma unroll
+        for (int r = 0; r < 16; ++r) v[r] = m < M ? half_bits_to_float(float_to_half_bits(acc[i][j][r])) : 0.0f;
+        quantize_pair_to_staging(v, m, h, (n_base + 32 * i) >> 5, m_pad_out, qout, sout);
+        continue;
+      }
 #pragma unroll
       for (int q = 0; q < 4; ++q) {
         const int n = n_base + 32 * i + 8 * q + 4 * h;
@@ -563,6 +585,12 @@ bool gemm_gated_supported(int M, int K, int N, int m_pad_out) {
          m_pad_out % 32 == 0;
 }
 
+bool gemm_cast_supported(int M, int K, int N, int n_cast, int m_pad_out) {
+  const Plan p = plan_gemm(M, K, N);
+  return n_cast >= 32 && n_cast % 32 == 0 && n_cast <= N && m_pad_out >= M && m_pad_out <= p.m_pad &&
+         m_pad_out % 32 == 0;
+}
+
 size_t gemm_staging_bytes(int M, int K, int N) {
   const Plan p = plan_gemm(M, K, N);
   const size_t nb = K / kBlock;
@@ -616,7 +644,7 @@ int launch_gemm_kernel(const GemmArgs& a, int mode, const GemmStaging& s, hipStr
   hipLaunchKernelGGL((gemm_kernel<TN, TM, WN, WM, WK, MODE>), grid, dim3(64 * WN * WM * WK), 0,     \
                      stream, a.packed_w, ws, qxs, sxs, a.M, p.m_pad, a.K, a.N, p.tiles_n, p.tiles_m,       \
                      p.bps, mode == 2 ? a.resid : a.out, a.sums, partials, sc->tickets, a.alpha, a.q_out,        \
-                     a.s_out, a.m_pad_out)
+                     a.s_out, a.m_pad_out, a.n_cast)
 #define W4A8_GEMM_MODE(MODE)                                                                           \
   do {                                                                                                 \
     if (p.wk == 4) {                                                                                   \
@@ -633,6 +661,10 @@ int launch_gemm_kernel(const GemmArgs& a, int mode, const GemmStaging& s, hipStr
     if (!gemm_gated_supported(a.M, a.K, a.N, a.m_pad_out) || !a.q_out || !a.s_out)
       return hip_fail(hipErrorInvalidValue, "gemm: gated epilogue needs 128 x 128 tiles, N % 128 == 0 and a staging within the tile rows");
     W4A8_GEMM_LAUNCH(1, 2, 4, 2, 1, 3);
+  } else if (mode == 4) {
+    if (!gemm_cast_supported(a.M, a.K, a.N, a.n_cast, a.m_pad_out) || !a.q_out || !a.s_out)
+      return hip_fail(hipErrorInvalidValue, "gemm: cast epilogue needs whole blocks and a staging within the tile rows");
+    W4A8_GEMM_MODE(4);
   } else if (mode == 1) W4A8_GEMM_MODE(1);
   else if (mode == 2) W4A8_GEMM_MODE(2);
   else W4A8_GEMM_MODE(0);
@@ -672,6 +704,16 @@ int launch_gemm_staged(const GemmArgs& a, const GemmStaging& s, hipStream_t stre
 
 int launch_gemm_staged_resid(const GemmArgs& a, const GemmStaging& s, hipStream_t stream) {
   return launch_gemm_kernel(a, 2, s, stream);
+}
+
+int launch_gemm_staged_cast(const GemmArgs& a, int n_cast, const GemmStaging& s, const GemmStaging& out,
+                            hipStream_t stream) {
+  GemmArgs g = a;
+  g.q_out = out.qxs;
+  g.s_out = out.sxs;
+  g.m_pad_out = out.m_pad;
+  g.n_cast = n_cast;
+  return launch_gemm_kernel(g, 4, s, stream);
 }
 
 int launch_gemm_staged_gated(const GemmArgs& a, const GemmStaging& s, const GemmStaging& out, hipStream_t stream) {

@@ -61,6 +61,7 @@ struct GemmArgs {
   uint8_t* q_out = nullptr;  // gated epilogue: staging of the next GEMM (codes, scales, rows)
   float* s_out = nullptr;
   int m_pad_out = 0;
+  int n_cast = 0;  // cast epilogue: leading columns quantised into the staging
 };
 int launch_gemm(const GemmArgs& a, int mode, hipStream_t stream);
 size_t gemm_scratch_bytes(int M, int K, int N);
@@ -90,6 +91,14 @@ GemmStaging gemm_staging_at(void* base, int M, int K, int N);
 // run 128 x 128 tiles without a K split, and a staging of at most as many
 // rows as the tiles cover.
 bool gemm_gated_supported(int M, int K, int N, int m_pad_out);
+// A GEMM whose epilogue quantises fp16(y) of its leading n_cast columns
+// (a multiple of 32) into `out`, the staging of a GEMM with K = n_cast, and
+// writes the other columns to a.out; the codes and scales equal those that
+// the cast glue kernel writes.  `out` holds at least M and at most the
+// GEMM's tile rows (its m_pad).
+bool gemm_cast_supported(int M, int K, int N, int n_cast, int m_pad_out);
+int launch_gemm_staged_cast(const GemmArgs& a, int n_cast, const GemmStaging& s, const GemmStaging& out,
+                            hipStream_t stream);
 int launch_gemm_staged_gated(const GemmArgs& a, const GemmStaging& s, const GemmStaging& out, hipStream_t stream);
 
 // MX variant (mx.hip): MXFP4 weights x MXFP8 activations on the block-scaled

@@ -296,7 +296,11 @@ LayerWorkspace layer_workspace(int M, int H, int n_qkv, int n_gu) {
     return at;
   };
   w.q = take(static_cast<size_t>(M) * n_qkv * 4);
-  w.a = take(static_cast<size_t>(M) * H * 2);
+  // a: the fp16 query slice, or (when the qkv GEMM quantises it itself) the
+  // staging of the o projection.
+  const size_t a_bytes = static_cast<size_t>(M) * H * 2;
+  const size_t so_bytes = gemm_staging_bytes(M, H, H);
+  w.a = take(a_bytes > so_bytes ? a_bytes : so_bytes);
   w.o = take(static_cast<size_t>(M) * H * 4);
   w.n = take(static_cast<size_t>(M) * H * 2);
   // g: the gate/up output, or (when the gate/up GEMM quantises its gated
