@@ -88,6 +88,8 @@ def parse():
     ap.add_argument("--decode-steps", type=int, default=128)
     ap.add_argument("--profile-gemv", action="store_true",
                     help="only run the gate_up GEMV (cold weights) and a 256 MiB copy, for counter runs")
+    ap.add_argument("--profile-gemm", action="store_true",
+                    help="only run the prefill gate_up projection (M = 512) a few times, for counter runs")
     ap.add_argument("--summarize-traffic", nargs=2, metavar=("FETCH_CSV", "WRITE_CSV"),
                     help="turn two rocprofv3 --pmc counter_collection.csv files into " + TRAFFIC_FILE)
     ap.add_argument("--cpu-seconds", type=float, default=10.0, help="CPU oracle sample budget")
@@ -507,6 +509,19 @@ def profile_gemv(w4, torch, synth, launches=40):
     print(json.dumps({"profile_gemv": launches, "copies": 3, "copy_bytes": COPY_BYTES}), flush=True)
 
 
+def profile_gemm(w4, torch, synth, launches=6):
+    """Launches of the prefill gate_up projection (M = 512, pre-pass + GEMM) for counter runs."""
+    x, qw, sw = synth.workload_inputs("prefill")["gate_up"]
+    dev = torch.device("cuda:0")
+    packed, ws = w4.pack_weights(torch.from_numpy(qw).to(dev), torch.from_numpy(sw).to(dev))
+    xd = torch.from_numpy(x).to(dev)
+    out = torch.empty((x.shape[0], qw.shape[0]), dtype=torch.float32, device=dev)
+    for _ in range(launches):
+        w4.linear(xd, packed, ws, out=out)
+    torch.cuda.synchronize()
+    print(json.dumps({"profile_gemm": launches, "M": x.shape[0], "K": qw.shape[1], "N": qw.shape[0]}), flush=True)
+
+
 def summarize_traffic(fetch_csv, write_csv):
     """Median KiB per dispatch of FETCH_SIZE / WRITE_SIZE for the GEMV, scaled by the copy's."""
     import csv
@@ -593,6 +608,9 @@ def main():
     w4.init(0)
     if args.profile_gemv:
         profile_gemv(w4, torch, synth)
+        return
+    if args.profile_gemm:
+        profile_gemm(w4, torch, synth)
         return
     timer = Timer(torch)
     monitor = DeviceMonitor().start()
