@@ -175,6 +175,15 @@ W4A8_API int w4a8_decoder_layer_workspace(int64_t M, int64_t H, const w4a8_weigh
  * operators: sciencestack summary of the ML Drift paper, Figure 4).  The
  * result equals the nine-launch chain up to the summation order inside
  * rms(x); q is still written to the workspace.
+ * When every projection runs the prefill GEMM, the layer is six launches: the
+ * two normalisations quantise straight into GEMM staging; the qkv GEMM
+ * quantises fp16(q[:, :H]) into the o projection's staging (its other columns
+ * are written to the workspace); the o and down GEMMs add 0.01 times their
+ * result into x in their epilogues; and, where the gate/up GEMM runs 128 x 128
+ * tiles without a K split, it quantises fp16(gate * up) into the down
+ * projection's staging (otherwise g is written and a glue kernel quantises
+ * it).  Those stagings live in the workspace.  The codes, scales and sums
+ * equal those of the nine-launch chain bit for bit.
  */
 W4A8_API int w4a8_decoder_layer(float* x, int64_t M, int64_t H, const w4a8_weights* qkv,
                                 const w4a8_weights* o, const w4a8_weights* gate_up,
