@@ -182,8 +182,9 @@ W4A8_API int w4a8_decoder_layer_workspace(int64_t M, int64_t H, const w4a8_weigh
  * result into x in their epilogues; and, where the gate/up GEMM runs 128 x 128
  * tiles without a K split, it quantises fp16(gate * up) into the down
  * projection's staging (otherwise g is written and a glue kernel quantises
- * it).  Those stagings live in the workspace.  The codes, scales and sums
- * equal those of the nine-launch chain bit for bit.
+ * it).  Those stagings live in the workspace.  Each fused epilogue forms
+ * the same fp16 values as the glue kernel it replaces and quantises them with
+ * the same routine, so its codes and scales are those the glue kernel wrote.
  */
 W4A8_API int w4a8_decoder_layer(float* x, int64_t M, int64_t H, const w4a8_weights* qkv,
                                 const w4a8_weights* o, const w4a8_weights* gate_up,
