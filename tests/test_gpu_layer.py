@@ -104,6 +104,22 @@ def test_decoder_layer_gated_gemm_epilogue(m):
     assert not np.array_equal(got, x)
 
 
+def test_decoder_layer_fused_epilogues_on_narrow_wide_grids():
+    """22000 rows at hidden 192: the qkv GEMM (384 columns) runs 128 x 128 tiles, one of which
+    quantises its first 64 columns (the end of the query slice) and writes the other 64; the
+    gate/up GEMM (2F = 384) runs three 128-column tiles of 64 gate and 64 up columns each; the
+    last 16 rows of every staging are padding."""
+    h, n_qkv, f, m = 192, 384, 192, 22000
+    host_w, dev_w = _weights(33, h, n_qkv, f)
+    x = (np.random.default_rng(17).standard_normal((m, h)) * 2).astype(np.float32)
+    got = _run_layer(x, dev_w)
+    ref = oracle.decoder_layer(x, host_w, SCALE, EPS)
+    err = np.abs(got.astype(np.float64) - ref) - (1e-3 + 1e-3 * np.abs(ref))
+    assert err.max() <= 0, f"max excess {err.max():.3g}"
+    assert np.median(np.abs(got - ref)) < 1e-4
+    assert not np.array_equal(got, x)
+
+
 def test_decoder_layer_full_decode_shape():
     """One layer at the end-to-end shapes (hidden 2048), M = 1."""
     h = 2048
