@@ -47,8 +47,8 @@ constexpr int kRows = 16;           // matrix rows: hi parts of 8 heads, then lo
 constexpr int kMaxGroup = 8;        // query heads per KV head
 constexpr float kLo = 4096.0f;      // lo parts are stored times 2^12
 constexpr float kInvLo = 1.0f / 4096.0f;
-constexpr int kMaxGroups = 8;       // merge groups per KV head
-constexpr int kGroupChunks = 64;    // chunks per merge group, at least
+constexpr int kMaxGroups = 32;      // merge groups per KV head
+constexpr int kGroupChunks = 16;    // chunks per merge group, at least
 constexpr int kMergeUnroll = 8;     // partials fetched per merge round
 
 typedef _Float16 h4 __attribute__((ext_vector_type(4)));

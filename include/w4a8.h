@@ -284,7 +284,7 @@ W4A8_API int w4a8_mx_linear(const uint16_t* x, const uint8_t* packed, const uint
  * of n_kv_heads, at most 8 times it; capacity a multiple of 64 in [64, 2^24];
  * 1 <= length <= capacity; every pointer 16-byte aligned; |q|, |k_new|, |v_new|
  * within fp16 range.  Uses library scratch (about n_kv_heads * (length / 64 +
- * 8) * n_heads / n_kv_heads * (head_dim + 2) * 4 bytes).  Errors: W4A8_EINVAL for
+ * 32) * n_heads / n_kv_heads * (head_dim + 2) * 4 bytes).  Errors: W4A8_EINVAL for
  * arguments outside these limits, W4A8_ENOINIT, W4A8_EHIP.
  */
 W4A8_API int w4a8_decode_attention(const float* q, const float* k_new, const float* v_new,
