@@ -65,9 +65,10 @@ struct AttnArgs {
   float* stats;          // [Hkv][chunks][G][2]: chunk max (base-2 units), weight sum
   float* part2;          // [Hkv][kMaxGroups][G][D] unnormalised merge-group outputs
   float* stats2;         // [Hkv][kMaxGroups][G][2]
-  uint32_t* tickets;     // [Hkv][kMaxGroups + 1], zero between launches
+  uint32_t* tickets;     // [Hkv][max_groups + 1], zero between launches
   int group, length, capacity;
   int group_chunks;      // chunks per merge group
+  int max_groups;        // merge groups per KV head at most (<= kMaxGroups): the ticket stride
   float scale2;          // log2(e) / sqrt(D)
 };
 
@@ -316,7 +317,7 @@ __global__ __launch_bounds__(kThreads) void decode_attention_kernel(AttnArgs a) 
   const int ngroups = (chunks + gsz - 1) / gsz;
   const int grp = c / gsz;
   const int cb = grp * gsz, ce = min(chunks, cb + gsz);
-  uint32_t* tix = a.tickets + g * (kMaxGroups + 1);
+  uint32_t* tix = a.tickets + g * (a.max_groups + 1);
   __builtin_amdgcn_s_waitcnt(0);
   __syncthreads();
   if (tid == 0)
@@ -344,11 +345,11 @@ __global__ __launch_bounds__(kThreads) void decode_attention_kernel(AttnArgs a) 
     __builtin_amdgcn_s_waitcnt(0);
     __syncthreads();
     if (tid == 0)
-      last = __hip_atomic_fetch_add(&tix[kMaxGroups], 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) ==
+      last = __hip_atomic_fetch_add(&tix[a.max_groups], 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) ==
              static_cast<uint32_t>(ngroups - 1);
     __syncthreads();
     if (!last) return;
-    if (tid == 0) __hip_atomic_store(&tix[kMaxGroups], 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    if (tid == 0) __hip_atomic_store(&tix[a.max_groups], 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
   }
   for (int it = tid; it < G * (D / 8); it += kThreads) {
     const int h = it / (D / 8), d0 = (it % (D / 8)) * 8;
@@ -376,7 +377,7 @@ int launch_decode_attention(const float* q, const float* k_new, const float* v_n
                             uint16_t* v_cache, int n_heads, int n_kv_heads, int head_dim, int length, int capacity,
                             uint16_t* out, Scratch* sc, hipStream_t stream) {
   if (n_heads % n_kv_heads != 0 || n_heads / n_kv_heads > kMaxGroup || capacity % kChunk != 0 ||
-      length < 1 || length > capacity || n_kv_heads * (kMaxGroups + 1) >= kMaxTickets - 1 ||
+      length < 1 || length > capacity || n_kv_heads < 1 || n_kv_heads >= (kMaxTickets - 2) / 2 ||
       attention_scratch_bytes(n_kv_heads, n_heads / n_kv_heads, head_dim, length) > sc->work_bytes)
     return hip_fail(hipErrorInvalidValue, "decode attention: shape outside the kernel's limits");
   const int chunks = attention_chunks(length);
@@ -392,8 +393,11 @@ int launch_decode_attention(const float* q, const float* k_new, const float* v_n
   a.stats = a.part + static_cast<size_t>(n_kv_heads) * chunks * group * head_dim;
   a.part2 = a.stats + static_cast<size_t>(n_kv_heads) * chunks * group * 2;
   a.stats2 = a.part2 + static_cast<size_t>(n_kv_heads) * kMaxGroups * group * head_dim;
+  // The tickets (one per merge group and one for the group results, per KV
+  // head) must fit the library's ticket array: many KV heads get fewer groups.
+  a.max_groups = std::min(kMaxGroups, (kMaxTickets - 2) / n_kv_heads - 1);
   a.tickets = sc->tickets + 1;
-  a.group_chunks = std::max(kGroupChunks, (chunks + kMaxGroups - 1) / kMaxGroups);
+  a.group_chunks = std::max(kGroupChunks, (chunks + a.max_groups - 1) / a.max_groups);
   a.group = group;
   a.length = length;
   a.capacity = capacity;

@@ -87,8 +87,10 @@ CASES = [
     (8, 8, 128, 200, 256),
     (5, 1, 64, 1000, 1024),
     (16, 2, 256, 2048, 2112),
-    (4, 2, 128, 5000, 5056),      # two merge groups of unequal size (64 + 15 chunks)
-    (8, 1, 256, 32768, 32768),    # eight merge groups of 64 chunks
+    (4, 2, 128, 5000, 5056),      # five merge groups of unequal size (4 x 16 + 15 chunks)
+    (8, 1, 256, 32768, 32768),    # 32 merge groups of 16 chunks
+    (4096, 4096, 64, 40, 64),     # the most KV heads: fewer merge groups per head fit the tickets
+    (2048, 2048, 64, 1040, 1088), # 2048 KV heads of two merge groups (16 + 1 chunks), ticket stride 31
 ]
 
 
