@@ -140,26 +140,24 @@ def mx_dequantize(codes: np.ndarray, scale_codes: np.ndarray, elem: str) -> np.n
 def mx_linear(x16: np.ndarray, w16: np.ndarray) -> np.ndarray:
     """out [M][N] fp64 = MXFP8(x) . MXFP4(w)^T with per-block scales (see the module doc).
 
-    x16 fp16 [M][K] activations, w16 fp16 [N][K] weights.  Each block term is
-    X_a * X_w * (integer-valued block dot of the element values), summed in
-    fp64.  Parity: pinned by the lossless special case (equals np.matmul of
-    the raw inputs) and power-of-two scaling (tests/test_oracle_mx.py).
+    x16 fp16 [M][K] activations, w16 fp16 [N][K] weights: both are converted
+    by mx_quantize, then multiplied by mx_linear_prequantized (one body for
+    both entry points).  Parity: pinned by the lossless special case (equals
+    np.matmul of the raw inputs) and power-of-two scaling
+    (tests/test_oracle_mx.py).
     """
     qa, sa = mx_quantize(x16, "e4m3")
     qw, sw = mx_quantize(w16, "e2m1")
-    va = e4m3_value(qa).reshape(qa.shape[0], -1, BLOCK)
-    vw = e2m1_value(qw).reshape(qw.shape[0], -1, BLOCK)
-    dots = np.einsum("mbj,nbj->mnb", va, vw)          # exact block dots (small integers times 2^-k)
-    scale = np.exp2(sa.astype(np.float64)[:, None, :] + sw.astype(np.float64)[None, :, :] - 254.0)
-    return np.sum(dots * scale, axis=2)
+    return mx_linear_prequantized(qa, sa, qw, sw)
 
 
 def mx_linear_prequantized(qa, sa, qw, sw) -> np.ndarray:
-    """The same product from codes already converted (for large shapes: the
-    codes come from mx_quantize on the same inputs)."""
+    """The product from codes already converted by mx_quantize: each block term
+    is X_a * X_w * (the exact block dot of the element values), summed in fp64.
+    mx_linear is this function after the conversions, so its pins cover it."""
     va = e4m3_value(qa).reshape(qa.shape[0], -1, BLOCK)
     vw = e2m1_value(qw).reshape(qw.shape[0], -1, BLOCK)
-    dots = np.einsum("mbj,nbj->mnb", va, vw)
+    dots = np.einsum("mbj,nbj->mnb", va, vw)          # exact block dots (small integers times 2^-k)
     scale = np.exp2(sa.astype(np.float64)[:, None, :] + sw.astype(np.float64)[None, :, :] - 254.0)
     return np.sum(dots * scale, axis=2)
 

@@ -87,3 +87,60 @@ def test_layer_keeps_the_residual_stream_bounded(seed):
     y = oracle.decoder_layer(x, w, 0.01, 1e-6)
     rel = np.linalg.norm(y - x) / np.linalg.norm(x)
     assert 1e-4 < rel < 0.5
+
+
+def _zeroed(w, name, rows=None):
+    """A copy of w with the weights of `name` zeroed (all rows, or rows[0]:rows[1])."""
+    out = {k: (v[0].copy(), v[1]) for k, v in w.items()}
+    qw = out[name][0]
+    if rows is None:
+        qw[:] = 0
+    else:
+        qw[rows[0]:rows[1]] = 0
+    return out
+
+
+@pytest.mark.parametrize("seed", [0, 1, 2])
+def test_feed_forward_reads_the_stream_after_attention(seed):
+    """The feed-forward half normalises x after the attention residual add.
+
+    layer(x) equals two layer calls: the first without the feed-forward path
+    (down = 0, so it returns x after attention exactly), the second without
+    the attention path (o = 0, so its attention add is exact and its
+    feed-forward path sees the first call's result).  A layer whose
+    feed-forward path normalised the pre-attention x, or added d to it, would
+    differ."""
+    x = np.random.default_rng(20 + seed).standard_normal((3, 64)).astype(np.float32)
+    w = _layer_weights(30 + seed)
+    whole = oracle.decoder_layer(x, w, 0.01, 1e-6)
+    after_attention = oracle.decoder_layer(x, _zeroed(w, "down"), 0.01, 1e-6)
+    assert not np.array_equal(after_attention, x)
+    two_calls = oracle.decoder_layer(after_attention, _zeroed(w, "o"), 0.01, 1e-6)
+    assert np.array_equal(whole, two_calls)
+    # and the feed-forward path of the second call does change the stream
+    assert not np.array_equal(two_calls, after_attention)
+
+
+@pytest.mark.parametrize("half", ["gate", "up"])
+def test_feed_forward_needs_both_halves_of_gate_up(half):
+    """u = fp16(gate * up): with either half of gate/up zero the product is
+    zero and the feed-forward path adds nothing (the same result as down = 0)."""
+    x = np.random.default_rng(40).standard_normal((2, 64)).astype(np.float32)
+    f = 128
+    w = _layer_weights(41, f=f)
+    rows = (0, f) if half == "gate" else (f, 2 * f)
+    got = oracle.decoder_layer(x, _zeroed(w, "gate_up", rows), 0.01, 1e-6)
+    assert np.array_equal(got, oracle.decoder_layer(x, _zeroed(w, "down"), 0.01, 1e-6))
+    assert not np.array_equal(oracle.decoder_layer(x, w, 0.01, 1e-6), got)
+
+
+def test_attention_path_reads_only_the_query_slice():
+    """a = fp16(q[:, :H]): qkv columns past H never matter, and with the first H
+    zero the attention path adds nothing (the same result as o = 0)."""
+    x = np.random.default_rng(50).standard_normal((2, 64)).astype(np.float32)
+    w = _layer_weights(51, n_qkv=192)
+    whole = oracle.decoder_layer(x, w, 0.01, 1e-6)
+    assert np.array_equal(oracle.decoder_layer(x, _zeroed(w, "qkv", (64, 192)), 0.01, 1e-6), whole)
+    no_query = oracle.decoder_layer(x, _zeroed(w, "qkv", (0, 64)), 0.01, 1e-6)
+    assert np.array_equal(no_query, oracle.decoder_layer(x, _zeroed(w, "o"), 0.01, 1e-6))
+    assert not np.array_equal(no_query, whole)

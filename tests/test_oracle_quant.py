@@ -131,3 +131,33 @@ def test_rejects_non_finite():
     x[0, 3] = np.inf
     with pytest.raises(AssertionError):
         oracle.quantize_activations(x)
+
+
+def _division_blocks():
+    with open(os.path.join(GOLDEN, "quant_division_blocks.json")) as f:
+        return json.load(f)["blocks"]
+
+
+@pytest.mark.parametrize("blk", _division_blocks(), ids=lambda b: b["name"])
+def test_division_block(blk):
+    """Non-power-of-two scales: codes derived with exact rational arithmetic
+    (tests/golden/make_quant_division_blocks.py), where a reciprocal multiply
+    or a reciprocal scale would round some elements the other way."""
+    x = np.array([blk["x"]], dtype=np.float16)
+    assert x.astype(np.float64)[0].tolist() == blk["x"]
+    q, sx = oracle.quantize_activations(x)
+    assert sx[0, 0] == np.float32(blk["sx"])
+    assert q[0].tolist() == blk["q"]
+
+
+def test_division_blocks_tell_the_shortcuts_apart():
+    """The fixture only pins the division if the shortcuts give other codes somewhere."""
+    blocks = _division_blocks()
+    assert any(b["q"] != b["q_if_reciprocal_multiply"] for b in blocks)
+    assert any(b["q"] != b["q_if_inverse_scale"] for b in blocks)
+    assert any(b["q"] != b["q_if_scale_times_rcp127"] or b["sx"] != b["sx_if_scale_times_rcp127"]
+               for b in blocks)
+    for b in blocks:
+        s = np.float32(b["sx"])
+        m, _ = np.frexp(s)
+        assert m != 0.5, "scale must not be a power of two"
