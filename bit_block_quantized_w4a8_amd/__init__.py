@@ -22,7 +22,9 @@ __all__ = [
     "PATH_AUTO", "PATH_GEMV", "PATH_GEMM", "W4A8Error", "library_path", "load_library",
     "declared_functions", "init", "pack_weights", "linear", "linear_argmax",
     "quantize_act", "block_sums", "gemv_max_m", "auto_path", "mx_pack_weights", "mx_quantize_act", "mx_linear", "kv_cache", "decode_attention", "Weights", "residual_norm_cast",
-    "decoder_layer_workspace", "decoder_layer",
+    "decoder_layer_workspace", "decoder_layer", "reserve_scratch", "scratch_capacity", "linear_scratch_bytes",
+    "decoder_layer_scratch_bytes", "norm_linear_argmax_scratch_bytes", "mx_linear_scratch_bytes",
+    "decode_attention_scratch_bytes", "decoder_layer_workspace_offsets",
 ]
 
 PATH_AUTO, PATH_GEMV, PATH_GEMM = 0, 1, 2
@@ -87,6 +89,16 @@ def load_library() -> ctypes.CDLL:
                                 ctypes.POINTER(_CWeights), ctypes.POINTER(_CWeights), ctypes.c_float,
                                 ctypes.c_float, p, ctypes.c_size_t, p], i32),
         "w4a8_last_error": ([], ctypes.c_char_p),
+        "w4a8_decoder_layer_workspace_offsets": ([i64, i64, ctypes.POINTER(_CWeights), ctypes.POINTER(_CWeights),
+                                                  ctypes.POINTER(ctypes.c_size_t)], i32),
+        "w4a8_reserve_scratch": ([ctypes.c_size_t], i32),
+        "w4a8_scratch_capacity": ([ctypes.POINTER(ctypes.c_size_t)], i32),
+        "w4a8_linear_scratch_bytes": ([i64, i64, i64, i32, ctypes.POINTER(ctypes.c_size_t)], i32),
+        "w4a8_decoder_layer_scratch_bytes": ([i64, i64, ctypes.POINTER(_CWeights), ctypes.POINTER(_CWeights),
+                                              ctypes.POINTER(ctypes.c_size_t)], i32),
+        "w4a8_norm_linear_argmax_scratch_bytes": ([i64, i64, i64, ctypes.POINTER(ctypes.c_size_t)], i32),
+        "w4a8_mx_linear_scratch_bytes": ([i64, i64, i64, ctypes.POINTER(ctypes.c_size_t)], i32),
+        "w4a8_decode_attention_scratch_bytes": ([i64, i64, i64, i64, ctypes.POINTER(ctypes.c_size_t)], i32),
     }
     for name, (args, res) in sig.items():
         fn = getattr(lib, name)
@@ -126,6 +138,46 @@ def init(device: int | None = None) -> None:
     _check("w4a8_init", load_library().w4a8_init(dev))
     torch.cuda.set_device(dev)
     _initialised.add(dev)
+
+
+def reserve_scratch(nbytes: int, device: int | None = None) -> None:
+    """Grow the library's scratch work area on the device to at least nbytes (allocates;
+    call it before timing or graph capture, never inside)."""
+    init(device)
+    _check("w4a8_reserve_scratch", load_library().w4a8_reserve_scratch(int(nbytes)))
+
+
+def scratch_capacity(device: int | None = None) -> int:
+    init(device)
+    nbytes = ctypes.c_size_t(0)
+    _check("w4a8_scratch_capacity", load_library().w4a8_scratch_capacity(ctypes.byref(nbytes)))
+    return int(nbytes.value)
+
+
+def _size_query(fn: str, *args) -> int:
+    nbytes = ctypes.c_size_t(0)
+    _check(fn, getattr(load_library(), fn)(*args, ctypes.byref(nbytes)))
+    return int(nbytes.value)
+
+
+def linear_scratch_bytes(m: int, k: int, n: int, path: int = PATH_AUTO) -> int:
+    return _size_query("w4a8_linear_scratch_bytes", m, k, n, path)
+
+
+def decoder_layer_scratch_bytes(m: int, h: int, qkv: "Weights", gate_up: "Weights") -> int:
+    return _size_query("w4a8_decoder_layer_scratch_bytes", m, h, ctypes.byref(qkv.c), ctypes.byref(gate_up.c))
+
+
+def norm_linear_argmax_scratch_bytes(m: int, k: int, n: int) -> int:
+    return _size_query("w4a8_norm_linear_argmax_scratch_bytes", m, k, n)
+
+
+def mx_linear_scratch_bytes(m: int, k: int, n: int) -> int:
+    return _size_query("w4a8_mx_linear_scratch_bytes", m, k, n)
+
+
+def decode_attention_scratch_bytes(n_heads: int, n_kv_heads: int, head_dim: int, length: int) -> int:
+    return _size_query("w4a8_decode_attention_scratch_bytes", n_heads, n_kv_heads, head_dim, length)
 
 
 def _ready(t: torch.Tensor):
@@ -377,6 +429,14 @@ def decoder_layer_workspace(m: int, h: int, qkv: Weights, gate_up: Weights) -> i
     _check("w4a8_decoder_layer_workspace", load_library().w4a8_decoder_layer_workspace(
         m, h, ctypes.byref(qkv.c), ctypes.byref(gate_up.c), ctypes.byref(nbytes)))
     return int(nbytes.value)
+
+
+def decoder_layer_workspace_offsets(m: int, h: int, qkv: Weights, gate_up: Weights) -> dict:
+    """Byte offsets of the intermediates q, a, o, n, g, u, d in the layer workspace."""
+    offs = (ctypes.c_size_t * 7)()
+    _check("w4a8_decoder_layer_workspace_offsets", load_library().w4a8_decoder_layer_workspace_offsets(
+        m, h, ctypes.byref(qkv.c), ctypes.byref(gate_up.c), offs))
+    return dict(zip("q a o n g u d".split(), (int(v) for v in offs)))
 
 
 def decoder_layer(x: torch.Tensor, qkv: Weights, o: Weights, gate_up: Weights, down: Weights,

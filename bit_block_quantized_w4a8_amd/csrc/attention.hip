@@ -378,8 +378,10 @@ int launch_decode_attention(const float* q, const float* k_new, const float* v_n
                             uint16_t* out, Scratch* sc, hipStream_t stream) {
   if (n_heads % n_kv_heads != 0 || n_heads / n_kv_heads > kMaxGroup || capacity % kChunk != 0 ||
       length < 1 || length > capacity || n_kv_heads < 1 || n_kv_heads >= (kMaxTickets - 2) / 2 ||
-      attention_scratch_bytes(n_kv_heads, n_heads / n_kv_heads, head_dim, length) > sc->work_bytes)
+      sc->n_tickets < kMaxTickets)
     return hip_fail(hipErrorInvalidValue, "decode attention: shape outside the kernel's limits");
+  const int rc = require_scratch(sc, attention_scratch_bytes(n_kv_heads, n_heads / n_kv_heads, head_dim, length));
+  if (rc != W4A8_OK) return rc;
   const int chunks = attention_chunks(length);
   const int group = n_heads / n_kv_heads;
   AttnArgs a{};

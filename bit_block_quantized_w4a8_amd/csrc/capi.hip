@@ -1,10 +1,12 @@
 // C ABI of the W4A8 block-32 library: argument validation, per-device scratch,
 // stage dispatch (decode GEMV or prefill GEMM) and error reporting.
+#include <algorithm>
 #include <cstdarg>
 #include <cstdio>
 #include <cstdlib>
 #include <cstring>
 #include <mutex>
+#include <vector>
 
 #include "kernels.hpp"
 
@@ -15,11 +17,17 @@ namespace {
 thread_local char g_error[512] = "";
 
 constexpr int kMaxDevices = 64;
-constexpr size_t kInitialWork = 32u << 20;
+// Work area reserved by w4a8_init: enough for every shape of the pages'
+// workloads (prefill staging of 512 x 8192 is 4.7 MB, decode attention over
+// 32768 positions of one KV head ~2 MB); w4a8_reserve_scratch adds more.
+constexpr size_t kInitialWork = 64u << 20;
 
 struct DeviceState {
   bool ready = false;
   Scratch sc;
+  // Work areas replaced by w4a8_reserve_scratch.  They are never freed: a HIP
+  // graph captured while one was current still reads and writes it.
+  std::vector<void*> retired;
 };
 DeviceState g_dev[kMaxDevices];
 bool g_any_ready = false;
@@ -100,25 +108,20 @@ int hip_fail(hipError_t e, const char* what) {
   return W4A8_EHIP;
 }
 
-int scratch_for(size_t work_bytes, Scratch** out) {
+int library_scratch(Scratch** out) {
   DeviceState* st = nullptr;
-  int rc = current_state(&st);
+  const int rc = current_state(&st);
   if (rc != W4A8_OK) return rc;
-  Scratch& sc = st->sc;
-  if (work_bytes > sc.work_bytes) {
-    std::lock_guard<std::mutex> lock(g_mutex);
-    if (work_bytes > sc.work_bytes) {
-      // Kernels already queued may still read the old buffer.
-      W4A8_HIP(hipDeviceSynchronize());
-      if (sc.work) W4A8_HIP(hipFree(sc.work));
-      sc.work = nullptr;
-      sc.work_bytes = 0;
-      const size_t bytes = (work_bytes + (1u << 20) - 1) & ~static_cast<size_t>((1u << 20) - 1);
-      W4A8_HIP(hipMalloc(&sc.work, bytes));
-      sc.work_bytes = bytes;
-    }
+  *out = &st->sc;
+  return W4A8_OK;
+}
+
+int require_scratch(const Scratch* sc, size_t work_bytes) {
+  if (work_bytes > sc->work_bytes) {
+    set_error("this call needs %zu bytes of scratch and %zu are reserved: call w4a8_reserve_scratch(%zu) first",
+              work_bytes, sc->work_bytes, work_bytes);
+    return W4A8_EINVAL;
   }
-  *out = &sc;
   return W4A8_OK;
 }
 
@@ -151,6 +154,72 @@ int auto_path(int64_t M, int64_t K, int64_t N) {
   return M <= (big ? (lim < 2 ? lim : 2) : lim) ? W4A8_PATH_GEMV : W4A8_PATH_GEMM;
 }
 
+namespace {
+
+int check_weights(const w4a8_weights* w, const char* name) {
+  W4A8_REQUIRE(w && w->packed_w && w->w_scales, "%s: null weights", name);
+  W4A8_REQUIRE(aligned(w->packed_w, 16) && aligned(w->w_scales, 16), "%s: weights must be 16-byte aligned", name);
+  return check_shape(1, w->K, w->N, 1);
+}
+
+int check_layer_shapes(int64_t M, int64_t H, const w4a8_weights* qkv, const w4a8_weights* gate_up) {
+  W4A8_REQUIRE(qkv && gate_up, "null weights");
+  W4A8_REQUIRE(M >= 1 && M <= 65536 && H >= 64 && H % 64 == 0 && H < (int64_t{1} << 24), "bad shape M=%lld H=%lld",
+               static_cast<long long>(M), static_cast<long long>(H));
+  W4A8_REQUIRE(qkv->K == H && qkv->N >= H && qkv->N < (int64_t{1} << 30) && qkv->N % 64 == 0,
+               "qkv must be H x N with N >= H");
+  W4A8_REQUIRE(gate_up->K == H && gate_up->N % 128 == 0 && gate_up->N >= 128 && gate_up->N < (int64_t{1} << 30),
+               "gate_up must be H x 2F with 2F a multiple of 128");
+  return W4A8_OK;
+}
+
+// Whether the one-token layer runs as the four fused GEMV launches.
+bool layer_fused(int64_t M, int64_t H, int64_t n_qkv, int64_t n_gu) {
+  return M == 1 && gemv_fused_supported(kGemvCast, true, static_cast<int>(H), static_cast<int>(n_qkv)) &&
+         gemv_fused_supported(kGemvGated, true, static_cast<int>(H), static_cast<int>(n_gu));
+}
+
+// Whether every projection of the layer runs the prefill GEMM.
+bool layer_all_gemm(int64_t M, int64_t H, int64_t n_qkv, int64_t n_gu) {
+  return auto_path(M, H, n_qkv) == W4A8_PATH_GEMM && auto_path(M, H, H) == W4A8_PATH_GEMM &&
+         auto_path(M, H, n_gu) == W4A8_PATH_GEMM && auto_path(M, n_gu / 2, H) == W4A8_PATH_GEMM;
+}
+
+size_t linear_scratch(int64_t M, int64_t K, int64_t N, int path) {
+  if (path == W4A8_PATH_AUTO) path = auto_path(M, K, N);
+  if (path == W4A8_PATH_GEMV) return 0;
+  return gemm_scratch_bytes(static_cast<int>(M), static_cast<int>(K), static_cast<int>(N));
+}
+
+// Scratch of one decoder layer: every linear of it runs with the library's
+// staging and split-K partials (the fused one-token launches need none).
+size_t layer_scratch(int64_t M, int64_t H, int64_t n_qkv, int64_t n_gu) {
+  if (layer_fused(M, H, n_qkv, n_gu)) return 0;
+  const size_t a = linear_scratch(M, H, n_qkv, W4A8_PATH_AUTO), b = linear_scratch(M, H, H, W4A8_PATH_AUTO);
+  const size_t c = linear_scratch(M, H, n_gu, W4A8_PATH_AUTO), d = linear_scratch(M, n_gu / 2, H, W4A8_PATH_AUTO);
+  return std::max(std::max(a, b), std::max(c, d));
+}
+
+size_t norm_argmax_scratch(int64_t M, int64_t K, int64_t N) {
+  if (M == 1 && gemv_fused_supported(kGemvArgmax, true, static_cast<int>(K), static_cast<int>(N))) return 0;
+  return static_cast<size_t>(M) * K * 2;
+}
+
+int check_attention(int64_t n_heads, int64_t n_kv_heads, int64_t head_dim, int64_t length) {
+  W4A8_REQUIRE(head_dim == 64 || head_dim == 128 || head_dim == 256, "head_dim = %lld must be 64, 128 or 256",
+               static_cast<long long>(head_dim));
+  W4A8_REQUIRE(n_kv_heads >= 1 && n_kv_heads <= 4096, "n_kv_heads = %lld out of range [1, 4096]",
+               static_cast<long long>(n_kv_heads));
+  W4A8_REQUIRE(n_heads >= n_kv_heads && n_heads % n_kv_heads == 0 && n_heads / n_kv_heads <= 8,
+               "n_heads = %lld must be 1 to 8 times n_kv_heads = %lld", static_cast<long long>(n_heads),
+               static_cast<long long>(n_kv_heads));
+  W4A8_REQUIRE(length >= 1 && length <= (int64_t{1} << 24), "length = %lld out of range [1, 2^24]",
+               static_cast<long long>(length));
+  return W4A8_OK;
+}
+
+}  // namespace
+
 }  // namespace w4a8
 
 using namespace w4a8;
@@ -178,11 +247,83 @@ int w4a8_init(int device) {
   sc.slots = static_cast<unsigned long long*>(sc.base);
   sc.tickets = reinterpret_cast<uint32_t*>(static_cast<char*>(sc.base) +
                                            kMaxArgmaxRows * kArgmaxSpread * sizeof(unsigned long long));
+  sc.n_tickets = kMaxTickets;
   W4A8_HIP(hipMalloc(&sc.work, kInitialWork));
   sc.work_bytes = kInitialWork;
   W4A8_HIP(hipDeviceSynchronize());
   st.ready = true;
   g_any_ready = true;
+  return W4A8_OK;
+}
+
+int w4a8_reserve_scratch(size_t bytes) {
+  W4A8_REQUIRE(bytes <= (size_t{1} << 40), "scratch of %zu bytes is beyond 2^40", bytes);
+  DeviceState* st = nullptr;
+  int rc = current_state(&st);
+  if (rc != W4A8_OK) return rc;
+  std::lock_guard<std::mutex> lock(g_mutex);
+  Scratch& sc = st->sc;
+  if (bytes <= sc.work_bytes) return W4A8_OK;
+  const size_t rounded = (bytes + (size_t{1} << 20) - 1) & ~((size_t{1} << 20) - 1);
+  void* p = nullptr;
+  W4A8_HIP(hipMalloc(&p, rounded));
+  st->retired.push_back(sc.work);
+  sc.work = p;
+  sc.work_bytes = rounded;
+  return W4A8_OK;
+}
+
+int w4a8_scratch_capacity(size_t* bytes) {
+  W4A8_REQUIRE(bytes, "null pointer");
+  Scratch* sc = nullptr;
+  const int rc = library_scratch(&sc);
+  if (rc != W4A8_OK) return rc;
+  *bytes = sc->work_bytes;
+  return W4A8_OK;
+}
+
+int w4a8_linear_scratch_bytes(int64_t M, int64_t K, int64_t N, int path, size_t* bytes) {
+  W4A8_REQUIRE(bytes, "null pointer");
+  const int rc = check_shape(M, K, N, int64_t{1} << 20);
+  if (rc != W4A8_OK) return rc;
+  W4A8_REQUIRE(path == W4A8_PATH_AUTO || path == W4A8_PATH_GEMV || path == W4A8_PATH_GEMM, "unknown path %d", path);
+  *bytes = linear_scratch(M, K, N, path);
+  return W4A8_OK;
+}
+
+int w4a8_decoder_layer_scratch_bytes(int64_t M, int64_t H, const w4a8_weights* qkv, const w4a8_weights* gate_up,
+                                     size_t* bytes) {
+  W4A8_REQUIRE(bytes, "null pointer");
+  const int rc = check_layer_shapes(M, H, qkv, gate_up);
+  if (rc != W4A8_OK) return rc;
+  *bytes = layer_scratch(M, H, qkv->N, gate_up->N);
+  return W4A8_OK;
+}
+
+int w4a8_norm_linear_argmax_scratch_bytes(int64_t M, int64_t K, int64_t N, size_t* bytes) {
+  W4A8_REQUIRE(bytes, "null pointer");
+  const int rc = check_shape(M, K, N, kMaxArgmaxRows);
+  if (rc != W4A8_OK) return rc;
+  *bytes = norm_argmax_scratch(M, K, N);
+  return W4A8_OK;
+}
+
+int w4a8_mx_linear_scratch_bytes(int64_t M, int64_t K, int64_t N, size_t* bytes) {
+  W4A8_REQUIRE(bytes, "null pointer");
+  const int rc = check_shape(M, K, N, int64_t{1} << 20);
+  if (rc != W4A8_OK) return rc;
+  W4A8_REQUIRE(K % 64 == 0, "K = %lld must be a multiple of 64", static_cast<long long>(K));
+  *bytes = mx_scratch_bytes(static_cast<int>(M), static_cast<int>(K));
+  return W4A8_OK;
+}
+
+int w4a8_decode_attention_scratch_bytes(int64_t n_heads, int64_t n_kv_heads, int64_t head_dim, int64_t length,
+                                        size_t* bytes) {
+  W4A8_REQUIRE(bytes, "null pointer");
+  const int rc = check_attention(n_heads, n_kv_heads, head_dim, length);
+  if (rc != W4A8_OK) return rc;
+  *bytes = attention_scratch_bytes(static_cast<int>(n_kv_heads), static_cast<int>(n_heads / n_kv_heads),
+                                   static_cast<int>(head_dim), static_cast<int>(length));
   return W4A8_OK;
 }
 
@@ -199,6 +340,24 @@ int w4a8_pack_weights(const int8_t* q, const uint16_t* s, int64_t K, int64_t N, 
   return launch_pack(q, s, static_cast<int>(K), static_cast<int>(N), packed_w, w_scales, stream);
 }
 
+namespace {
+// w4a8_linear_path on the scratch `sc`, arguments already checked.
+int linear_on(const uint16_t* x, const uint8_t* packed_w, const uint16_t* w_scales, int64_t M, int64_t K, int64_t N,
+              float* out, int path, Scratch* sc, hipStream_t stream) {
+  if (path == W4A8_PATH_AUTO) path = auto_path(M, K, N);
+  const int rc = require_scratch(sc, linear_scratch(M, K, N, path));
+  if (rc != W4A8_OK) return rc;
+  if (path == W4A8_PATH_GEMV) {
+    GemvArgs a{x, packed_w, w_scales, static_cast<int>(M), static_cast<int>(K), static_cast<int>(N),
+               out, nullptr, nullptr, nullptr};
+    return launch_gemv(a, 0, sc, stream);
+  }
+  GemmArgs a{x, packed_w, w_scales, static_cast<int>(M), static_cast<int>(K), static_cast<int>(N), out,
+             nullptr};
+  return launch_gemm(a, 0, sc, stream);
+}
+}  // namespace
+
 int w4a8_linear_path(const uint16_t* x, const uint8_t* packed_w, const uint16_t* w_scales, int64_t M,
                      int64_t K, int64_t N, float* out, int path, hipStream_t stream) {
   int rc = check_linear_args(x, packed_w, w_scales, M, K, N, int64_t{1} << 20);
@@ -207,18 +366,10 @@ int w4a8_linear_path(const uint16_t* x, const uint8_t* packed_w, const uint16_t*
   W4A8_REQUIRE(aligned(out, 16), "out must be 16-byte aligned");
   W4A8_REQUIRE(path == W4A8_PATH_AUTO || path == W4A8_PATH_GEMV || path == W4A8_PATH_GEMM,
                "unknown path %d", path);
-  DeviceState* st = nullptr;
-  rc = current_state(&st);
+  Scratch* sc = nullptr;
+  rc = library_scratch(&sc);
   if (rc != W4A8_OK) return rc;
-  if (path == W4A8_PATH_AUTO) path = auto_path(M, K, N);
-  if (path == W4A8_PATH_GEMV) {
-    GemvArgs a{x, packed_w, w_scales, static_cast<int>(M), static_cast<int>(K), static_cast<int>(N),
-               out, nullptr, nullptr, nullptr};
-    return launch_gemv(a, 0, stream);
-  }
-  GemmArgs a{x, packed_w, w_scales, static_cast<int>(M), static_cast<int>(K), static_cast<int>(N), out,
-             nullptr};
-  return launch_gemm(a, 0, stream);
+  return linear_on(x, packed_w, w_scales, M, K, N, out, path, sc, stream);
 }
 
 int w4a8_linear(const uint16_t* x, const uint8_t* packed_w, const uint16_t* w_scales, int64_t M,
@@ -233,12 +384,12 @@ int w4a8_linear_argmax(const uint16_t* x, const uint8_t* packed_w, const uint16_
   W4A8_REQUIRE(argmax, "null argmax pointer");
   W4A8_REQUIRE(aligned(argmax, 4), "argmax must be 4-byte aligned");
   W4A8_REQUIRE(!logits || aligned(logits, 16), "logits must be 16-byte aligned");
-  DeviceState* st = nullptr;
-  rc = current_state(&st);
+  Scratch* sc = nullptr;
+  rc = library_scratch(&sc);
   if (rc != W4A8_OK) return rc;
   GemvArgs a{x, packed_w, w_scales, static_cast<int>(M), static_cast<int>(K), static_cast<int>(N),
              nullptr, nullptr, logits, argmax};
-  return launch_gemv(a, 2, stream);
+  return launch_gemv(a, 2, sc, stream);
 }
 
 int w4a8_quantize_act(const uint16_t* x, int64_t M, int64_t K, int8_t* qx, float* sx,
@@ -263,18 +414,20 @@ int w4a8_block_sums(const uint16_t* x, const uint8_t* packed_w, int64_t M, int64
   W4A8_REQUIRE(sums && aligned(sums, 16), "sums must be a 16-byte aligned pointer");
   W4A8_REQUIRE(path == W4A8_PATH_AUTO || path == W4A8_PATH_GEMV || path == W4A8_PATH_GEMM,
                "unknown path %d", path);
-  DeviceState* st = nullptr;
-  rc = current_state(&st);
+  Scratch* sc = nullptr;
+  rc = library_scratch(&sc);
   if (rc != W4A8_OK) return rc;
   if (path == W4A8_PATH_AUTO) path = auto_path(M, K, N);
+  rc = require_scratch(sc, linear_scratch(M, K, N, path));
+  if (rc != W4A8_OK) return rc;
   if (path == W4A8_PATH_GEMV) {
     GemvArgs a{x, packed_w, nullptr, static_cast<int>(M), static_cast<int>(K), static_cast<int>(N),
                nullptr, sums, nullptr, nullptr};
-    return launch_gemv(a, 1, stream);
+    return launch_gemv(a, 1, sc, stream);
   }
   GemmArgs a{x, packed_w, nullptr, static_cast<int>(M), static_cast<int>(K), static_cast<int>(N),
              nullptr, sums};
-  return launch_gemm(a, 1, stream);
+  return launch_gemm(a, 1, sc, stream);
 }
 
 int w4a8_residual_norm_cast(float* x, const float* d, int64_t ld_d, float alpha, float eps, int64_t M,
@@ -290,22 +443,25 @@ int w4a8_residual_norm_cast(float* x, const float* d, int64_t ld_d, float alpha,
   return launch_residual_norm_cast(x, d, ld_d, alpha, eps, static_cast<int>(M), static_cast<int>(H), y, stream);
 }
 
-namespace {
-int check_weights(const w4a8_weights* w, const char* name) {
-  W4A8_REQUIRE(w && w->packed_w && w->w_scales, "%s: null weights", name);
-  W4A8_REQUIRE(aligned(w->packed_w, 16) && aligned(w->w_scales, 16), "%s: weights must be 16-byte aligned", name);
-  return check_shape(1, w->K, w->N, 1);
-}
-}  // namespace
-
 int w4a8_decoder_layer_workspace(int64_t M, int64_t H, const w4a8_weights* qkv, const w4a8_weights* gate_up,
                                  size_t* bytes) {
-  W4A8_REQUIRE(bytes && qkv && gate_up, "null pointer");
-  W4A8_REQUIRE(M >= 1 && M <= 65536 && H >= 64 && H % 64 == 0 && H < (int64_t{1} << 24), "bad shape");
-  W4A8_REQUIRE(qkv->N >= H && qkv->N < (int64_t{1} << 30) && gate_up->N >= 128 && gate_up->N < (int64_t{1} << 30),
-               "bad weight shapes");
+  W4A8_REQUIRE(bytes, "null pointer");
+  const int rc = check_layer_shapes(M, H, qkv, gate_up);
+  if (rc != W4A8_OK) return rc;
   *bytes = layer_workspace(static_cast<int>(M), static_cast<int>(H), static_cast<int>(qkv->N),
                            static_cast<int>(gate_up->N)).bytes;
+  return W4A8_OK;
+}
+
+int w4a8_decoder_layer_workspace_offsets(int64_t M, int64_t H, const w4a8_weights* qkv, const w4a8_weights* gate_up,
+                                         size_t offsets[7]) {
+  W4A8_REQUIRE(offsets, "null pointer");
+  const int rc = check_layer_shapes(M, H, qkv, gate_up);
+  if (rc != W4A8_OK) return rc;
+  const LayerWorkspace w = layer_workspace(static_cast<int>(M), static_cast<int>(H), static_cast<int>(qkv->N),
+                                           static_cast<int>(gate_up->N));
+  const size_t o[7] = {w.q, w.a, w.o, w.n, w.g, w.u, w.d};
+  for (int i = 0; i < 7; ++i) offsets[i] = o[i];
   return W4A8_OK;
 }
 
@@ -313,23 +469,22 @@ int w4a8_decoder_layer(float* x, int64_t M, int64_t H, const w4a8_weights* qkv, 
                        const w4a8_weights* gate_up, const w4a8_weights* down, float residual_scale, float eps,
                        void* workspace, size_t workspace_bytes, hipStream_t stream) {
   W4A8_REQUIRE(x && aligned(x, 16), "x must be a 16-byte aligned pointer");
-  W4A8_REQUIRE(M >= 1 && M <= 65536 && H >= 64 && H % 64 == 0 && H < (int64_t{1} << 24), "bad shape M=%lld H=%lld",
-               static_cast<long long>(M), static_cast<long long>(H));
-  int rc;
+  int rc = check_layer_shapes(M, H, qkv, gate_up);
+  if (rc != W4A8_OK) return rc;
   if ((rc = check_weights(qkv, "qkv")) != W4A8_OK || (rc = check_weights(o, "o")) != W4A8_OK ||
       (rc = check_weights(gate_up, "gate_up")) != W4A8_OK || (rc = check_weights(down, "down")) != W4A8_OK)
     return rc;
-  W4A8_REQUIRE(qkv->K == H && qkv->N >= H, "qkv must be H x N with N >= H");
   W4A8_REQUIRE(o->K == H && o->N == H, "o must be H x H");
-  W4A8_REQUIRE(gate_up->K == H && gate_up->N % 128 == 0 && down->K == gate_up->N / 2 && down->N == H,
-               "gate_up must be H x 2F and down F x H");
-  W4A8_REQUIRE(gate_up->N < (int64_t{1} << 30) && qkv->N < (int64_t{1} << 30), "weights too wide");
+  W4A8_REQUIRE(down->K == gate_up->N / 2 && down->N == H, "gate_up must be H x 2F and down F x H");
   const LayerWorkspace w = layer_workspace(static_cast<int>(M), static_cast<int>(H), static_cast<int>(qkv->N),
                                            static_cast<int>(gate_up->N));
   W4A8_REQUIRE(workspace && aligned(workspace, 256) && workspace_bytes >= w.bytes,
                "workspace must be 256-byte aligned and hold %zu bytes", w.bytes);
-  DeviceState* st = nullptr;
-  rc = current_state(&st);
+  Scratch* sc = nullptr;
+  rc = library_scratch(&sc);
+  if (rc != W4A8_OK) return rc;
+  // Checked before the first launch, so a rejected call leaves x untouched.
+  rc = require_scratch(sc, layer_scratch(M, H, qkv->N, gate_up->N));
   if (rc != W4A8_OK) return rc;
 
   char* base = static_cast<char*>(workspace);
@@ -346,8 +501,7 @@ int w4a8_decoder_layer(float* x, int64_t M, int64_t H, const w4a8_weights* qkv, 
   do {                              \
     if ((rc = (call)) != W4A8_OK) return rc; \
   } while (0)
-  if (M == 1 && gemv_fused_supported(kGemvCast, true, Hi, static_cast<int>(qkv->N)) &&
-      gemv_fused_supported(kGemvGated, true, Hi, 2 * F)) {
+  if (layer_fused(M, H, qkv->N, gate_up->N)) {
     // One token: four GEMV launches, with the normalisation in the prologue
     // of qkv and gate/up and the cast, residual and gated product in the
     // epilogues (the same values as the launches below, up to the summation
@@ -357,40 +511,41 @@ int w4a8_decoder_layer(float* x, int64_t M, int64_t H, const w4a8_weights* qkv, 
     qa.eps = eps;
     qa.y16 = a;
     qa.n16 = Hi;
-    W4A8_STEP(launch_gemv(qa, kGemvCast, stream));
-    GemvArgs oa{a, o->packed_w, o->w_scales, 1, Hi, Hi, nullptr, nullptr, nullptr, nullptr};
+    W4A8_STEP(launch_gemv(qa, kGemvCast, sc, stream));
+    // Each projection's own output also goes to the workspace (o, g and d, as
+    // the nine-launch chain leaves them).
+    GemvArgs oa{a, o->packed_w, o->w_scales, 1, Hi, Hi, ob, nullptr, nullptr, nullptr};
     oa.resid = x;
     oa.alpha = residual_scale;
-    W4A8_STEP(launch_gemv(oa, kGemvResid, stream));
-    GemvArgs ga{nullptr, gate_up->packed_w, gate_up->w_scales, 1, Hi, 2 * F, nullptr, nullptr, nullptr, nullptr};
+    W4A8_STEP(launch_gemv(oa, kGemvResid, sc, stream));
+    GemvArgs ga{nullptr, gate_up->packed_w, gate_up->w_scales, 1, Hi, 2 * F, g, nullptr, nullptr, nullptr};
     ga.xf = x;
     ga.eps = eps;
     ga.y16 = u;
-    W4A8_STEP(launch_gemv(ga, kGemvGated, stream));
-    GemvArgs da{u, down->packed_w, down->w_scales, 1, F, Hi, nullptr, nullptr, nullptr, nullptr};
+    W4A8_STEP(launch_gemv(ga, kGemvGated, sc, stream));
+    GemvArgs da{u, down->packed_w, down->w_scales, 1, F, Hi, d, nullptr, nullptr, nullptr};
     da.resid = x;
     da.alpha = residual_scale;
-    W4A8_STEP(launch_gemv(da, kGemvResid, stream));
+    W4A8_STEP(launch_gemv(da, kGemvResid, sc, stream));
     return W4A8_OK;
   }
   const int Nq = static_cast<int>(qkv->N);
-  if (auto_path(M, H, qkv->N) == W4A8_PATH_GEMM && auto_path(M, H, H) == W4A8_PATH_GEMM &&
-      auto_path(M, H, gate_up->N) == W4A8_PATH_GEMM && auto_path(M, F, H) == W4A8_PATH_GEMM) {
+  if (layer_all_gemm(M, H, qkv->N, gate_up->N)) {
     // Many rows: every projection is a prefill GEMM, and the glue kernels
     // write their fp16 results straight into the next GEMM's quantised
     // staging, so no separate quantise pre-pass runs (four launches fewer).
     GemmStaging sg{};
-    W4A8_STEP(gemm_staging(Mi, Hi, Nq, &sg));
+    W4A8_STEP(gemm_staging(Mi, Hi, Nq, sc, &sg));
     W4A8_STEP(launch_residual_norm_quant(x, nullptr, 0, 0.0f, eps, Mi, Hi, sg, stream));
     const GemmArgs qa{nullptr, qkv->packed_w, qkv->w_scales, Mi, Hi, Nq, q, nullptr};
     GemmStaging so = gemm_staging_at(a, Mi, Hi, Hi);
     if (gemm_cast_supported(Mi, Hi, Nq, Hi, so.m_pad)) {
       // The qkv GEMM quantises fp16 of its query slice into the o
       // projection's staging (in the workspace, in place of a) itself.
-      W4A8_STEP(launch_gemm_staged_cast(qa, Hi, sg, so, stream));
+      W4A8_STEP(launch_gemm_staged_cast(qa, Hi, sg, so, sc, stream));
     } else {
-      W4A8_STEP(launch_gemm_staged(qa, sg, stream));
-      W4A8_STEP(gemm_staging(Mi, Hi, Hi, &so));
+      W4A8_STEP(launch_gemm_staged(qa, sg, sc, stream));
+      W4A8_STEP(gemm_staging(Mi, Hi, Hi, sc, &so));
       W4A8_STEP(launch_cast_quant(q, qkv->N, Mi, Hi, so, stream));
     }
     // The o projection adds 0.01 * o into the residual stream in its
@@ -398,18 +553,18 @@ int w4a8_decoder_layer(float* x, int64_t M, int64_t H, const w4a8_weights* qkv, 
     GemmArgs oa{nullptr, o->packed_w, o->w_scales, Mi, Hi, Hi, nullptr, nullptr};
     oa.resid = x;
     oa.alpha = residual_scale;
-    W4A8_STEP(launch_gemm_staged_resid(oa, so, stream));
-    W4A8_STEP(gemm_staging(Mi, Hi, 2 * F, &sg));
+    W4A8_STEP(launch_gemm_staged_resid(oa, so, sc, stream));
+    W4A8_STEP(gemm_staging(Mi, Hi, 2 * F, sc, &sg));
     W4A8_STEP(launch_residual_norm_quant(x, nullptr, 0, 0.0f, eps, Mi, Hi, sg, stream));
     const GemmArgs gua{nullptr, gate_up->packed_w, gate_up->w_scales, Mi, Hi, 2 * F, g, nullptr};
     GemmStaging sd = gemm_staging_at(g, Mi, F, Hi);
     if (gemm_gated_supported(Mi, Hi, 2 * F, sd.m_pad)) {
       // The gate/up GEMM forms fp16(gate * up) and quantises it into the down
       // projection's staging (in the workspace, in place of g) itself.
-      W4A8_STEP(launch_gemm_staged_gated(gua, sg, sd, stream));
+      W4A8_STEP(launch_gemm_staged_gated(gua, sg, sd, sc, stream));
     } else {
-      W4A8_STEP(launch_gemm_staged(gua, sg, stream));
-      W4A8_STEP(gemm_staging(Mi, F, Hi, &sd));
+      W4A8_STEP(launch_gemm_staged(gua, sg, sc, stream));
+      W4A8_STEP(gemm_staging(Mi, F, Hi, sc, &sd));
       W4A8_STEP(launch_gated_quant(g, Mi, F, sd, stream));
     }
     // The down projection adds 0.01 * d straight into the residual stream in
@@ -417,17 +572,17 @@ int w4a8_decoder_layer(float* x, int64_t M, int64_t H, const w4a8_weights* qkv, 
     GemmArgs da{nullptr, down->packed_w, down->w_scales, Mi, F, Hi, nullptr, nullptr};
     da.resid = x;
     da.alpha = residual_scale;
-    W4A8_STEP(launch_gemm_staged_resid(da, sd, stream));
+    W4A8_STEP(launch_gemm_staged_resid(da, sd, sc, stream));
     return W4A8_OK;
   }
   W4A8_STEP(launch_residual_norm_cast(x, nullptr, 0, 0.0f, eps, Mi, Hi, n, stream));
-  W4A8_STEP(w4a8_linear(n, qkv->packed_w, qkv->w_scales, M, H, qkv->N, q, stream));
+  W4A8_STEP(linear_on(n, qkv->packed_w, qkv->w_scales, M, H, qkv->N, q, W4A8_PATH_AUTO, sc, stream));
   W4A8_STEP(launch_cast_rows(q, qkv->N, Mi, Hi, a, stream));
-  W4A8_STEP(w4a8_linear(a, o->packed_w, o->w_scales, M, H, H, ob, stream));
+  W4A8_STEP(linear_on(a, o->packed_w, o->w_scales, M, H, H, ob, W4A8_PATH_AUTO, sc, stream));
   W4A8_STEP(launch_residual_norm_cast(x, ob, H, residual_scale, eps, Mi, Hi, n, stream));
-  W4A8_STEP(w4a8_linear(n, gate_up->packed_w, gate_up->w_scales, M, H, gate_up->N, g, stream));
+  W4A8_STEP(linear_on(n, gate_up->packed_w, gate_up->w_scales, M, H, gate_up->N, g, W4A8_PATH_AUTO, sc, stream));
   W4A8_STEP(launch_gated_cast(g, Mi, F, u, stream));
-  W4A8_STEP(w4a8_linear(u, down->packed_w, down->w_scales, M, F, H, d, stream));
+  W4A8_STEP(linear_on(u, down->packed_w, down->w_scales, M, F, H, d, W4A8_PATH_AUTO, sc, stream));
   W4A8_STEP(launch_residual_norm_cast(x, d, H, residual_scale, eps, Mi, Hi, nullptr, stream));
 #undef W4A8_STEP
   return W4A8_OK;
@@ -442,25 +597,24 @@ int w4a8_norm_linear_argmax(const float* x, float eps, const uint8_t* packed_w, 
   if (rc != W4A8_OK) return rc;
   W4A8_REQUIRE(argmax && aligned(argmax, 4), "argmax must be a 4-byte aligned pointer");
   W4A8_REQUIRE(!logits || aligned(logits, 16), "logits must be 16-byte aligned");
-  DeviceState* st = nullptr;
-  rc = current_state(&st);
+  Scratch* sc = nullptr;
+  rc = library_scratch(&sc);
+  if (rc != W4A8_OK) return rc;
+  rc = require_scratch(sc, norm_argmax_scratch(M, K, N));
   if (rc != W4A8_OK) return rc;
   const int Mi = static_cast<int>(M), Ki = static_cast<int>(K), Ni = static_cast<int>(N);
-  if (M == 1 && gemv_fused_supported(kGemvArgmax, true, Ki, Ni)) {
+  if (norm_argmax_scratch(M, K, N) == 0) {
     GemvArgs a{nullptr, packed_w, w_scales, 1, Ki, Ni, nullptr, nullptr, logits, argmax};
     a.xf = x;
     a.eps = eps;
-    return launch_gemv(a, kGemvArgmax, stream);
+    return launch_gemv(a, kGemvArgmax, sc, stream);
   }
   // Otherwise normalise into library scratch, then the fused-argmax GEMV.
-  Scratch* sc = nullptr;
-  rc = scratch_for(static_cast<size_t>(M) * K * 2, &sc);
-  if (rc != W4A8_OK) return rc;
   uint16_t* y = static_cast<uint16_t*>(sc->work);
   rc = launch_residual_norm_cast(const_cast<float*>(x), nullptr, 0, 0.0f, eps, Mi, Ki, y, stream);
   if (rc != W4A8_OK) return rc;
   GemvArgs a{y, packed_w, w_scales, Mi, Ki, Ni, nullptr, nullptr, logits, argmax};
-  return launch_gemv(a, kGemvArgmax, stream);
+  return launch_gemv(a, kGemvArgmax, sc, stream);
 }
 
 int w4a8_mx_pack_weights(const uint16_t* w, int64_t K, int64_t N, uint8_t* packed, uint8_t* scales,
@@ -498,27 +652,22 @@ int w4a8_mx_linear(const uint16_t* x, const uint8_t* packed, const uint8_t* scal
   if (rc != W4A8_OK) return rc;
   W4A8_REQUIRE(K % 64 == 0, "K = %lld must be a multiple of 64", static_cast<long long>(K));
   W4A8_REQUIRE(aligned(x, 16) && aligned(packed, 16) && aligned(out, 4), "misaligned pointer");
-  DeviceState* st = nullptr;
-  rc = current_state(&st);
+  Scratch* sc = nullptr;
+  rc = library_scratch(&sc);
   if (rc != W4A8_OK) return rc;
   return launch_mx_linear(x, packed, scales, static_cast<int>(M), static_cast<int>(K), static_cast<int>(N), out,
-                          stream);
+                          sc, stream);
 }
 
 int w4a8_decode_attention(const float* q, const float* k_new, const float* v_new, uint16_t* k_cache,
                           uint16_t* v_cache, int64_t n_heads, int64_t n_kv_heads, int64_t head_dim, int64_t length,
                           int64_t capacity, uint16_t* out, hipStream_t stream) {
   W4A8_REQUIRE(q && k_new && v_new && k_cache && v_cache && out, "null pointer");
-  W4A8_REQUIRE(head_dim == 64 || head_dim == 128 || head_dim == 256, "head_dim = %lld must be 64, 128 or 256",
-               static_cast<long long>(head_dim));
-  W4A8_REQUIRE(n_kv_heads >= 1 && n_kv_heads <= 4096, "n_kv_heads = %lld out of range [1, 4096]",
-               static_cast<long long>(n_kv_heads));
-  W4A8_REQUIRE(n_heads >= n_kv_heads && n_heads % n_kv_heads == 0 && n_heads / n_kv_heads <= 8,
-               "n_heads = %lld must be 1 to 8 times n_kv_heads = %lld", static_cast<long long>(n_heads),
-               static_cast<long long>(n_kv_heads));
+  int rc = check_attention(n_heads, n_kv_heads, head_dim, length);
+  if (rc != W4A8_OK) return rc;
   W4A8_REQUIRE(capacity >= 64 && capacity % 64 == 0 && capacity <= (int64_t{1} << 24),
                "capacity = %lld must be a multiple of 64 in [64, 2^24]", static_cast<long long>(capacity));
-  W4A8_REQUIRE(length >= 1 && length <= capacity, "length = %lld out of range [1, capacity = %lld]",
+  W4A8_REQUIRE(length <= capacity, "length = %lld out of range [1, capacity = %lld]",
                static_cast<long long>(length), static_cast<long long>(capacity));
   W4A8_REQUIRE(n_kv_heads * capacity * head_dim < (int64_t{1} << 38), "KV cache too large");
   W4A8_REQUIRE(aligned(q, 16) && aligned(k_new, 16) && aligned(v_new, 16) && aligned(out, 16) &&
@@ -527,7 +676,7 @@ int w4a8_decode_attention(const float* q, const float* k_new, const float* v_new
   const int Hq = static_cast<int>(n_heads), Hkv = static_cast<int>(n_kv_heads), D = static_cast<int>(head_dim);
   const int Li = static_cast<int>(length), cap = static_cast<int>(capacity);
   Scratch* sc = nullptr;
-  int rc = scratch_for(attention_scratch_bytes(Hkv, Hq / Hkv, D, Li), &sc);
+  rc = library_scratch(&sc);
   if (rc != W4A8_OK) return rc;
   return launch_decode_attention(q, k_new, v_new, k_cache, v_cache, Hq, Hkv, D, Li, cap, out, sc, stream);
 }

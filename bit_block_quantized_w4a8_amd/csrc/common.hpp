@@ -29,11 +29,14 @@ int hip_fail(hipError_t e, const char* what);
     if (e_ != hipSuccess) return ::w4a8::hip_fail(e_, #call); \
   } while (0)
 
-// Library scratch of the current device.
+// Scratch memory of the kernels: the library's own per-device buffers
+// (w4a8_init, w4a8_reserve_scratch) or a view over another region of device
+// memory.  No launcher allocates: each checks that `work` is large enough.
 struct Scratch {
   void* base = nullptr;
   size_t bytes = 0;
-  uint32_t* tickets = nullptr;       // split-K / argmax completion counters, self-resetting
+  uint32_t* tickets = nullptr;       // split-K / attention completion counters, self-resetting
+  int n_tickets = 0;
   unsigned long long* slots = nullptr;  // argmax keys [kMaxArgmaxRows][kArgmaxSpread], reset by the finaliser
   void* work = nullptr;              // staging: quantised activations, split-K partials
   size_t work_bytes = 0;
@@ -43,7 +46,11 @@ constexpr int kMaxArgmaxRows = 64;
 // Argmax keys of one row are spread over this many slots (tile % spread), so
 // the per-workgroup atomic maxima of a launch do not all meet on one address.
 constexpr int kArgmaxSpread = 64;
-int scratch_for(size_t work_bytes, Scratch** out);  // grows `work` if needed
+// The library scratch of the current device (W4A8_ENOINIT before w4a8_init).
+int library_scratch(Scratch** out);
+// W4A8_EINVAL, with a message naming the bytes needed, if sc's work area is
+// smaller than work_bytes.
+int require_scratch(const Scratch* sc, size_t work_bytes);
 
 // ------------------------------------------------------------- device side
 __device__ __forceinline__ float half_bits_to_float(uint32_t h) {
@@ -131,6 +138,34 @@ __device__ __forceinline__ void quantize_to_staging(const float* v, int64_t m, i
   const int64_t row_slot = ((m >> 5) * 2 + (g & 1)) * 32 + (m & 31);
   *reinterpret_cast<uint2*>(qxs + b * m_pad * kBlock + row_slot * 16 + 8 * (g >> 1)) = codes;
   if (g == 0) sxs[b * m_pad + m] = scale;
+}
+
+// fp16 bits of fp16(fp32(a * b)): the product is rounded to fp32 first, then
+// to fp16.  The product is made opaque to the optimiser because the backend
+// otherwise folds the multiply and the conversion into one mixed-precision
+// instruction (v_fma_mixlo_f16) that rounds the exact product to fp16 once;
+// near an fp16 rounding midpoint the two differ by one fp16 unit.
+__device__ __forceinline__ uint16_t half_of_product(float a, float b) {
+  float p = a * b;
+  asm("" : "+v"(p));
+  return float_to_half_bits(p);
+}
+
+// 1 / sqrt(mean(x^2) + eps) of a row of H fp32 values, from the row's sum of
+// squares ss formed in fp64.  Each square of an fp32 value is exact in fp64
+// and a sum of H of them, in any order, is within H * 2^-53 of the exact sum
+// (relative; 2^-42 for H = 2048).  Kernels that add the squares in different
+// orders (the normalising GEMV prologue, the glue kernels) therefore get the
+// same fp32 result unless the exact value lies that close to an fp32
+// rounding boundary (2^-23 apart), and the fp16 inputs they hand to a linear
+// agree bit for bit.
+__device__ __forceinline__ float rms_inverse(double ss, int H, float eps) {
+  return static_cast<float>(1.0 / sqrt(ss / static_cast<double>(H) + static_cast<double>(eps)));
+}
+// Square of an fp32 value added to an fp64 sum (the square is exact).
+__device__ __forceinline__ double add_square(double acc, float v) {
+  const double d = static_cast<double>(v);
+  return fma(d, d, acc);
 }
 
 // The eight fp16 values of a 16-byte load, widened to fp32 (exact).

@@ -410,7 +410,7 @@ void gemm_kernel(
         float v[16];
 #pragma unroll
         for (int r = 0; r < 16; ++r)
-          v[r] = m < M ? half_bits_to_float(float_to_half_bits(acc[0][j][r] * xch[r * 64 + lane])) : 0.0f;
+          v[r] = m < M ? half_bits_to_float(half_of_product(acc[0][j][r], xch[r * 64 + lane])) : 0.0f;
         quantize_pair_to_staging(v, m, h, bo, m_pad_out, qout, sout);
       }
     }
@@ -625,13 +625,14 @@ float* gemm_partials(void* work, const GemmStaging& s, int K) {
                                   align256(nb * s.m_pad * sizeof(float)));
 }
 
-int launch_gemm_kernel(const GemmArgs& a, int mode, const GemmStaging& s, hipStream_t stream) {
+int launch_gemm_kernel(const GemmArgs& a, int mode, const GemmStaging& s, Scratch* sc, hipStream_t stream) {
   const Plan p = plan_gemm(a.M, a.K, a.N);
   if (p.tiles_n * p.tiles_m >= kMaxTickets - 1) return hip_fail(hipErrorInvalidValue, "gemm: too many tiles");
   if (s.m_pad != p.m_pad) return hip_fail(hipErrorInvalidValue, "gemm: staging of another shape");
-  Scratch* sc = nullptr;
-  int rc = scratch_for(gemm_scratch_bytes(a.M, a.K, a.N), &sc);
+  int rc = require_scratch(sc, gemm_scratch_bytes(a.M, a.K, a.N));
   if (rc != W4A8_OK) return rc;
+  if (p.ksplit > 1 && p.tiles_n * p.tiles_m + 1 > sc->n_tickets)
+    return hip_fail(hipErrorInvalidValue, "gemm: more split tiles than tickets");
   const uint8_t* qxs = s.qxs;
   const float* sxs = s.sxs;
   float* partials = gemm_partials(sc->work, s, a.K);
@@ -676,10 +677,9 @@ int launch_gemm_kernel(const GemmArgs& a, int mode, const GemmStaging& s, hipStr
 
 }  // namespace
 
-int gemm_staging(int M, int K, int N, GemmStaging* s) {
+int gemm_staging(int M, int K, int N, Scratch* sc, GemmStaging* s) {
   const Plan p = plan_gemm(M, K, N);
-  Scratch* sc = nullptr;
-  const int rc = scratch_for(gemm_scratch_bytes(M, K, N), &sc);
+  const int rc = require_scratch(sc, gemm_scratch_bytes(M, K, N));
   if (rc != W4A8_OK) return rc;
   const size_t nb = K / kBlock;
   uint8_t* base = static_cast<uint8_t*>(sc->work);
@@ -689,39 +689,40 @@ int gemm_staging(int M, int K, int N, GemmStaging* s) {
   return W4A8_OK;
 }
 
-int launch_gemm(const GemmArgs& a, int mode, hipStream_t stream) {
+int launch_gemm(const GemmArgs& a, int mode, Scratch* sc, hipStream_t stream) {
   GemmStaging s{};
-  int rc = gemm_staging(a.M, a.K, a.N, &s);
+  int rc = gemm_staging(a.M, a.K, a.N, sc, &s);
   if (rc != W4A8_OK) return rc;
   rc = launch_quantize_stage(a.x, a.M, s.m_pad, a.K, s.qxs, s.sxs, stream);
   if (rc != W4A8_OK) return rc;
-  return launch_gemm_kernel(a, mode, s, stream);
+  return launch_gemm_kernel(a, mode, s, sc, stream);
 }
 
-int launch_gemm_staged(const GemmArgs& a, const GemmStaging& s, hipStream_t stream) {
-  return launch_gemm_kernel(a, 0, s, stream);
+int launch_gemm_staged(const GemmArgs& a, const GemmStaging& s, Scratch* sc, hipStream_t stream) {
+  return launch_gemm_kernel(a, 0, s, sc, stream);
 }
 
-int launch_gemm_staged_resid(const GemmArgs& a, const GemmStaging& s, hipStream_t stream) {
-  return launch_gemm_kernel(a, 2, s, stream);
+int launch_gemm_staged_resid(const GemmArgs& a, const GemmStaging& s, Scratch* sc, hipStream_t stream) {
+  return launch_gemm_kernel(a, 2, s, sc, stream);
 }
 
 int launch_gemm_staged_cast(const GemmArgs& a, int n_cast, const GemmStaging& s, const GemmStaging& out,
-                            hipStream_t stream) {
+                            Scratch* sc, hipStream_t stream) {
   GemmArgs g = a;
   g.q_out = out.qxs;
   g.s_out = out.sxs;
   g.m_pad_out = out.m_pad;
   g.n_cast = n_cast;
-  return launch_gemm_kernel(g, 4, s, stream);
+  return launch_gemm_kernel(g, 4, s, sc, stream);
 }
 
-int launch_gemm_staged_gated(const GemmArgs& a, const GemmStaging& s, const GemmStaging& out, hipStream_t stream) {
+int launch_gemm_staged_gated(const GemmArgs& a, const GemmStaging& s, const GemmStaging& out, Scratch* sc,
+                             hipStream_t stream) {
   GemmArgs g = a;
   g.q_out = out.qxs;
   g.s_out = out.sxs;
   g.m_pad_out = out.m_pad;
-  return launch_gemm_kernel(g, 3, s, stream);
+  return launch_gemm_kernel(g, 3, s, sc, stream);
 }
 
 }  // namespace w4a8

@@ -89,10 +89,10 @@ bool gemv_fused_supported(int mode, bool norm, int K, int N) {
   return gemv_detail::chunk_blocks(gemv_detail::pick_plan(K, N, true)) >= K / kBlock;
 }
 
-int launch_gemv(const GemvArgs& a, int mode, hipStream_t stream) {
-  Scratch* sc = nullptr;
-  int rc = scratch_for(0, &sc);
-  if (rc != W4A8_OK) return rc;
+int launch_gemv(const GemvArgs& a, int mode, Scratch* sc, hipStream_t stream) {
+  int rc = W4A8_OK;
+  if (mode == kGemvArgmax && (!sc->slots || a.M > kMaxArgmaxRows))
+    return hip_fail(hipErrorInvalidValue, "gemv: argmax needs the library's argmax slots");
   if (mode >= kGemvCast || a.xf) {
     // Fused decoder-layer kernels: one token row.
     if (a.M != 1 || !gemv_fused_supported(mode, a.xf != nullptr, a.K, a.N))

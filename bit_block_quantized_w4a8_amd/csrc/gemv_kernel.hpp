@@ -87,6 +87,22 @@ __device__ __forceinline__ float row_sum(float v) {
   return v;
 }
 
+// row_sum<1> on fp64 values: the same DPP pattern on both halves.
+template <int kCtrl>
+__device__ __forceinline__ double dpp_move_f64(double v) {
+  const uint64_t b = __builtin_bit_cast(uint64_t, v);
+  const uint32_t lo = __builtin_amdgcn_mov_dpp(static_cast<int>(static_cast<uint32_t>(b)), kCtrl, 0xF, 0xF, true);
+  const uint32_t hi = __builtin_amdgcn_mov_dpp(static_cast<int>(static_cast<uint32_t>(b >> 32)), kCtrl, 0xF, 0xF, true);
+  return __builtin_bit_cast(double, (static_cast<uint64_t>(hi) << 32) | lo);
+}
+__device__ __forceinline__ double row_sum_f64(double v) {
+  v += dpp_move_f64<0xB1>(v);
+  v += dpp_move_f64<0x4E>(v);
+  v += dpp_move_f64<0x124>(v);
+  v += dpp_move_f64<0x128>(v);
+  return v;
+}
+
 // Output column of lane column c in tile `tile`.
 template <int MODE, int C>
 __device__ __forceinline__ int column_of(int tile, int c, int N) {
@@ -132,7 +148,7 @@ __global__ __launch_bounds__(T) void gemv_kernel(GemvArgs a, uint32_t* __restric
   __shared__ uint32_t q_lds[MR][kChunkBlocks][8];  // int8 codes, 8 dwords per block
   __shared__ float s_lds[MR][kChunkBlocks];         // sx / 16 per block
   __shared__ float red[kWaves][MR][kParts][C];
-  __shared__ float red_ss[NORM ? kWaves : 1][MR][4];
+  __shared__ double red_ss[NORM ? kWaves : 1][MR][4];
 
   const uint16_t* __restrict__ x = a.x;
   const uint8_t* __restrict__ pw = a.packed_w;
@@ -228,24 +244,24 @@ __global__ __launch_bounds__(T) void gemv_kernel(GemvArgs a, uint32_t* __restric
       }
     };
     if constexpr (NORM) {
-      // Sum of squares of each row (one chunk holds the whole row), in a fixed
-      // order: per lane, then across the wave, then the four waves.
-      float ss[MR];
+      // Sum of squares of each row (one chunk holds the whole row) in fp64:
+      // per lane, then across the wave, then the waves (rms_inverse).
+      double ss[MR];
 #pragma unroll
-      for (int m = 0; m < MR; ++m) ss[m] = 0.0f;
+      for (int m = 0; m < MR; ++m) ss[m] = 0.0;
 #pragma unroll
       for (int j = 0; j < XQ; ++j) {
         const int g = j * T + tid;
         if (g < tasks) {
           const int m = task_row<MR>(g, nbc);
-          float q = xa[j].x * xa[j].x;
-          q = fmaf(xa[j].y, xa[j].y, q);
-          q = fmaf(xa[j].z, xa[j].z, q);
-          q = fmaf(xa[j].w, xa[j].w, q);
-          q = fmaf(xb[j].x, xb[j].x, q);
-          q = fmaf(xb[j].y, xb[j].y, q);
-          q = fmaf(xb[j].z, xb[j].z, q);
-          q = fmaf(xb[j].w, xb[j].w, q);
+          double q = add_square(0.0, xa[j].x);
+          q = add_square(q, xa[j].y);
+          q = add_square(q, xa[j].z);
+          q = add_square(q, xa[j].w);
+          q = add_square(q, xb[j].x);
+          q = add_square(q, xb[j].y);
+          q = add_square(q, xb[j].z);
+          q = add_square(q, xb[j].w);
 #pragma unroll
           for (int mm = 0; mm < MR; ++mm)
             if (m == mm) ss[mm] += q;
@@ -253,19 +269,19 @@ __global__ __launch_bounds__(T) void gemv_kernel(GemvArgs a, uint32_t* __restric
       }
 #pragma unroll
       for (int m = 0; m < MR; ++m) {
-        const float rs = row_sum<1>(ss[m]);
+        const double rs = row_sum_f64(ss[m]);
         if ((lane & 15) == 0) red_ss[wave][m][lane >> 4] = rs;
       }
       __syncthreads();
       float inv[MR];
 #pragma unroll
       for (int m = 0; m < MR; ++m) {
-        float t = 0.0f;
+        double t = 0.0;
 #pragma unroll
         for (int wv = 0; wv < kWaves; ++wv)
 #pragma unroll
           for (int r = 0; r < 4; ++r) t += red_ss[wv][m][r];
-        inv[m] = 1.0f / sqrtf(t / static_cast<float>(K) + a.eps);
+        inv[m] = rms_inverse(t, K, a.eps);
       }
 #pragma unroll
       for (int j = 0; j < XQ; ++j) {
@@ -279,7 +295,7 @@ __global__ __launch_bounds__(T) void gemv_kernel(GemvArgs a, uint32_t* __restric
           const float raw[8] = {xa[j].x, xa[j].y, xa[j].z, xa[j].w, xb[j].x, xb[j].y, xb[j].z, xb[j].w};
           float v[8];
 #pragma unroll
-          for (int k = 0; k < 8; ++k) v[k] = half_bits_to_float(float_to_half_bits(raw[k] * im));
+          for (int k = 0; k < 8; ++k) v[k] = half_bits_to_float(half_of_product(raw[k], im));
           store_codes(g, v);
         }
       }
@@ -413,7 +429,10 @@ __global__ __launch_bounds__(T) void gemv_kernel(GemvArgs a, uint32_t* __restric
     if (lane < C) {
 #pragma unroll
       for (int m = 0; m < MR; ++m) {
-        if (m < M) a.resid[static_cast<int64_t>(m) * N + n] = fmaf(a.alpha, v[m], resid_in[m]);
+        if (m < M) {
+          a.resid[static_cast<int64_t>(m) * N + n] = fmaf(a.alpha, v[m], resid_in[m]);
+          if (a.out) a.out[static_cast<int64_t>(m) * N + n] = v[m];  // the projection's own output
+        }
       }
     }
     return;
@@ -423,8 +442,9 @@ __global__ __launch_bounds__(T) void gemv_kernel(GemvArgs a, uint32_t* __restric
 #pragma unroll
     for (int m = 0; m < MR; ++m) {
       const float up = __shfl(v[m], (lane + kHalf) & 63);  // lane < C/2: its up column
+      if (a.out && lane < C && m < M) a.out[static_cast<int64_t>(m) * N + n] = v[m];  // gate and up values
       if (lane < kHalf && m < M)
-        a.y16[static_cast<int64_t>(m) * (N / 2) + n] = float_to_half_bits(v[m] * up);
+        a.y16[static_cast<int64_t>(m) * (N / 2) + n] = half_of_product(v[m], up);
     }
     return;
   }

@@ -41,7 +41,7 @@ struct GemvArgs {
   uint16_t* y16 = nullptr;    // kGemvCast: [M][n16]; kGemvGated: [M][N/2]
   int n16 = 0;
 };
-int launch_gemv(const GemvArgs& a, int mode, hipStream_t stream);
+int launch_gemv(const GemvArgs& a, int mode, Scratch* sc, hipStream_t stream);
 // Whether a fused (one-row) GEMV launch supports the shape: the normalising
 // prologue needs the whole row of K in one chunk.
 bool gemv_fused_supported(int mode, bool norm, int K, int N);
@@ -63,23 +63,23 @@ struct GemmArgs {
   int m_pad_out = 0;
   int n_cast = 0;  // cast epilogue: leading columns quantised into the staging
 };
-int launch_gemm(const GemmArgs& a, int mode, hipStream_t stream);
+int launch_gemm(const GemmArgs& a, int mode, Scratch* sc, hipStream_t stream);
 size_t gemm_scratch_bytes(int M, int K, int N);
 // Staging of one GEMM launch in library scratch (the pre-pass's output):
 // codes and scales of M_pad rows (rows M .. M_pad-1 zero) for an M x K by K x N
-// product.  gemm_staging grows the scratch if needed, so it is called before
-// anything is written into the staging.
+// product.  gemm_staging checks that sc holds it (with room for split-K
+// partials after it).
 struct GemmStaging {
   uint8_t* qxs;
   float* sxs;
   int m_pad;
 };
-int gemm_staging(int M, int K, int N, GemmStaging* s);
+int gemm_staging(int M, int K, int N, Scratch* sc, GemmStaging* s);
 // The GEMM (scaled output) on activations already quantised into `s`.
-int launch_gemm_staged(const GemmArgs& a, const GemmStaging& s, hipStream_t stream);
+int launch_gemm_staged(const GemmArgs& a, const GemmStaging& s, Scratch* sc, hipStream_t stream);
 // The same, adding alpha times the result into a.resid (fp32 [M][N]) instead
 // of writing a.out: one fma per element, as a separate residual add would.
-int launch_gemm_staged_resid(const GemmArgs& a, const GemmStaging& s, hipStream_t stream);
+int launch_gemm_staged_resid(const GemmArgs& a, const GemmStaging& s, Scratch* sc, hipStream_t stream);
 // Staging in caller memory (gemm_staging_bytes(M, K, N) bytes, 256-byte
 // aligned) for a GEMM of that shape.
 size_t gemm_staging_bytes(int M, int K, int N);
@@ -98,8 +98,9 @@ bool gemm_gated_supported(int M, int K, int N, int m_pad_out);
 // GEMM's tile rows (its m_pad).
 bool gemm_cast_supported(int M, int K, int N, int n_cast, int m_pad_out);
 int launch_gemm_staged_cast(const GemmArgs& a, int n_cast, const GemmStaging& s, const GemmStaging& out,
-                            hipStream_t stream);
-int launch_gemm_staged_gated(const GemmArgs& a, const GemmStaging& s, const GemmStaging& out, hipStream_t stream);
+                            Scratch* sc, hipStream_t stream);
+int launch_gemm_staged_gated(const GemmArgs& a, const GemmStaging& s, const GemmStaging& out, Scratch* sc,
+                             hipStream_t stream);
 
 // MX variant (mx.hip): MXFP4 weights x MXFP8 activations on the block-scaled
 // matrix instruction.
@@ -109,7 +110,7 @@ int launch_mx_quantize_act(const uint16_t* x, int M, int M_pad, int K, uint8_t* 
                            hipStream_t stream);
 int launch_mx_pack(const uint16_t* w, int K, int N, uint8_t* packed, uint8_t* scales, hipStream_t stream);
 int launch_mx_linear(const uint16_t* x, const uint8_t* packed, const uint8_t* wscales, int M, int K, int N,
-                     float* out, hipStream_t stream);
+                     float* out, Scratch* sc, hipStream_t stream);
 
 // Decode attention over an fp16 KV cache (attention.hip).
 int attention_chunks(int length);

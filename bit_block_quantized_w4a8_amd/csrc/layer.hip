@@ -26,14 +26,15 @@ constexpr int kGlueThreads = 256;
 // between the sum of squares and the quantisation.
 constexpr int kRegGroups = 2;
 
-// Fixed-order workgroup sum: wave shuffles, then the 4 wave totals in order.
-__device__ __forceinline__ float block_sum(float v, float* red) {
+// Fixed-order workgroup sum of fp64 partial sums of squares: wave shuffles,
+// then the 4 wave totals in order.
+__device__ __forceinline__ double block_sum(double v, double* red) {
 #pragma unroll
   for (int off = 32; off >= 1; off >>= 1) v += __shfl_xor(v, off);
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
   if (lane == 0) red[wave] = v;
   __syncthreads();
-  const float t = ((red[0] + red[1]) + red[2]) + red[3];
+  const double t = ((red[0] + red[1]) + red[2]) + red[3];
   __syncthreads();
   return t;
 }
@@ -43,21 +44,21 @@ __device__ __forceinline__ float block_sum(float v, float* red) {
 __global__ __launch_bounds__(kGlueThreads) void residual_norm_cast_kernel(
     float* __restrict__ x, const float* __restrict__ d, int64_t ld_d, float alpha, float eps, int H,
     uint16_t* __restrict__ y) {
-  __shared__ float red[4];
+  __shared__ double red[4];
   const int64_t m = blockIdx.x;
   float* xr = x + m * H;
-  float ss = 0.0f;
+  double ss = 0.0;
   for (int h = threadIdx.x; h < H; h += kGlueThreads) {
     float v = xr[h];
     if (d) {
       v = fmaf(alpha, d[m * ld_d + h], v);
       xr[h] = v;
     }
-    ss = fmaf(v, v, ss);
+    ss = add_square(ss, v);
   }
-  const float inv = 1.0f / sqrtf(block_sum(ss, red) / static_cast<float>(H) + eps);
+  const float inv = rms_inverse(block_sum(ss, red), H, eps);
   if (y)
-    for (int h = threadIdx.x; h < H; h += kGlueThreads) y[m * H + h] = float_to_half_bits(xr[h] * inv);
+    for (int h = threadIdx.x; h < H; h += kGlueThreads) y[m * H + h] = half_of_product(xr[h], inv);
 }
 
 // x += alpha * d with no normalised output: elementwise, four floats per
@@ -93,7 +94,7 @@ __global__ __launch_bounds__(kGlueThreads) void gated_cast_kernel(const float* _
   if (f >= F) return;
   for (int64_t m = blockIdx.y; m < M; m += gridDim.y) {
     const float* row = g + m * 2 * static_cast<int64_t>(F);
-    u[m * F + f] = float_to_half_bits(row[f] * row[F + f]);
+    u[m * F + f] = half_of_product(row[f], row[F + f]);
   }
 }
 
@@ -109,7 +110,7 @@ __global__ __launch_bounds__(kGlueThreads) void gated_cast_kernel(const float* _
 __global__ __launch_bounds__(kGlueThreads) void residual_norm_quant_kernel(
     float* __restrict__ x, const float* __restrict__ d, int64_t ld_d, float alpha, float eps, int M, int H,
     int m_pad, uint8_t* __restrict__ qxs, float* __restrict__ sxs) {
-  __shared__ float red[4];
+  __shared__ double red[4];
   const int64_t m = blockIdx.x;
   const int groups = H / 8;
   if (m >= M) {  // padding row (uniform)
@@ -118,7 +119,7 @@ __global__ __launch_bounds__(kGlueThreads) void residual_norm_quant_kernel(
     return;
   }
   float* xr = x + m * H;
-  float ss = 0.0f;
+  double ss = 0.0;
   if (groups <= kRegGroups * kGlueThreads) {  // uniform: the row stays in registers
     float4 lo[kRegGroups], hi[kRegGroups];
 #pragma unroll
@@ -137,13 +138,13 @@ __global__ __launch_bounds__(kGlueThreads) void residual_norm_quant_kernel(
           *reinterpret_cast<float4*>(xr + 8 * e) = lo[i];
           *reinterpret_cast<float4*>(xr + 8 * e + 4) = hi[i];
         }
-        ss = fmaf(lo[i].x, lo[i].x, ss); ss = fmaf(lo[i].y, lo[i].y, ss);
-        ss = fmaf(lo[i].z, lo[i].z, ss); ss = fmaf(lo[i].w, lo[i].w, ss);
-        ss = fmaf(hi[i].x, hi[i].x, ss); ss = fmaf(hi[i].y, hi[i].y, ss);
-        ss = fmaf(hi[i].z, hi[i].z, ss); ss = fmaf(hi[i].w, hi[i].w, ss);
+        ss = add_square(ss, lo[i].x); ss = add_square(ss, lo[i].y);
+        ss = add_square(ss, lo[i].z); ss = add_square(ss, lo[i].w);
+        ss = add_square(ss, hi[i].x); ss = add_square(ss, hi[i].y);
+        ss = add_square(ss, hi[i].z); ss = add_square(ss, hi[i].w);
       }
     }
-    const float inv = 1.0f / sqrtf(block_sum(ss, red) / static_cast<float>(H) + eps);
+    const float inv = rms_inverse(block_sum(ss, red), H, eps);
 #pragma unroll
     for (int i = 0; i < kRegGroups; ++i) {
       const int e = threadIdx.x + i * kGlueThreads;
@@ -151,7 +152,7 @@ __global__ __launch_bounds__(kGlueThreads) void residual_norm_quant_kernel(
         const float raw[8] = {lo[i].x, lo[i].y, lo[i].z, lo[i].w, hi[i].x, hi[i].y, hi[i].z, hi[i].w};
         float v[8];
 #pragma unroll
-        for (int k = 0; k < 8; ++k) v[k] = half_bits_to_float(float_to_half_bits(raw[k] * inv));
+        for (int k = 0; k < 8; ++k) v[k] = half_bits_to_float(half_of_product(raw[k], inv));
         quantize_to_staging(v, m, e, m_pad, qxs, sxs);
       }
     }
@@ -169,10 +170,10 @@ __global__ __launch_bounds__(kGlueThreads) void residual_norm_quant_kernel(
       *reinterpret_cast<float4*>(xr + 8 * e) = lo;
       *reinterpret_cast<float4*>(xr + 8 * e + 4) = hi;
     }
-    ss = fmaf(lo.x, lo.x, ss); ss = fmaf(lo.y, lo.y, ss); ss = fmaf(lo.z, lo.z, ss); ss = fmaf(lo.w, lo.w, ss);
-    ss = fmaf(hi.x, hi.x, ss); ss = fmaf(hi.y, hi.y, ss); ss = fmaf(hi.z, hi.z, ss); ss = fmaf(hi.w, hi.w, ss);
+    ss = add_square(ss, lo.x); ss = add_square(ss, lo.y); ss = add_square(ss, lo.z); ss = add_square(ss, lo.w);
+    ss = add_square(ss, hi.x); ss = add_square(ss, hi.y); ss = add_square(ss, hi.z); ss = add_square(ss, hi.w);
   }
-  const float inv = 1.0f / sqrtf(block_sum(ss, red) / static_cast<float>(H) + eps);
+  const float inv = rms_inverse(block_sum(ss, red), H, eps);
   // Each thread re-reads only the elements it wrote above.
   for (int e = threadIdx.x; e < groups; e += kGlueThreads) {
     const float4 lo = *reinterpret_cast<const float4*>(xr + 8 * e);
@@ -180,7 +181,7 @@ __global__ __launch_bounds__(kGlueThreads) void residual_norm_quant_kernel(
     const float raw[8] = {lo.x, lo.y, lo.z, lo.w, hi.x, hi.y, hi.z, hi.w};
     float v[8];
 #pragma unroll
-    for (int k = 0; k < 8; ++k) v[k] = half_bits_to_float(float_to_half_bits(raw[k] * inv));
+    for (int k = 0; k < 8; ++k) v[k] = half_bits_to_float(half_of_product(raw[k], inv));
     quantize_to_staging(v, m, e, m_pad, qxs, sxs);
   }
 }
@@ -220,10 +221,10 @@ __global__ __launch_bounds__(kGlueThreads) void gated_quant_kernel(const float* 
       const float4 g1 = *reinterpret_cast<const float4*>(row + 4);
       const float4 u0 = *reinterpret_cast<const float4*>(row + F);
       const float4 u1 = *reinterpret_cast<const float4*>(row + F + 4);
-      const float raw[8] = {g0.x * u0.x, g0.y * u0.y, g0.z * u0.z, g0.w * u0.w,
-                            g1.x * u1.x, g1.y * u1.y, g1.z * u1.z, g1.w * u1.w};
+      const float gv[8] = {g0.x, g0.y, g0.z, g0.w, g1.x, g1.y, g1.z, g1.w};
+      const float uv[8] = {u0.x, u0.y, u0.z, u0.w, u1.x, u1.y, u1.z, u1.w};
 #pragma unroll
-      for (int k = 0; k < 8; ++k) v[k] = half_bits_to_float(float_to_half_bits(raw[k]));
+      for (int k = 0; k < 8; ++k) v[k] = half_bits_to_float(half_of_product(gv[k], uv[k]));
     }
     quantize_to_staging(v, m, e, m_pad, qxs, sxs);
   }

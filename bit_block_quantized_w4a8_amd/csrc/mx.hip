@@ -465,10 +465,9 @@ int launch_mx_pack(const uint16_t* w, int K, int N, uint8_t* packed, uint8_t* sc
 }
 
 int launch_mx_linear(const uint16_t* x, const uint8_t* packed, const uint8_t* wscales, int M, int K, int N,
-                     float* out, hipStream_t stream) {
+                     float* out, Scratch* sc, hipStream_t stream) {
   const int m_pad = mx_m_pad(M);
-  Scratch* sc = nullptr;
-  int rc = scratch_for(mx_scratch_bytes(M, K), &sc);
+  int rc = require_scratch(sc, mx_scratch_bytes(M, K));
   if (rc != W4A8_OK) return rc;
   uint8_t* codes = static_cast<uint8_t*>(sc->work);
   uint8_t* ascale = codes + align256(static_cast<size_t>(m_pad) * K);

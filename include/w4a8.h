@@ -20,9 +20,12 @@
  * Conventions for every entry point:
  *   - tensor pointers are HIP device pointers to row-major, contiguous data;
  *     fp16 tensors are passed as uint16_t bit patterns;
- *   - the caller owns every tensor; the library owns only the scratch memory it
- *     allocates in w4a8_init (per device) and grows when a larger problem
- *     arrives (growth synchronises the device, so warm up before timing);
+ *   - the caller owns every tensor; the library owns only its scratch memory
+ *     (per device): w4a8_init reserves 64 MiB of it, and only
+ *     w4a8_reserve_scratch adds more.  No other call allocates, frees or
+ *     synchronises: a call that needs more scratch than is reserved fails
+ *     with W4A8_EINVAL before launching anything, and the *_scratch_bytes
+ *     queries below give the size each call needs;
  *   - calls are asynchronous on `stream` (0 = the null stream); none
  *     synchronises and none returns results on the host, except as noted;
  *   - calls that share a device share its scratch and its argmax slots:
@@ -65,10 +68,40 @@ extern "C" {
 
 /*
  * Select `device`, check that it is gfx950 and allocate the library's scratch
- * (quantised-activation staging, split-K partials, completion tickets, argmax
- * slots).  Idempotent per device.  Returns W4A8_EUNSUPPORTED on other GPUs.
+ * (completion tickets, argmax slots, and a 64 MiB work area for
+ * quantised-activation staging and split-K partials).  Idempotent per device.
+ * Synchronises the device.  Returns W4A8_EUNSUPPORTED on other GPUs.
  */
 W4A8_API int w4a8_init(int device);
+
+/*
+ * Make the current device's scratch work area at least `bytes` long
+ * (hipMalloc; rounded up to 1 MiB).  The area it replaces is kept, never
+ * freed, because a HIP graph captured while it was in use still reads and
+ * writes it; so reserve the largest size once, before capturing or timing.
+ * Not for use while kernels of this library run on another stream.
+ * W4A8_ENOINIT before w4a8_init; W4A8_EHIP when the allocation fails.
+ */
+W4A8_API int w4a8_reserve_scratch(size_t bytes);
+
+/* Bytes in the current device's scratch work area (after w4a8_init). */
+W4A8_API int w4a8_scratch_capacity(size_t* bytes);
+
+/*
+ * Scratch each call needs, host-only (no device, no w4a8_init): the bytes of
+ * work area that w4a8_linear_path (and w4a8_block_sums with the same path),
+ * w4a8_decoder_layer, w4a8_norm_linear_argmax, w4a8_mx_linear and
+ * w4a8_decode_attention need for these shapes.  Shapes are validated as the
+ * calls validate them (W4A8_EINVAL).  The decode GEMV paths need 0.
+ */
+W4A8_API int w4a8_linear_scratch_bytes(int64_t M, int64_t K, int64_t N, int path, size_t* bytes);
+struct w4a8_weights;
+W4A8_API int w4a8_decoder_layer_scratch_bytes(int64_t M, int64_t H, const struct w4a8_weights* qkv,
+                                              const struct w4a8_weights* gate_up, size_t* bytes);
+W4A8_API int w4a8_norm_linear_argmax_scratch_bytes(int64_t M, int64_t K, int64_t N, size_t* bytes);
+W4A8_API int w4a8_mx_linear_scratch_bytes(int64_t M, int64_t K, int64_t N, size_t* bytes);
+W4A8_API int w4a8_decode_attention_scratch_bytes(int64_t n_heads, int64_t n_kv_heads, int64_t head_dim,
+                                                 int64_t length, size_t* bytes);
 
 /*
  * Pack int4 weights into the K-block-major layout read by every kernel
@@ -139,17 +172,20 @@ W4A8_API int w4a8_block_sums(const uint16_t* x, const uint8_t* packed_w, int64_t
  * ------------------------------------------------------------------------ */
 
 /* One packed weight matrix as produced by w4a8_pack_weights (device pointers). */
-typedef struct w4a8_weights {
+struct w4a8_weights {
   const uint8_t* packed_w;   /* uint8 [K/32][N][16], 16-byte aligned */
   const uint16_t* w_scales;  /* fp16  [K/32][N], 16-byte aligned */
   int64_t K;
   int64_t N;
-} w4a8_weights;
+};
+typedef struct w4a8_weights w4a8_weights;
 
 /*
  * Per row m of x (fp32 [M][H]): if d is not NULL, x[m][h] = RN(x[m][h] + alpha *
  * d[m * ld_d + h]) (one fused multiply-add); then, if y is not NULL,
- * y[m][h] = fp16(x[m][h] * (1 / sqrt(mean_h x[m][h]^2 + eps))) (fp32 arithmetic).
+ * y[m][h] = fp16(x[m][h] * r) with r = fp32(1 / sqrt(mean_h x[m][h]^2 + eps))
+ * and the sum of squares formed in fp64: the same fp16 values every
+ * normalising kernel of this library forms from that row.
  * H >= 1; y fp16 [M][H].
  */
 W4A8_API int w4a8_residual_norm_cast(float* x, const float* d, int64_t ld_d, float alpha, float eps,
@@ -160,21 +196,35 @@ W4A8_API int w4a8_decoder_layer_workspace(int64_t M, int64_t H, const w4a8_weigh
                                           const w4a8_weights* gate_up, size_t* bytes);
 
 /*
+ * Byte offsets in that workspace of the layer's intermediates, in this order:
+ *   q fp32 [M][qkv.N], a fp16 [M][H], o fp32 [M][H], n fp16 [M][H],
+ *   g fp32 [M][2F], u fp16 [M][F], d fp32 [M][H].
+ * When every projection of the call runs the decode GEMV (M = 1 among them),
+ * the call leaves q, a = fp16(q[:, :H]), o = L(a; o), g = L(n2; gate_up),
+ * u and d = L(u; down) there (n only on the nine-launch path), so each
+ * projection can be checked on its own inputs.  The prefill path keeps
+ * quantised GEMM staging in a and g and writes none of o, n, u, d.
+ */
+W4A8_API int w4a8_decoder_layer_workspace_offsets(int64_t M, int64_t H, const w4a8_weights* qkv,
+                                                  const w4a8_weights* gate_up, size_t offsets[7]);
+
+/*
  * One decoder layer (wiring above), in place on x (fp32 [M][H], 16-byte aligned).
  * Shapes: qkv.K = H <= qkv.N; o.K = o.N = H; gate_up.K = H; gate_up.N = 2 * down.K;
  * down.N = H; H % 64 == 0.  workspace: device memory of at least
  * w4a8_decoder_layer_workspace bytes, 256-byte aligned, owned by the caller and
  * not touched by other calls in flight.  Allocates nothing (the linears use the
- * library scratch as w4a8_linear does), so a warmed-up call can be captured in
- * a HIP graph.  M must not exceed 65536.
+ * library scratch as w4a8_linear does: w4a8_decoder_layer_scratch_bytes), so
+ * the call can be captured in a HIP graph.  M must not exceed 65536.
  * With M = 1, when the GEMV tiles of qkv and gate/up cover all of K = H in one
  * chunk (H <= 2048 for N >= 32768, H <= 4096 for N >= 16384, H <= 8192
  * otherwise), the layer runs as four GEMV launches: the normalisation sits in the prologue of qkv and
  * gate/up, the fp16 cast of q[:, :H], the residual adds and the gated product
  * in the epilogues (the pages fold such element-wise work into neighbouring
- * operators: sciencestack summary of the ML Drift paper, Figure 4).  The
- * result equals the nine-launch chain up to the summation order inside
- * rms(x); q is still written to the workspace.
+ * operators: sciencestack summary of the ML Drift paper, Figure 4).  Every
+ * normalisation sums its squares in fp64, so the fused prologue and the glue
+ * kernel form the same fp16 inputs and the result equals the nine-launch
+ * chain; q, o, g and d are still written to the workspace.
  * When every projection runs the prefill GEMM, the layer is six launches: the
  * two normalisations quantise straight into GEMM staging; the qkv GEMM
  * quantises fp16(q[:, :H]) into the o projection's staging (its other columns

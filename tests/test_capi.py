@@ -14,7 +14,7 @@ def lib():
 
 def test_exports_every_declared_symbol(lib):
     names = w4.declared_functions()
-    assert len(names) == 18, names
+    assert len(names) == 26, names
     for name in names:
         assert hasattr(lib, name), name
 
@@ -134,3 +134,33 @@ def test_decode_attention_validates(lib):
     assert call(length=641) == w4.W4A8_EINVAL
     assert call() == w4.W4A8_ENOINIT
     assert call(hq=16, hkv=2, d=64, length=1, cap=64) == w4.W4A8_ENOINIT
+
+
+def test_scratch_sizes_on_the_host(lib):
+    """The sizing queries need no device: the decode GEMV needs no scratch, the prefill
+    GEMM its staging (codes and fp32 scales of every 32-row padded block, 256-byte aligned)."""
+    assert w4.linear_scratch_bytes(1, 2048, 16384, w4.PATH_GEMV) == 0
+    assert w4.linear_scratch_bytes(1, 2048, 16384) == 0
+    nb, m_pad = 2048 // 32, 512
+    assert w4.linear_scratch_bytes(512, 2048, 16384) == nb * m_pad * 32 + nb * m_pad * 4
+    assert w4.linear_scratch_bytes(512, 2048, 16384, w4.PATH_GEMM) == nb * m_pad * 32 + nb * m_pad * 4
+    assert w4.norm_linear_argmax_scratch_bytes(1, 2048, 262144) == 0
+    assert w4.norm_linear_argmax_scratch_bytes(2, 256, 4096) == 2 * 256 * 2
+    assert w4.mx_linear_scratch_bytes(512, 2048, 2560) == 512 * 2048 + 512 * 64
+    assert w4.decode_attention_scratch_bytes(8, 1, 256, 640) > 0
+
+
+@pytest.mark.parametrize("args", [(0, 64, 64, 0), (1, 48, 64, 0), (1, 64, 96, 0), (1, 64, 64, 7)])
+def test_scratch_queries_reject_bad_shapes(lib, args):
+    n = ctypes.c_size_t(0)
+    assert lib.w4a8_linear_scratch_bytes(*args, ctypes.byref(n)) == w4.W4A8_EINVAL
+    n = ctypes.c_size_t(0)
+    assert lib.w4a8_decode_attention_scratch_bytes(8, 3, 256, 640, ctypes.byref(n)) == w4.W4A8_EINVAL
+    assert lib.w4a8_decode_attention_scratch_bytes(8, 1, 96, 640, ctypes.byref(n)) == w4.W4A8_EINVAL
+    assert lib.w4a8_mx_linear_scratch_bytes(1, 96, 64, ctypes.byref(n)) == w4.W4A8_EINVAL
+
+
+def test_reserve_needs_init(lib):
+    assert lib.w4a8_reserve_scratch(1 << 20) == w4.W4A8_ENOINIT
+    n = ctypes.c_size_t(0)
+    assert lib.w4a8_scratch_capacity(ctypes.byref(n)) == w4.W4A8_ENOINIT

@@ -189,28 +189,40 @@ def test_chain_of_layers_and_lm_head_argmax():
     assert np.array_equal(am, tf)
 
 
+def assert_close(got, ref, what=""):
+    excess = np.abs(np.asarray(got, np.float64) - ref) - (1e-3 + 1e-3 * np.abs(ref))
+    bad = int((excess > 0).sum())
+    assert bad == 0, f"{what}: {bad} of {ref.size} outside 1e-3 + 1e-3 |ref|, max excess {excess.max():.3g}"
+
+
 @pytest.mark.parametrize("m,h,vocab", [(1, 256, 4096), (1, 2048, 262144), (2, 256, 4096), (1, 8192, 4096),
                                         (1, 4096, 32768)])
 def test_norm_linear_argmax(m, h, vocab):
     """LM-head argmax on the fp32 residual stream (one fused launch for one row; rows normalised
-    first otherwise), against the oracle and against the two-step GPU path."""
+    first otherwise).  Teacher-forced: the oracle linear runs on the GPU's own fp16 head input
+    (w4a8_residual_norm_cast, whose fp64 sum of squares gives the same fp16 values as the fused
+    prologue), and every logit of both GPU paths is held to 1e-3 + 1e-3 |ref|."""
     qh = synth.int4_values(synth.rng(50 + h, 0), vocab, h)
     sh = synth.weight_scales(synth.rng(50 + h, 1), vocab, h)
     head = w4.Weights.pack(dev(qh), dev(sh))
     x = (np.random.default_rng(h + m).standard_normal((m, h)) * 3).astype(np.float32)
     am, logits = w4.norm_linear_argmax(dev(x), head.packed, head.w_scales, eps=EPS, logits=True)
     am, logits = host(am), host(logits)
-    ref = oracle.linear(oracle.rms_norm_fp16(x, EPS), qh, sh)
-    assert np.abs(logits - ref).max() < 1e-2
+    hb = host(w4.residual_norm_cast(dev(x), eps=EPS))
+    assert fp16_ulp_diff(hb, oracle.rms_norm_fp16(x, EPS)).max() <= 1
+    ref = oracle.linear(hb, qh, sh)
+    assert_close(logits, ref, "logits")
     assert np.array_equal(am, oracle.argmax_first(logits))  # the fused argmax of its own logits
     want = oracle.argmax_first(ref)
     for r in range(m):
-        if am[r] != want[r]:
-            assert ref[r, want[r]] - ref[r, am[r]] < 1e-2, (am, want)
-    # two-step path: normalise, then the fp16 fused-argmax GEMV
-    hd = w4.residual_norm_cast(dev(x), eps=EPS)
-    am2, logits2 = w4.linear_argmax(hd, head.packed, head.w_scales, logits=True)
-    assert np.abs(host(logits2) - logits).max() < 1e-2
+        if am[r] != want[r]:     # allowed only for a near-tie within the output tolerance
+            assert ref[r, want[r]] - ref[r, am[r]] <= 1e-3 + 1e-3 * abs(ref[r, want[r]]), (am, want)
+    # two-step path: the fp16 fused-argmax GEMV on the same fp16 values (its launch plan, and so
+    # its fp32 summation order, may differ from the normalising kernel's)
+    am2, logits2 = w4.linear_argmax(dev(hb), head.packed, head.w_scales, logits=True)
+    am2, logits2 = host(am2), host(logits2)
+    assert_close(logits2, ref, "two-step logits")
+    assert np.array_equal(am2, oracle.argmax_first(logits2))
 
 
 def test_graph_replay_matches_eager():
@@ -261,6 +273,46 @@ def test_graph_replay_matches_eager():
         assert int(host(am_fused)[0]) == eager_fused[i], f"replay {i}"
         scratch = w4.linear(dev(np.ones((2, h), np.float16)), head.packed, head.w_scales)  # eager work between
         host(scratch)
+
+
+def test_graph_of_a_prefill_layer_survives_scratch_growth():
+    """A captured 130-row layer (prefill GEMMs staging in library scratch) keeps replaying
+    correctly after w4a8_reserve_scratch has replaced the scratch it was captured with: the old
+    buffer is retired, not freed, and eager calls between replays use the new one."""
+    h, n_qkv, f, m = 256, 320, 512, 130
+    _, dev_w = _weights(60, h, n_qkv, f)
+    assert w4.decoder_layer_scratch_bytes(m, h, dev_w["qkv"], dev_w["gate_up"]) > 0
+    x0 = np.random.default_rng(61).standard_normal((m, h)).astype(np.float32)
+    x = dev(x0)
+    ws = torch.empty(w4.decoder_layer_workspace(m, h, dev_w["qkv"], dev_w["gate_up"]), dtype=torch.uint8,
+                     device=DEV)
+
+    def layer():
+        w4.decoder_layer(x, dev_w["qkv"], dev_w["o"], dev_w["gate_up"], dev_w["down"], SCALE, EPS, ws)
+
+    eager = []
+    for _ in range(3):
+        layer()
+        eager.append(host(x).copy())
+    side = torch.cuda.Stream()
+    side.wait_stream(torch.cuda.current_stream())
+    with torch.cuda.stream(side):
+        layer()
+    torch.cuda.current_stream().wait_stream(side)
+    torch.cuda.synchronize()
+    graph = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(graph):
+        layer()
+    before = w4.scratch_capacity()
+    w4.reserve_scratch(before + (64 << 20))
+    assert w4.scratch_capacity() >= before + (64 << 20)
+    xe = np.random.default_rng(62).standard_normal((256, h)).astype(np.float16)
+    x.copy_(dev(x0))
+    for i in range(3):
+        graph.replay()
+        assert np.array_equal(host(x), eager[i]), f"replay {i}"
+        # eager prefill work on the new scratch between replays
+        host(w4.linear(dev(xe), dev_w["gate_up"].packed, dev_w["gate_up"].w_scales))
 
 
 def test_residual_add_more_rows_than_a_grid_dimension():

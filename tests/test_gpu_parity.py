@@ -320,6 +320,52 @@ def test_argmax_ties_take_lowest_index():
     assert host(w4.linear_argmax(dev(xz), packed, ws)).tolist() == [0, 0]
 
 
+def test_argmax_ties_at_the_row_maximum_across_workgroups():
+    """Three identical weight columns in different workgroups of the LM head (1000, 70001 and
+    200003: 64-column tiles) make the row maximum; the fused argmax returns the lowest of them."""
+    k, n = synth.LM_HEAD_SHAPE
+    x, qw, sw = inputs(23, 2, k, n)
+    cols = [1000, 70001, 200003]
+    q16 = oracle.quantize_activations(x)[0].astype(np.int64)
+    best = np.where(q16[0] >= 0, 7, -8).astype(np.int8)     # row 0's codes all pull the same way
+    for c in cols:
+        qw[c] = best
+        sw[c] = np.float16(0.02)
+    packed, ws = packed_on_gpu(qw, sw)
+    am, logits = w4.linear_argmax(dev(x), packed, ws, logits=True)
+    am, logits = host(am), host(logits)
+    assert logits[0, cols[0]] == logits[0, cols[1]] == logits[0, cols[2]] == logits[0].max()
+    assert (logits[0] == logits[0].max()).sum() == 3
+    assert am[0] == cols[0]
+    assert np.array_equal(am, oracle.argmax_first(logits))
+    # and the same logits when 1000 is taken out of the tie: the next lowest wins
+    qw[1000] = 0
+    packed, ws = packed_on_gpu(qw, sw)
+    assert host(w4.linear_argmax(dev(x), packed, ws))[0] == cols[1]
+
+
+def test_call_beyond_reserved_scratch_is_rejected():
+    """A prefill linear whose staging exceeds the reserved scratch fails with W4A8_EINVAL before
+    launching anything (out untouched) and runs after w4a8_reserve_scratch."""
+    k, n = 8192, 64
+    cap = w4.scratch_capacity()
+    m = ((cap // (k + k // 8)) // 32 + 64) * 32
+    need = w4.linear_scratch_bytes(m, k, n)
+    assert need > cap
+    x, qw, sw = inputs(25, m, k, n)
+    packed, ws = packed_on_gpu(qw, sw)
+    xd = dev(x)
+    out = torch.full((m, n), 7.0, dtype=torch.float32, device=DEV)
+    with pytest.raises(w4.W4A8Error) as err:
+        w4.linear(xd, packed, ws, out=out)
+    assert err.value.code == w4.W4A8_EINVAL and "w4a8_reserve_scratch" in str(err.value)
+    assert bool((host(out) == 7.0).all())
+    w4.reserve_scratch(need)
+    got = host(w4.linear(xd, packed, ws, out=out))
+    rows = np.random.default_rng(26).choice(m, 64, replace=False)
+    assert_close(got[rows], oracle.linear(x[rows], qw, sw), "sampled rows")
+
+
 def test_argmax_back_to_back_calls():
     """The fused argmax leaves its slots reset: consecutive calls with different inputs agree
     with their own logits."""
