@@ -72,6 +72,8 @@ def load_library() -> ctypes.CDLL:
         "w4a8_pack_weights": ([p, p, i64, i64, p, p, p], i32),
         "w4a8_linear": ([p, p, p, i64, i64, i64, p, p], i32),
         "w4a8_linear_path": ([p, p, p, i64, i64, i64, p, i32, p], i32),
+        "w4a8_linear_noalloc": ([p, p, p, i64, i64, i64, p, p], i32),
+        "w4a8_noalloc_scratch_bytes": ([ctypes.POINTER(ctypes.c_size_t)], i32),
         "w4a8_linear_argmax": ([p, p, p, i64, i64, i64, p, p, p], i32),
         "w4a8_norm_linear_argmax": ([p, ctypes.c_float, p, p, i64, i64, i64, p, p, p], i32),
         "w4a8_quantize_act": ([p, i64, i64, p, p, p], i32),

@@ -22,9 +22,23 @@ constexpr int kMaxDevices = 64;
 // 32768 positions of one KV head ~2 MB); w4a8_reserve_scratch adds more.
 constexpr size_t kInitialWork = 64u << 20;
 
+// Scratch of w4a8_linear_noalloc, for callers that cannot allocate: a
+// file-scope device array, so the library never allocates it; every GPU the
+// library runs on holds its own copy until the process ends.  Host code never
+// uses the array's name as an address (on the host it is only a stand-in):
+// w4a8_init looks up the device address once per device and keeps it in
+// DeviceState::noalloc.  Layout: tickets, argmax slots, then the work area.
+constexpr size_t kNoallocBytes = 32u << 20;
+constexpr int kNoallocTickets = 1024;
+constexpr size_t kNoallocTicketBytes = kNoallocTickets * sizeof(uint32_t);
+constexpr size_t kNoallocSlotBytes = kMaxArgmaxRows * kArgmaxSpread * sizeof(unsigned long long);
+constexpr size_t kNoallocWorkOffset = (kNoallocTicketBytes + kNoallocSlotBytes + 255) & ~size_t{255};
+static __device__ __align__(256) unsigned char scratch[kNoallocBytes];
+
 struct DeviceState {
   bool ready = false;
   Scratch sc;
+  Scratch noalloc;  // a view of this device's copy of `scratch`
   // Work areas replaced by w4a8_reserve_scratch.  They are never freed: a HIP
   // graph captured while one was current still reads and writes it.
   std::vector<void*> retired;
@@ -250,6 +264,19 @@ int w4a8_init(int device) {
   sc.n_tickets = kMaxTickets;
   W4A8_HIP(hipMalloc(&sc.work, kInitialWork));
   sc.work_bytes = kInitialWork;
+  // This device's copy of the static scratch: its address, then its tickets
+  // cleared (every launch leaves them at zero again).
+  void* ptr = nullptr;
+  W4A8_HIP(hipGetSymbolAddress(&ptr, HIP_SYMBOL(scratch)));
+  W4A8_HIP(hipMemset(ptr, 0, kNoallocWorkOffset));
+  Scratch& na = st.noalloc;
+  na.base = ptr;
+  na.bytes = kNoallocBytes;
+  na.tickets = static_cast<uint32_t*>(ptr);
+  na.n_tickets = kNoallocTickets;
+  na.slots = reinterpret_cast<unsigned long long*>(static_cast<char*>(ptr) + kNoallocTicketBytes);
+  na.work = static_cast<char*>(ptr) + kNoallocWorkOffset;
+  na.work_bytes = kNoallocBytes - kNoallocWorkOffset;
   W4A8_HIP(hipDeviceSynchronize());
   st.ready = true;
   g_any_ready = true;
@@ -375,6 +402,28 @@ int w4a8_linear_path(const uint16_t* x, const uint8_t* packed_w, const uint16_t*
 int w4a8_linear(const uint16_t* x, const uint8_t* packed_w, const uint16_t* w_scales, int64_t M,
                 int64_t K, int64_t N, float* out, hipStream_t stream) {
   return w4a8_linear_path(x, packed_w, w_scales, M, K, N, out, W4A8_PATH_AUTO, stream);
+}
+
+int w4a8_linear_noalloc(const uint16_t* x, const uint8_t* packed_w, const uint16_t* w_scales, int64_t M,
+                        int64_t K, int64_t N, float* out, hipStream_t stream) {
+  int rc = check_linear_args(x, packed_w, w_scales, M, K, N, int64_t{1} << 20);
+  if (rc != W4A8_OK) return rc;
+  W4A8_REQUIRE(out, "null output pointer");
+  W4A8_REQUIRE(aligned(out, 16), "out must be 16-byte aligned");
+  DeviceState* st = nullptr;
+  rc = current_state(&st);
+  if (rc != W4A8_OK) return rc;
+  const size_t need = linear_scratch(M, K, N, W4A8_PATH_AUTO);
+  W4A8_REQUIRE(need <= st->noalloc.work_bytes,
+               "w4a8_linear_noalloc: this call needs %zu bytes of scratch and the static scratch holds %zu", need,
+               st->noalloc.work_bytes);
+  return linear_on(x, packed_w, w_scales, M, K, N, out, W4A8_PATH_AUTO, &st->noalloc, stream);
+}
+
+int w4a8_noalloc_scratch_bytes(size_t* bytes) {
+  W4A8_REQUIRE(bytes, "null pointer");
+  *bytes = kNoallocBytes - kNoallocWorkOffset;
+  return W4A8_OK;
 }
 
 int w4a8_linear_argmax(const uint16_t* x, const uint8_t* packed_w, const uint16_t* w_scales, int64_t M,

@@ -126,6 +126,26 @@ W4A8_API int w4a8_pack_weights(const int8_t* q, const uint16_t* s, int64_t K, in
 W4A8_API int w4a8_linear(const uint16_t* x, const uint8_t* packed_w, const uint16_t* w_scales,
                 int64_t M, int64_t K, int64_t N, float* out, hipStream_t stream);
 
+/*
+ * For callers that cannot allocate device memory (code under HIP graph
+ * capture, tight serving loops, harnesses that forbid hipMalloc): w4a8_linear
+ * with the same arguments, kernels and results, whose scratch (prefill
+ * staging, split-K partials, completion tickets) is a static device array of
+ * the library instead of memory the library allocates.  It allocates and
+ * frees nothing; the array (32 MiB per GPU, held from the library's load to
+ * the process end) is set up by w4a8_init.  A call whose scratch need
+ * (w4a8_linear_scratch_bytes with W4A8_PATH_AUTO) exceeds
+ * w4a8_noalloc_scratch_bytes fails with W4A8_EINVAL before launching
+ * anything.  Every call on a GPU shares that GPU's array, which keeps the last
+ * call's contents: calls that overlap on one GPU (other streams, other host
+ * threads) race; issue them on one stream.
+ */
+W4A8_API int w4a8_linear_noalloc(const uint16_t* x, const uint8_t* packed_w, const uint16_t* w_scales,
+                                 int64_t M, int64_t K, int64_t N, float* out, hipStream_t stream);
+
+/* Work-area bytes of the static scratch that w4a8_linear_noalloc uses (host-only). */
+W4A8_API int w4a8_noalloc_scratch_bytes(size_t* bytes);
+
 /* w4a8_linear with an explicit kernel choice (W4A8_PATH_*), for tests and tuning. */
 W4A8_API int w4a8_linear_path(const uint16_t* x, const uint8_t* packed_w, const uint16_t* w_scales,
                      int64_t M, int64_t K, int64_t N, float* out, int path,

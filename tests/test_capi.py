@@ -14,7 +14,7 @@ def lib():
 
 def test_exports_every_declared_symbol(lib):
     names = w4.declared_functions()
-    assert len(names) == 26, names
+    assert len(names) == 28, names
     for name in names:
         assert hasattr(lib, name), name
 
