@@ -569,25 +569,103 @@ def summarize_traffic(fetch_csv, write_csv):
     print(json.dumps(out))
 
 
-def cpu_baseline(synth, budget_s):
-    """The numpy oracle on the decode layer (all four projections, M = 1), repeated to fill the budget."""
-    import oracle
-    from threadpoolctl import threadpool_info
+def cpu_model():
+    try:
+        with open("/proc/cpuinfo") as f:
+            for line in f:
+                if line.startswith("model name"):
+                    return line.split(":", 1)[1].strip()
+    except OSError:
+        pass
+    return "unknown"
 
-    inputs = synth.workload_inputs("decode")
-    layer_bytes = sum(algorithmic_bytes(x.shape[0], x.shape[1], qw.shape[0]) for x, qw, _ in inputs.values())
-    passes, t0 = 0, time.perf_counter()
-    while True:
-        for x, qw, sw in inputs.values():
-            oracle.linear(x, qw, sw)
-        passes += 1
-        el = time.perf_counter() - t0
-        if el >= budget_s:
-            break
-    threads = max([i.get("num_threads", 1) for i in threadpool_info()] + [1])
-    return {"value": round(passes * layer_bytes / el / 1e9, 4), "unit": "GB/s", "cores": threads,
-            "kind": "oracle",
-            "sample": f"{passes} passes of the decode layer (4 projections, M=1, {layer_bytes} B) in {el:.1f} s"}
+
+def cpu_baseline(synth, budget_s):
+    """The plain C oracle (oracle/w4a8_ref.c) timed on the host cores, single-threaded and on all
+    cores (at most 16, the host share of one GPU): the single linear, the decode layer (the headline
+    value, GB/s), the decode-batch sweep, the prefill layer on a sample of rows (rows are
+    independent; extrapolated to 512 rows and labelled so) and one end-to-end decode token
+    (26 layers + the LM head).  Repetitions fill about budget_s seconds per measurement group."""
+    import numpy as np
+
+    import oracle
+    from oracle import cref
+
+    nproc = os.cpu_count() or 1
+    threads = max(1, min(16, nproc))
+    cref.load()
+
+    def timed(fn, min_s):
+        reps, t0 = 0, time.perf_counter()
+        while True:
+            fn()
+            reps += 1
+            el = time.perf_counter() - t0
+            if el >= min_s:
+                return el / reps
+
+    each = max(0.2, budget_s / 12)
+    out = {"kind": "oracle", "cores": threads, "nproc": nproc, "cpu_model": cpu_model(),
+           "implementation": "oracle/w4a8_ref.c: quantise, int32 block dots, fp64 scaled sum; OpenMP over columns"}
+    # config 0: single linear 2048 x 2048, M = 1
+    x, qw, sw = synth.workload_inputs("single")["single"]
+    b0 = algorithmic_bytes(1, 2048, 2048)
+    t1 = timed(lambda: cref.linear(x, qw, sw, 1), each)
+    ta = timed(lambda: cref.linear(x, qw, sw, threads), each)
+    out["single_2048x2048"] = {"GB_s_1_thread": round(b0 / t1 / 1e9, 4), f"GB_s_{threads}_threads": round(b0 / ta / 1e9, 4)}
+    # config 1: the decode layer (headline)
+    dec = synth.workload_inputs("decode")
+    layer_bytes = sum(algorithmic_bytes(x.shape[0], x.shape[1], qw.shape[0]) for x, qw, _ in dec.values())
+    t1 = timed(lambda: [cref.linear(x, qw, sw, 1) for x, qw, sw in dec.values()], each)
+    ta = timed(lambda: [cref.linear(x, qw, sw, threads) for x, qw, sw in dec.values()], each)
+    out["value"] = round(layer_bytes / ta / 1e9, 4)
+    out["unit"] = "GB/s"
+    out["single_thread_value"] = round(layer_bytes / t1 / 1e9, 4)
+    out["sample"] = (f"decode layer (qkv, o, gate_up, down at M=1, {layer_bytes} B): {ta * 1e3:.1f} ms on "
+                     f"{threads} threads, {t1 * 1e3:.1f} ms on 1 thread")
+    # config 3: decode-batch sweep K = 4096, N = 14336
+    sweep = {}
+    for m in synth.WORKLOADS["wide"]["M"]:
+        x, qw, sw = synth.workload_inputs("wide", m)["wide"]
+        tm = timed(lambda: cref.linear(x, qw, sw, threads), each / 2)
+        sweep[str(m)] = round(algorithmic_bytes(m, 4096, 14336) / tm / 1e9, 4)
+    out["decode_batch_sweep_GB_s"] = sweep
+    # config 2: prefill layer at M = 512 from a sample of rows
+    rows = 16
+    pre = synth.workload_inputs("prefill")
+    ops = sum(2 * rows * x.shape[1] * qw.shape[0] for x, qw, _ in pre.values())
+    ta = timed(lambda: [cref.linear(x[:rows], qw, sw, threads) for x, qw, sw in pre.values()], each)
+    t1 = timed(lambda: [cref.linear(x[:4], qw, sw, 1) for x, qw, sw in pre.values()], each)
+    out["prefill_layer"] = {"sample_rows": rows, "extrapolated_to_rows": 512,
+                            "TOPS_extrapolated": round(ops / ta / 1e12, 6),
+                            "us_per_layer_extrapolated": round(ta * 512 / rows * 1e6, 1),
+                            "TOPS_1_thread_extrapolated": round(ops * 4 / rows / t1 / 1e12, 6)}
+    prefill_s = synth.N_LAYERS_E2E * ta * synth.PREFILL_TOKENS / rows
+    # config 4: one decode token through 26 layers and the LM head (C oracle linears, numpy glue)
+    layers = [synth.e2e_layer_weights(i) for i in range(synth.N_LAYERS_E2E)]
+    qh, sh = synth.e2e_head_weights()
+    x0 = synth.e2e_prompt()[-1:].astype(np.float32)
+
+    def token():
+        xr = x0.copy()
+        for w in layers:
+            n1 = oracle.rms_norm_fp16(xr, 1e-6)
+            q = cref.linear(n1, *w["qkv"], threads).astype(np.float32)
+            o = cref.linear(q[:, :2048].astype(np.float16), *w["o"], threads).astype(np.float32)
+            xr = oracle.residual_add(xr, o, 0.01)
+            g = cref.linear(oracle.rms_norm_fp16(xr, 1e-6), *w["gate_up"], threads).astype(np.float32)
+            d = cref.linear(oracle.gated_fp16(g), *w["down"], threads).astype(np.float32)
+            xr = oracle.residual_add(xr, d, 0.01)
+        logits = cref.linear(oracle.rms_norm_fp16(xr, 1e-6), qh, sh, threads)
+        return int(np.argmax(logits))
+
+    tt = timed(token, 0.0)
+    out["end_to_end"] = {"decode_tok_s": round(1.0 / tt, 3), "s_per_token": round(tt, 3),
+                         "note": "one decode token (26 layers + 2048x262144 LM head, argmax) on synthetic inputs "
+                                 "of the timed shape; the teacher-forced check of the GPU's inputs does the same work",
+                         "prefill_tok_s_extrapolated": round(synth.PREFILL_TOKENS / prefill_s, 3),
+                         "prefill_note": f"26 layers of the prefill layer's {rows}-row sample time, scaled to 512 rows"}
+    return out
 
 
 def main():

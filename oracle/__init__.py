@@ -24,7 +24,9 @@ scaled sum is formed in fp64 and is exact up to the final rounding for every
 size used here (I*sw needs 26 bits, times sx 50 bits, both below 53).
 
 Every function here is plain numpy, without blocking or reordering beyond the
-definition above.  Parity status of each function is stated in its docstring;
+definition above.  oracle/w4a8_ref.c (bound by oracle/cref.py) computes the
+same linear in plain C for timing on the host cores; the tests hold it to this
+module bit for bit.  Parity status of each function is stated in its docstring;
 the pins live in tests/test_oracle_*.py.
 """
 from __future__ import annotations
