@@ -24,10 +24,14 @@ __all__ = [
     "quantize_act", "block_sums", "gemv_max_m", "auto_path", "mx_pack_weights", "mx_quantize_act", "mx_linear", "kv_cache", "decode_attention", "Weights", "residual_norm_cast",
     "decoder_layer_workspace", "decoder_layer", "reserve_scratch", "scratch_capacity", "linear_scratch_bytes",
     "decoder_layer_scratch_bytes", "norm_linear_argmax_scratch_bytes", "mx_linear_scratch_bytes",
-    "decode_attention_scratch_bytes", "decoder_layer_workspace_offsets",
+    "decode_attention_scratch_bytes", "decoder_layer_workspace_offsets", "layer_kernel", "set_option",
+    "get_option", "take_device_errors", "OPTION_RESIDENT_LAYER", "LAYER_CHAIN", "LAYER_GEMM", "LAYER_GEMV4",
+    "LAYER_RESIDENT",
 ]
 
 PATH_AUTO, PATH_GEMV, PATH_GEMM = 0, 1, 2
+LAYER_CHAIN, LAYER_GEMM, LAYER_GEMV4, LAYER_RESIDENT = 0, 1, 2, 3
+OPTION_RESIDENT_LAYER = 1
 W4A8_OK, W4A8_EINVAL, W4A8_EUNSUPPORTED, W4A8_EHIP, W4A8_ENOINIT = 0, -1, -2, -3, -4
 
 _HERE = os.path.dirname(os.path.abspath(__file__))
@@ -101,6 +105,11 @@ def load_library() -> ctypes.CDLL:
         "w4a8_norm_linear_argmax_scratch_bytes": ([i64, i64, i64, ctypes.POINTER(ctypes.c_size_t)], i32),
         "w4a8_mx_linear_scratch_bytes": ([i64, i64, i64, ctypes.POINTER(ctypes.c_size_t)], i32),
         "w4a8_decode_attention_scratch_bytes": ([i64, i64, i64, i64, ctypes.POINTER(ctypes.c_size_t)], i32),
+        "w4a8_layer_kernel": ([i64, i64, ctypes.POINTER(_CWeights), ctypes.POINTER(_CWeights),
+                               ctypes.POINTER(i32)], i32),
+        "w4a8_set_option": ([i32, i32], i32),
+        "w4a8_get_option": ([i32, ctypes.POINTER(i32)], i32),
+        "w4a8_take_device_errors": ([ctypes.POINTER(ctypes.c_uint32)], i32),
     }
     for name, (args, res) in sig.items():
         fn = getattr(lib, name)
@@ -439,6 +448,31 @@ def decoder_layer_workspace_offsets(m: int, h: int, qkv: Weights, gate_up: Weigh
     _check("w4a8_decoder_layer_workspace_offsets", load_library().w4a8_decoder_layer_workspace_offsets(
         m, h, ctypes.byref(qkv.c), ctypes.byref(gate_up.c), offs))
     return dict(zip("q a o n g u d".split(), (int(v) for v in offs)))
+
+
+def layer_kernel(m: int, h: int, qkv: Weights, gate_up: Weights) -> int:
+    """LAYER_CHAIN, LAYER_GEMM, LAYER_GEMV4 or LAYER_RESIDENT: how decoder_layer runs this shape here."""
+    k = ctypes.c_int(0)
+    _check("w4a8_layer_kernel", load_library().w4a8_layer_kernel(
+        m, h, ctypes.byref(qkv.c), ctypes.byref(gate_up.c), ctypes.byref(k)))
+    return int(k.value)
+
+
+def set_option(option: int, value: int) -> None:
+    _check("w4a8_set_option", load_library().w4a8_set_option(option, value))
+
+
+def get_option(option: int) -> int:
+    v = ctypes.c_int(0)
+    _check("w4a8_get_option", load_library().w4a8_get_option(option, ctypes.byref(v)))
+    return int(v.value)
+
+
+def take_device_errors() -> int:
+    """Error word of the current device's kernels since the last call (0: none), then cleared."""
+    v = ctypes.c_uint32(0)
+    _check("w4a8_take_device_errors", load_library().w4a8_take_device_errors(ctypes.byref(v)))
+    return int(v.value)
 
 
 def decoder_layer(x: torch.Tensor, qkv: Weights, o: Weights, gate_up: Weights, down: Weights,

@@ -9,6 +9,7 @@
 #include <vector>
 
 #include "kernels.hpp"
+#include "resident.hpp"
 
 namespace w4a8 {
 
@@ -39,6 +40,11 @@ struct DeviceState {
   bool ready = false;
   Scratch sc;
   Scratch noalloc;  // a view of this device's copy of `scratch`
+  // Exchange area of the one-launch decoder layer (epoch, done and error
+  // words, hand-over buffers), zeroed at init; and whether the device holds
+  // all of that kernel's workgroups at once.
+  uint32_t* exchange = nullptr;
+  bool resident_ok = false;
   // Work areas replaced by w4a8_reserve_scratch.  They are never freed: a HIP
   // graph captured while one was current still reads and writes it.
   std::vector<void*> retired;
@@ -49,6 +55,9 @@ std::mutex g_mutex;
 
 int g_gemv_max_m = -1;
 bool g_gemv_max_m_forced = false;
+// W4A8_OPTION_RESIDENT_LAYER: the one-token decoder layer in one launch when
+// the shape and the device allow it (1, the default) or as four launches (0).
+int g_resident_layer = 1;
 
 int current_state(DeviceState** out) {
   if (!g_any_ready) {
@@ -199,6 +208,17 @@ bool layer_all_gemm(int64_t M, int64_t H, int64_t n_qkv, int64_t n_gu) {
          auto_path(M, H, n_gu) == W4A8_PATH_GEMM && auto_path(M, n_gu / 2, H) == W4A8_PATH_GEMM;
 }
 
+// How a decoder layer of this shape runs on the device (W4A8_LAYER_*).
+int layer_kernel(const DeviceState* st, int64_t M, int64_t H, int64_t n_qkv, int64_t n_gu) {
+  if (layer_fused(M, H, n_qkv, n_gu)) {
+    if (g_resident_layer && st->resident_ok &&
+        resident::layer_supported(static_cast<int>(H), static_cast<int>(n_qkv), static_cast<int>(n_gu)))
+      return W4A8_LAYER_RESIDENT;
+    return W4A8_LAYER_GEMV4;
+  }
+  return layer_all_gemm(M, H, n_qkv, n_gu) ? W4A8_LAYER_GEMM : W4A8_LAYER_CHAIN;
+}
+
 size_t linear_scratch(int64_t M, int64_t K, int64_t N, int path) {
   if (path == W4A8_PATH_AUTO) path = auto_path(M, K, N);
   if (path == W4A8_PATH_GEMV) return 0;
@@ -277,9 +297,53 @@ int w4a8_init(int device) {
   na.slots = reinterpret_cast<unsigned long long*>(static_cast<char*>(ptr) + kNoallocTicketBytes);
   na.work = static_cast<char*>(ptr) + kNoallocWorkOffset;
   na.work_bytes = kNoallocBytes - kNoallocWorkOffset;
+  W4A8_HIP(hipMalloc(&st.exchange, resident::kExchangeBytes));
+  W4A8_HIP(hipMemset(st.exchange, 0, resident::kExchangeBytes));
+  int blocks = 0;
+  W4A8_HIP(resident::co_resident_blocks(&blocks) == W4A8_OK ? hipSuccess : hipErrorUnknown);
+  st.resident_ok = blocks >= resident::kG;
   W4A8_HIP(hipDeviceSynchronize());
   st.ready = true;
   g_any_ready = true;
+  return W4A8_OK;
+}
+
+int w4a8_set_option(int option, int value) {
+  W4A8_REQUIRE(option == W4A8_OPTION_RESIDENT_LAYER, "unknown option %d", option);
+  W4A8_REQUIRE(value == 0 || value == 1, "option %d takes 0 or 1, not %d", option, value);
+  std::lock_guard<std::mutex> lock(g_mutex);
+  g_resident_layer = value;
+  return W4A8_OK;
+}
+
+int w4a8_get_option(int option, int* value) {
+  W4A8_REQUIRE(value, "null pointer");
+  W4A8_REQUIRE(option == W4A8_OPTION_RESIDENT_LAYER, "unknown option %d", option);
+  *value = g_resident_layer;
+  return W4A8_OK;
+}
+
+int w4a8_take_device_errors(uint32_t* errors) {
+  W4A8_REQUIRE(errors, "null pointer");
+  DeviceState* st = nullptr;
+  const int rc = current_state(&st);
+  if (rc != W4A8_OK) return rc;
+  uint32_t* word = st->exchange + resident::kErrorWord;
+  W4A8_HIP(hipDeviceSynchronize());
+  W4A8_HIP(hipMemcpy(errors, word, sizeof(uint32_t), hipMemcpyDeviceToHost));
+  W4A8_HIP(hipMemset(word, 0, sizeof(uint32_t)));
+  W4A8_HIP(hipDeviceSynchronize());
+  return W4A8_OK;
+}
+
+int w4a8_layer_kernel(int64_t M, int64_t H, const w4a8_weights* qkv, const w4a8_weights* gate_up, int* kernel) {
+  W4A8_REQUIRE(kernel, "null pointer");
+  int rc = check_layer_shapes(M, H, qkv, gate_up);
+  if (rc != W4A8_OK) return rc;
+  DeviceState* st = nullptr;
+  rc = current_state(&st);
+  if (rc != W4A8_OK) return rc;
+  *kernel = layer_kernel(st, M, H, qkv->N, gate_up->N);
   return W4A8_OK;
 }
 
@@ -550,7 +614,34 @@ int w4a8_decoder_layer(float* x, int64_t M, int64_t H, const w4a8_weights* qkv, 
   do {                              \
     if ((rc = (call)) != W4A8_OK) return rc; \
   } while (0)
-  if (layer_fused(M, H, qkv->N, gate_up->N)) {
+  DeviceState* st = nullptr;
+  W4A8_STEP(current_state(&st));
+  const int kernel = layer_kernel(st, M, H, qkv->N, gate_up->N);
+  if (kernel == W4A8_LAYER_RESIDENT) {
+    // One token in one launch of resident workgroups (the same values as the
+    // four launches below, bit for bit).
+    resident::LayerArgs ra{x,
+                           qkv->packed_w,
+                           qkv->w_scales,
+                           static_cast<int>(qkv->N),
+                           o->packed_w,
+                           o->w_scales,
+                           gate_up->packed_w,
+                           gate_up->w_scales,
+                           down->packed_w,
+                           down->w_scales,
+                           residual_scale,
+                           eps,
+                           q,
+                           a,
+                           ob,
+                           g,
+                           u,
+                           d,
+                           st->exchange};
+    return resident::launch_layer(ra, stream);
+  }
+  if (kernel == W4A8_LAYER_GEMV4) {
     // One token: four GEMV launches, with the normalisation in the prologue
     // of qkv and gate/up and the cast, residual and gated product in the
     // epilogues (the same values as the launches below, up to the summation
@@ -579,7 +670,7 @@ int w4a8_decoder_layer(float* x, int64_t M, int64_t H, const w4a8_weights* qkv, 
     return W4A8_OK;
   }
   const int Nq = static_cast<int>(qkv->N);
-  if (layer_all_gemm(M, H, qkv->N, gate_up->N)) {
+  if (kernel == W4A8_LAYER_GEMM) {
     // Many rows: every projection is a prefill GEMM, and the glue kernels
     // write their fp16 results straight into the next GEMM's quantised
     // staging, so no separate quantise pre-pass runs (four launches fewer).

@@ -255,11 +255,52 @@ W4A8_API int w4a8_decoder_layer_workspace_offsets(int64_t M, int64_t H, const w4
  * it).  Those stagings live in the workspace.  Each fused epilogue forms
  * the same fp16 values as the glue kernel it replaces and quantises them with
  * the same routine, so its codes and scales are those the glue kernel wrote.
+ * With M = 1 at hidden 2048, feed-forward 8192 (gate_up.N = 16384) and
+ * 2048 <= qkv.N <= 4096, on a device that holds 256 of its 768-thread
+ * workgroups at once, the four projections run in ONE launch
+ * (W4A8_LAYER_RESIDENT): each workgroup owns the columns the four GEMV launches
+ * would give it, requests the weights of all four projections at its start,
+ * and hands each projection's output to the next through flagged words in
+ * the library's exchange area (the pages overlap transfers with compute:
+ * aigridhq article on the WebGPU kernel studio).  The outputs and the
+ * workspace values equal the four-launch layer's bit for bit.  Calls of this
+ * kind on one device share the exchange area: they must not overlap (one
+ * stream, or streams ordered by events).  Its waits are bounded: if the
+ * workgroups cannot all be resident (another process occupying the GPU), a
+ * wait gives up after about a second, the outputs are undefined and
+ * w4a8_take_device_errors reports it.  W4A8_OPTION_RESIDENT_LAYER = 0 selects
+ * the four launches instead.
  */
 W4A8_API int w4a8_decoder_layer(float* x, int64_t M, int64_t H, const w4a8_weights* qkv,
                                 const w4a8_weights* o, const w4a8_weights* gate_up,
                                 const w4a8_weights* down, float residual_scale, float eps,
                                 void* workspace, size_t workspace_bytes, hipStream_t stream);
+
+/* How w4a8_decoder_layer runs a layer of this shape on the current device. */
+#define W4A8_LAYER_CHAIN 0     /* separate linears with glue kernels (nine launches) */
+#define W4A8_LAYER_GEMM 1      /* prefill GEMMs with fused glue (six launches) */
+#define W4A8_LAYER_GEMV4 2     /* one token, four fused GEMV launches */
+#define W4A8_LAYER_RESIDENT 3  /* one token, one launch of resident workgroups */
+W4A8_API int w4a8_layer_kernel(int64_t M, int64_t H, const w4a8_weights* qkv, const w4a8_weights* gate_up,
+                               int* kernel);
+
+/*
+ * Library options (process-wide):
+ *   W4A8_OPTION_RESIDENT_LAYER  1 (default): the one-token layer runs in one
+ *                               launch where it can; 0: as four launches.
+ * W4A8_EINVAL for an unknown option or value.  Not for calls in flight.
+ */
+#define W4A8_OPTION_RESIDENT_LAYER 1
+W4A8_API int w4a8_set_option(int option, int value);
+W4A8_API int w4a8_get_option(int option, int* value);
+
+/*
+ * Errors that kernels of the current device raised since the last call
+ * (0: none; nonzero: a one-launch decoder layer gave up waiting for an input,
+ * so that call's outputs are undefined), then cleared.  Synchronises the
+ * device.
+ */
+W4A8_API int w4a8_take_device_errors(uint32_t* errors);
 
 /*
  * LM-head argmax on the residual stream: argmax[m] = first index of the

@@ -14,7 +14,7 @@ def lib():
 
 def test_exports_every_declared_symbol(lib):
     names = w4.declared_functions()
-    assert len(names) == 28, names
+    assert len(names) == 32, names
     for name in names:
         assert hasattr(lib, name), name
 
@@ -164,3 +164,31 @@ def test_reserve_needs_init(lib):
     assert lib.w4a8_reserve_scratch(1 << 20) == w4.W4A8_ENOINIT
     n = ctypes.c_size_t(0)
     assert lib.w4a8_scratch_capacity(ctypes.byref(n)) == w4.W4A8_ENOINIT
+
+
+def test_options_on_the_host(lib):
+    """The resident-layer option takes 0 or 1 and needs no device; unknown options and values are rejected."""
+    assert w4.get_option(w4.OPTION_RESIDENT_LAYER) == 1
+    try:
+        w4.set_option(w4.OPTION_RESIDENT_LAYER, 0)
+        assert w4.get_option(w4.OPTION_RESIDENT_LAYER) == 0
+    finally:
+        w4.set_option(w4.OPTION_RESIDENT_LAYER, 1)
+    assert lib.w4a8_set_option(w4.OPTION_RESIDENT_LAYER, 2) == w4.W4A8_EINVAL
+    assert lib.w4a8_set_option(99, 0) == w4.W4A8_EINVAL
+    v = ctypes.c_int(0)
+    assert lib.w4a8_get_option(99, ctypes.byref(v)) == w4.W4A8_EINVAL
+    assert lib.w4a8_get_option(w4.OPTION_RESIDENT_LAYER, None) == w4.W4A8_EINVAL
+
+
+def test_device_queries_need_init(lib):
+    e = ctypes.c_uint32(0)
+    assert lib.w4a8_take_device_errors(ctypes.byref(e)) == w4.W4A8_ENOINIT
+    assert lib.w4a8_take_device_errors(None) == w4.W4A8_EINVAL
+    qkv = w4._CWeights(ALIGNED, ALIGNED, 2048, 2560)
+    gu = w4._CWeights(ALIGNED, ALIGNED, 2048, 16384)
+    k = ctypes.c_int(-1)
+    assert lib.w4a8_layer_kernel(1, 2048, ctypes.byref(qkv), ctypes.byref(gu), ctypes.byref(k)) == w4.W4A8_ENOINIT
+    assert lib.w4a8_layer_kernel(1, 2048, ctypes.byref(qkv), ctypes.byref(gu), None) == w4.W4A8_EINVAL
+    bad = w4._CWeights(ALIGNED, ALIGNED, 2048, 100)
+    assert lib.w4a8_layer_kernel(1, 2048, ctypes.byref(qkv), ctypes.byref(bad), ctypes.byref(k)) == w4.W4A8_EINVAL
