@@ -422,8 +422,14 @@ def bench_e2e(w4, torch, synth, timer, decode_steps):
     am = torch.empty((1,), dtype=torch.int32, device=dev)
 
     def token():
-        # One token: 26 layers (4 fused GEMV launches each) and the LM head with the final
-        # normalisation in its prologue and the argmax in its epilogue.
+        # One token: the 26 layers in one launch of resident workgroups (w4a8_decoder_stack),
+        # then the LM head with the final normalisation in its prologue and the argmax in its
+        # epilogue.
+        w4.decoder_stack(x, layers, E2E_SCALE, E2E_EPS, ws)
+        w4.norm_linear_argmax(x, head.packed, head.w_scales, eps=E2E_EPS, argmax=am)
+
+    def token_by_layer():
+        # The same token with one w4a8_decoder_layer call per layer.
         run_layers(x, ws)
         w4.norm_linear_argmax(x, head.packed, head.w_scales, eps=E2E_EPS, argmax=am)
 
@@ -441,18 +447,33 @@ def bench_e2e(w4, torch, synth, timer, decode_steps):
             ids.append(int(am.item()))                     # host sync every token
         return time.perf_counter() - t_start, ids
 
-    stream_s, ids_stream = decode(token)
+    def graph_of(fn):
+        graph = torch.cuda.CUDAGraph()
+        side = torch.cuda.Stream()
+        side.wait_stream(torch.cuda.current_stream())
+        with torch.cuda.stream(side):
+            fn()                                           # warm-up on the capture stream
+        torch.cuda.current_stream().wait_stream(side)
+        torch.cuda.synchronize()
+        with torch.cuda.graph(graph):
+            fn()
+        return graph
 
-    graph = torch.cuda.CUDAGraph()
-    side = torch.cuda.Stream()
-    side.wait_stream(torch.cuda.current_stream())
-    with torch.cuda.stream(side):
-        token()                                            # warm-up on the capture stream
-    torch.cuda.current_stream().wait_stream(side)
-    torch.cuda.synchronize()
-    with torch.cuda.graph(graph):
-        token()
+    stream_s, ids_stream = decode(token)
+    graph = graph_of(token)
     graph_s, ids_graph = decode(graph.replay)
+    # The same decode with one launch per layer, and with the four GEMV launches per layer.
+    by_layer = {}
+    for name, mode in (("one_launch_per_layer", 1), ("four_launches_per_layer", 0)):
+        w4.set_option(w4.OPTION_RESIDENT_LAYER, mode)
+        try:
+            g = graph_of(token_by_layer)
+            secs, ids = decode(g.replay)
+        finally:
+            w4.set_option(w4.OPTION_RESIDENT_LAYER, 1)
+        by_layer[name] = {"decode_tok_s_graph": round(decode_steps / secs, 1), "ids_match": ids == ids_graph}
+        del g
+    device_errors = w4.take_device_errors()
 
     # The LM head alone (302 MB of weights and scales, more than the 256 MB memory-side cache,
     # so every launch streams it from HBM): plain linear and normalising argmax.
@@ -480,6 +501,9 @@ def bench_e2e(w4, torch, synth, timer, decode_steps):
         "frac_of_hbm_token_ceiling": round(tok_s_graph / ceiling, 4),
         "hbm_token_ceiling_tok_s": round(ceiling, 1),
         "graph_ids_match_stream": ids_graph == ids_stream,
+        "layers_kernel": "w4a8_decoder_stack: 26 layers in one launch of resident workgroups",
+        "decode_by_layer_kernel": by_layer,
+        "device_errors": device_errors,
         "lm_head": {"K": h, "N": synth.LM_HEAD_SHAPE[1], "bytes": head_bytes,
                     "linear_us": round(head_linear_ms * 1e3, 2),
                     "linear_GB_s": round(head_bytes / (head_linear_ms * 1e6), 1),

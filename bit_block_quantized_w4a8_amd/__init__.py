@@ -25,7 +25,7 @@ __all__ = [
     "decoder_layer_workspace", "decoder_layer", "reserve_scratch", "scratch_capacity", "linear_scratch_bytes",
     "decoder_layer_scratch_bytes", "norm_linear_argmax_scratch_bytes", "mx_linear_scratch_bytes",
     "decode_attention_scratch_bytes", "decoder_layer_workspace_offsets", "layer_kernel", "set_option",
-    "get_option", "take_device_errors", "OPTION_RESIDENT_LAYER", "LAYER_CHAIN", "LAYER_GEMM", "LAYER_GEMV4",
+    "get_option", "take_device_errors", "decoder_stack", "OPTION_RESIDENT_LAYER", "LAYER_CHAIN", "LAYER_GEMM", "LAYER_GEMV4",
     "LAYER_RESIDENT",
 ]
 
@@ -105,6 +105,8 @@ def load_library() -> ctypes.CDLL:
         "w4a8_norm_linear_argmax_scratch_bytes": ([i64, i64, i64, ctypes.POINTER(ctypes.c_size_t)], i32),
         "w4a8_mx_linear_scratch_bytes": ([i64, i64, i64, ctypes.POINTER(ctypes.c_size_t)], i32),
         "w4a8_decode_attention_scratch_bytes": ([i64, i64, i64, i64, ctypes.POINTER(ctypes.c_size_t)], i32),
+        "w4a8_decoder_stack": ([p, i64, i64, ctypes.POINTER(_CWeights), i64, ctypes.c_float, ctypes.c_float, p,
+                                ctypes.c_size_t, p], i32),
         "w4a8_layer_kernel": ([i64, i64, ctypes.POINTER(_CWeights), ctypes.POINTER(_CWeights),
                                ctypes.POINTER(i32)], i32),
         "w4a8_set_option": ([i32, i32], i32),
@@ -486,5 +488,28 @@ def decoder_layer(x: torch.Tensor, qkv: Weights, o: Weights, gate_up: Weights, d
     _check("w4a8_decoder_layer", load_library().w4a8_decoder_layer(
         x.data_ptr(), m, h, ctypes.byref(qkv.c), ctypes.byref(o.c), ctypes.byref(gate_up.c),
         ctypes.byref(down.c), residual_scale, eps, workspace.data_ptr(),
+        workspace.numel() * workspace.element_size(), _stream(x)))
+    return x
+
+
+def decoder_stack(x: torch.Tensor, layers: list, residual_scale: float, eps: float,
+                  workspace: torch.Tensor) -> torch.Tensor:
+    """Decoder layers in order, in place on the fp32 residual stream x [M][H].
+
+    layers: a list of dicts with Weights under "qkv", "o", "gate_up" and "down".
+    """
+    _need(x, "x", torch.float32, 2)
+    if not workspace.is_cuda or not workspace.is_contiguous():
+        raise ValueError("workspace must be a contiguous CUDA tensor")
+    if not layers:
+        raise ValueError("layers must not be empty")
+    table = (_CWeights * (4 * len(layers)))()
+    for i, lw in enumerate(layers):
+        for j, name in enumerate(("qkv", "o", "gate_up", "down")):
+            table[4 * i + j] = lw[name].c
+    m, h = x.shape
+    _ready(x)
+    _check("w4a8_decoder_stack", load_library().w4a8_decoder_stack(
+        x.data_ptr(), m, h, table, len(layers), residual_scale, eps, workspace.data_ptr(),
         workspace.numel() * workspace.element_size(), _stream(x)))
     return x

@@ -578,29 +578,13 @@ int w4a8_decoder_layer_workspace_offsets(int64_t M, int64_t H, const w4a8_weight
   return W4A8_OK;
 }
 
-int w4a8_decoder_layer(float* x, int64_t M, int64_t H, const w4a8_weights* qkv, const w4a8_weights* o,
-                       const w4a8_weights* gate_up, const w4a8_weights* down, float residual_scale, float eps,
-                       void* workspace, size_t workspace_bytes, hipStream_t stream) {
-  W4A8_REQUIRE(x && aligned(x, 16), "x must be a 16-byte aligned pointer");
-  int rc = check_layer_shapes(M, H, qkv, gate_up);
-  if (rc != W4A8_OK) return rc;
-  if ((rc = check_weights(qkv, "qkv")) != W4A8_OK || (rc = check_weights(o, "o")) != W4A8_OK ||
-      (rc = check_weights(gate_up, "gate_up")) != W4A8_OK || (rc = check_weights(down, "down")) != W4A8_OK)
-    return rc;
-  W4A8_REQUIRE(o->K == H && o->N == H, "o must be H x H");
-  W4A8_REQUIRE(down->K == gate_up->N / 2 && down->N == H, "gate_up must be H x 2F and down F x H");
-  const LayerWorkspace w = layer_workspace(static_cast<int>(M), static_cast<int>(H), static_cast<int>(qkv->N),
-                                           static_cast<int>(gate_up->N));
-  W4A8_REQUIRE(workspace && aligned(workspace, 256) && workspace_bytes >= w.bytes,
-               "workspace must be 256-byte aligned and hold %zu bytes", w.bytes);
-  Scratch* sc = nullptr;
-  rc = library_scratch(&sc);
-  if (rc != W4A8_OK) return rc;
-  // Checked before the first launch, so a rejected call leaves x untouched.
-  rc = require_scratch(sc, layer_scratch(M, H, qkv->N, gate_up->N));
-  if (rc != W4A8_OK) return rc;
-
-  char* base = static_cast<char*>(workspace);
+namespace {
+// One decoder layer on the launches other than the resident kernel (shapes
+// and workspace already checked).
+int run_layer(DeviceState* st, Scratch* sc, float* x, int64_t M, int64_t H, const w4a8_weights* qkv,
+              const w4a8_weights* o, const w4a8_weights* gate_up, const w4a8_weights* down, float residual_scale,
+              float eps, char* base, const LayerWorkspace& w, hipStream_t stream) {
+  int rc = W4A8_OK;
   float* q = reinterpret_cast<float*>(base + w.q);
   uint16_t* a = reinterpret_cast<uint16_t*>(base + w.a);
   float* ob = reinterpret_cast<float*>(base + w.o);
@@ -614,33 +598,7 @@ int w4a8_decoder_layer(float* x, int64_t M, int64_t H, const w4a8_weights* qkv, 
   do {                              \
     if ((rc = (call)) != W4A8_OK) return rc; \
   } while (0)
-  DeviceState* st = nullptr;
-  W4A8_STEP(current_state(&st));
   const int kernel = layer_kernel(st, M, H, qkv->N, gate_up->N);
-  if (kernel == W4A8_LAYER_RESIDENT) {
-    // One token in one launch of resident workgroups (the same values as the
-    // four launches below, bit for bit).
-    resident::LayerArgs ra{x,
-                           qkv->packed_w,
-                           qkv->w_scales,
-                           static_cast<int>(qkv->N),
-                           o->packed_w,
-                           o->w_scales,
-                           gate_up->packed_w,
-                           gate_up->w_scales,
-                           down->packed_w,
-                           down->w_scales,
-                           residual_scale,
-                           eps,
-                           q,
-                           a,
-                           ob,
-                           g,
-                           u,
-                           d,
-                           st->exchange};
-    return resident::launch_layer(ra, stream);
-  }
   if (kernel == W4A8_LAYER_GEMV4) {
     // One token: four GEMV launches, with the normalisation in the prologue
     // of qkv and gate/up and the cast, residual and gated product in the
@@ -727,6 +685,92 @@ int w4a8_decoder_layer(float* x, int64_t M, int64_t H, const w4a8_weights* qkv, 
 #undef W4A8_STEP
   return W4A8_OK;
 }
+
+}  // namespace
+
+int w4a8_decoder_layer(float* x, int64_t M, int64_t H, const w4a8_weights* qkv, const w4a8_weights* o,
+                       const w4a8_weights* gate_up, const w4a8_weights* down, float residual_scale, float eps,
+                       void* workspace, size_t workspace_bytes, hipStream_t stream) {
+  const w4a8_weights layer[4] = {qkv ? *qkv : w4a8_weights{}, o ? *o : w4a8_weights{},
+                                 gate_up ? *gate_up : w4a8_weights{}, down ? *down : w4a8_weights{}};
+  W4A8_REQUIRE(qkv && o && gate_up && down, "null weights");
+  return w4a8_decoder_stack(x, M, H, layer, 1, residual_scale, eps, workspace, workspace_bytes, stream);
+}
+
+int w4a8_decoder_stack(float* x, int64_t M, int64_t H, const w4a8_weights* layers, int64_t n_layers,
+                       float residual_scale, float eps, void* workspace, size_t workspace_bytes, hipStream_t stream) {
+  W4A8_REQUIRE(x && aligned(x, 16), "x must be a 16-byte aligned pointer");
+  W4A8_REQUIRE(layers, "null layers");
+  W4A8_REQUIRE(n_layers >= 1 && n_layers <= (int64_t{1} << 20), "n_layers = %lld out of range [1, 2^20]",
+               static_cast<long long>(n_layers));
+  const w4a8_weights* qkv0 = &layers[0];
+  const w4a8_weights* gu0 = &layers[2];
+  int rc = check_layer_shapes(M, H, qkv0, gu0);
+  if (rc != W4A8_OK) return rc;
+  // Every layer is checked before the first launch, so a rejected call leaves x untouched.
+  for (int64_t l = 0; l < n_layers; ++l) {
+    const w4a8_weights* qkv = &layers[4 * l];
+    const w4a8_weights* o = &layers[4 * l + 1];
+    const w4a8_weights* gate_up = &layers[4 * l + 2];
+    const w4a8_weights* down = &layers[4 * l + 3];
+    if ((rc = check_weights(qkv, "qkv")) != W4A8_OK || (rc = check_weights(o, "o")) != W4A8_OK ||
+        (rc = check_weights(gate_up, "gate_up")) != W4A8_OK || (rc = check_weights(down, "down")) != W4A8_OK)
+      return rc;
+    W4A8_REQUIRE(qkv->K == H && qkv->N == qkv0->N && gate_up->K == H && gate_up->N == gu0->N,
+                 "layer %lld: every layer must have the shapes of layer 0", static_cast<long long>(l));
+    W4A8_REQUIRE(o->K == H && o->N == H, "layer %lld: o must be H x H", static_cast<long long>(l));
+    W4A8_REQUIRE(down->K == gate_up->N / 2 && down->N == H, "layer %lld: gate_up must be H x 2F and down F x H",
+                 static_cast<long long>(l));
+  }
+  const LayerWorkspace w = layer_workspace(static_cast<int>(M), static_cast<int>(H), static_cast<int>(qkv0->N),
+                                           static_cast<int>(gu0->N));
+  W4A8_REQUIRE(workspace && aligned(workspace, 256) && workspace_bytes >= w.bytes,
+               "workspace must be 256-byte aligned and hold %zu bytes", w.bytes);
+  Scratch* sc = nullptr;
+  rc = library_scratch(&sc);
+  if (rc != W4A8_OK) return rc;
+  rc = require_scratch(sc, layer_scratch(M, H, qkv0->N, gu0->N));
+  if (rc != W4A8_OK) return rc;
+  DeviceState* st = nullptr;
+  rc = current_state(&st);
+  if (rc != W4A8_OK) return rc;
+  char* base = static_cast<char*>(workspace);
+  if (layer_kernel(st, M, H, qkv0->N, gu0->N) == W4A8_LAYER_RESIDENT) {
+    // One token through up to resident::kMaxStack layers per launch of
+    // resident workgroups (the same values as the four GEMV launches per
+    // layer, bit for bit).
+    resident::StackArgs ra{};
+    ra.x = x;
+    ra.n_qkv = static_cast<int>(qkv0->N);
+    ra.alpha = residual_scale;
+    ra.eps = eps;
+    ra.q = reinterpret_cast<float*>(base + w.q);
+    ra.a = reinterpret_cast<uint16_t*>(base + w.a);
+    ra.o = reinterpret_cast<float*>(base + w.o);
+    ra.g = reinterpret_cast<float*>(base + w.g);
+    ra.u = reinterpret_cast<uint16_t*>(base + w.u);
+    ra.d = reinterpret_cast<float*>(base + w.d);
+    ra.exchange = st->exchange;
+    for (int64_t l0 = 0; l0 < n_layers; l0 += resident::kMaxStack) {
+      ra.n_layers = static_cast<int>(std::min<int64_t>(resident::kMaxStack, n_layers - l0));
+      for (int i = 0; i < ra.n_layers; ++i) {
+        const w4a8_weights* lw = &layers[4 * (l0 + i)];
+        ra.w[i] = {lw[0].packed_w, lw[0].w_scales, lw[1].packed_w, lw[1].w_scales,
+                   lw[2].packed_w, lw[2].w_scales, lw[3].packed_w, lw[3].w_scales};
+      }
+      rc = resident::launch_stack(ra, stream);
+      if (rc != W4A8_OK) return rc;
+    }
+    return W4A8_OK;
+  }
+  for (int64_t l = 0; l < n_layers; ++l) {
+    rc = run_layer(st, sc, x, M, H, &layers[4 * l], &layers[4 * l + 1], &layers[4 * l + 2], &layers[4 * l + 3],
+                   residual_scale, eps, base, w, stream);
+    if (rc != W4A8_OK) return rc;
+  }
+  return W4A8_OK;
+}
+
 
 int w4a8_norm_linear_argmax(const float* x, float eps, const uint8_t* packed_w, const uint16_t* w_scales,
                             int64_t M, int64_t K, int64_t N, float* logits, int32_t* argmax, hipStream_t stream) {

@@ -276,6 +276,26 @@ W4A8_API int w4a8_decoder_layer(float* x, int64_t M, int64_t H, const w4a8_weigh
                                 const w4a8_weights* down, float residual_scale, float eps,
                                 void* workspace, size_t workspace_bytes, hipStream_t stream);
 
+/*
+ * n_layers decoder layers in order on x (the wiring above, layer l with the
+ * weights layers[4 l .. 4 l + 3] = qkv, o, gate_up, down; a host array read
+ * during the call).  Every layer must have the shapes of layer 0; each is
+ * checked as by w4a8_decoder_layer before anything runs.  The result equals
+ * n_layers calls of w4a8_decoder_layer bit for bit, and the workspace holds
+ * the last layer's intermediates.  Where w4a8_decoder_layer would run the
+ * one-launch layer (W4A8_LAYER_RESIDENT), up to 32 layers run in one launch:
+ * each layer's output stream is handed to the next layer inside the launch,
+ * and the next layer's qkv weights are requested while the current layer's
+ * down projection waits for its input (the pages overlap transfers with
+ * compute: aigridhq article on the WebGPU kernel studio; and decode a whole
+ * token per step: ML Drift explainer on tech.dede.sh, section "Stage-aware
+ * optimization for large language models").  Otherwise the layers run one
+ * after another as w4a8_decoder_layer runs them.  Allocates nothing.
+ */
+W4A8_API int w4a8_decoder_stack(float* x, int64_t M, int64_t H, const w4a8_weights* layers, int64_t n_layers,
+                                float residual_scale, float eps, void* workspace, size_t workspace_bytes,
+                                hipStream_t stream);
+
 /* How w4a8_decoder_layer runs a layer of this shape on the current device. */
 #define W4A8_LAYER_CHAIN 0     /* separate linears with glue kernels (nine launches) */
 #define W4A8_LAYER_GEMM 1      /* prefill GEMMs with fused glue (six launches) */

@@ -14,7 +14,7 @@ def lib():
 
 def test_exports_every_declared_symbol(lib):
     names = w4.declared_functions()
-    assert len(names) == 32, names
+    assert len(names) == 33, names
     for name in names:
         assert hasattr(lib, name), name
 
@@ -192,3 +192,33 @@ def test_device_queries_need_init(lib):
     assert lib.w4a8_layer_kernel(1, 2048, ctypes.byref(qkv), ctypes.byref(gu), None) == w4.W4A8_EINVAL
     bad = w4._CWeights(ALIGNED, ALIGNED, 2048, 100)
     assert lib.w4a8_layer_kernel(1, 2048, ctypes.byref(qkv), ctypes.byref(bad), ctypes.byref(k)) == w4.W4A8_EINVAL
+
+
+def test_decoder_stack_validates(lib):
+    """Argument errors come before the device is needed (EINVAL), a valid call without init is ENOINIT."""
+    def table(n, gu_n=16384):
+        t = (w4._CWeights * (4 * n))()
+        for i in range(n):
+            t[4 * i + 0] = w4._CWeights(ALIGNED, ALIGNED, 2048, 2560)
+            t[4 * i + 1] = w4._CWeights(ALIGNED, ALIGNED, 2048, 2048)
+            t[4 * i + 2] = w4._CWeights(ALIGNED, ALIGNED, 2048, gu_n)
+            t[4 * i + 3] = w4._CWeights(ALIGNED, ALIGNED, gu_n // 2, 2048)
+        return t
+
+    def call(t, n, x=ALIGNED, ws=ALIGNED, nbytes=1 << 30):
+        return lib.w4a8_decoder_stack(P(x), 1, 2048, t, n, ctypes.c_float(0.01), ctypes.c_float(1e-6), P(ws),
+                                      nbytes, None)
+
+    t = table(3)
+    assert call(t, 3) == w4.W4A8_ENOINIT
+    assert call(t, 0) == w4.W4A8_EINVAL
+    assert call(None, 3) == w4.W4A8_EINVAL
+    assert call(t, 3, x=ALIGNED + 4) == w4.W4A8_EINVAL
+    assert call(t, 3, ws=ALIGNED + 16) == w4.W4A8_EINVAL
+    assert call(t, 3, nbytes=64) == w4.W4A8_EINVAL
+    t[4 * 2 + 2] = w4._CWeights(ALIGNED, ALIGNED, 2048, 8192)   # layer 2's gate_up differs from layer 0's
+    t[4 * 2 + 3] = w4._CWeights(ALIGNED, ALIGNED, 4096, 2048)
+    assert call(t, 3) == w4.W4A8_EINVAL
+    t = table(2)
+    t[4 * 1 + 1] = w4._CWeights(ALIGNED, ALIGNED, 2048, 1024)   # o not H x H
+    assert call(t, 2) == w4.W4A8_EINVAL

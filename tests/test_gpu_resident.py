@@ -196,3 +196,88 @@ def test_resident_many_calls(layer):
     for _ in range(64):
         run(xf, layer, 2560, ws, resident=False)
     assert np.array_equal(host(xr).view(np.int32), host(xf).view(np.int32))
+
+
+@pytest.fixture(scope="module")
+def stack_layers(layer):
+    """Five distinct layers (qkv width 2560); longer stacks repeat them cyclically."""
+    out = [{"qkv": layer["qkv"][2560][1], "o": layer["o"][1], "gate_up": layer["gate_up"][1],
+            "down": layer["down"][1]}]
+    for i in range(1, 5):
+        out.append({"qkv": weights(H, 2560, 100 + 8 * i)[1], "o": weights(H, H, 102 + 8 * i)[1],
+                    "gate_up": weights(H, 2 * F, 104 + 8 * i)[1], "down": weights(F, H, 106 + 8 * i)[1]})
+    return out
+
+
+def run_single(x, lw, ws, resident):
+    w4.set_option(w4.OPTION_RESIDENT_LAYER, 1 if resident else 0)
+    try:
+        w4.decoder_layer(x, lw["qkv"], lw["o"], lw["gate_up"], lw["down"], SCALE, EPS, ws)
+    finally:
+        w4.set_option(w4.OPTION_RESIDENT_LAYER, 1)
+
+
+@pytest.mark.parametrize("n", [1, 2, 5, 33])
+def test_stack_equals_layer_by_layer(layer, stack_layers, n):
+    """A stack of n layers in one launch (two launches for 33) equals n one-launch layers and n
+    four-launch layers bit for bit, and leaves the last layer's intermediates in the workspace."""
+    lays = [stack_layers[i % len(stack_layers)] for i in range(n)]
+    x0 = stream_row(700 + n)
+    xs, xr, xf = dev(x0), dev(x0), dev(x0)
+    ws_s, ws_r, ws_f = workspace(layer, 2560), workspace(layer, 2560), workspace(layer, 2560)
+    w4.decoder_stack(xs, lays, SCALE, EPS, ws_s)
+    assert w4.take_device_errors() == 0
+    for lw in lays:
+        run_single(xr, lw, ws_r, resident=True)
+    for lw in lays:
+        run_single(xf, lw, ws_f, resident=False)
+    got = host(xs)
+    assert np.array_equal(got.view(np.int32), host(xr).view(np.int32)), "stack vs one-launch layers"
+    assert np.array_equal(got.view(np.int32), host(xf).view(np.int32)), "stack vs four-launch layers"
+    rs, rf = regions(layer, 2560, host(ws_s)), regions(layer, 2560, host(ws_f))
+    for k in rs:
+        assert np.array_equal(rs[k].view(np.uint8), rf[k].view(np.uint8)), f"last layer's {k}"
+    print(f"stack of {n}: equal to layer-by-layer", flush=True)
+
+
+def test_stack_four_launch_fallback(layer, stack_layers):
+    """With the one-launch kernel switched off, the stack runs layer by layer on the four launches."""
+    lays = stack_layers[:3]
+    x0 = stream_row(811)
+    xs, xf = dev(x0), dev(x0)
+    ws = workspace(layer, 2560)
+    w4.set_option(w4.OPTION_RESIDENT_LAYER, 0)
+    try:
+        w4.decoder_stack(xs, lays, SCALE, EPS, ws)
+        for lw in lays:
+            w4.decoder_layer(xf, lw["qkv"], lw["o"], lw["gate_up"], lw["down"], SCALE, EPS, ws)
+    finally:
+        w4.set_option(w4.OPTION_RESIDENT_LAYER, 1)
+    assert np.array_equal(host(xs).view(np.int32), host(xf).view(np.int32))
+
+
+def test_stack_graph_replay(layer, stack_layers):
+    """A 26-layer stack captured in a HIP graph: every replay equals the eager stack."""
+    lays = [stack_layers[i % len(stack_layers)] for i in range(26)]
+    x0 = stream_row(900)
+    ws = workspace(layer, 2560)
+    ref = dev(x0)
+    w4.decoder_stack(ref, lays, SCALE, EPS, ws)
+    want = host(ref)
+    x = dev(x0)
+    s = torch.cuda.Stream()
+    s.wait_stream(torch.cuda.current_stream())
+    with torch.cuda.stream(s):
+        w4.decoder_stack(x, lays, SCALE, EPS, ws)
+    torch.cuda.current_stream().wait_stream(s)
+    graph = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(graph):
+        w4.decoder_stack(x, lays, SCALE, EPS, ws)
+    for rep in range(3):
+        x.copy_(dev(x0))
+        graph.replay()
+        assert np.array_equal(host(x).view(np.int32), want.view(np.int32)), f"replay {rep}"
+        eager = dev(x0)
+        w4.decoder_stack(eager, lays[:2], SCALE, EPS, ws)  # other eager work between the replays
+        torch.cuda.synchronize()
+    assert w4.take_device_errors() == 0
