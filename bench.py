@@ -473,6 +473,48 @@ def bench_e2e(w4, torch, synth, timer, decode_steps):
             w4.set_option(w4.OPTION_RESIDENT_LAYER, 1)
         by_layer[name] = {"decode_tok_s_graph": round(decode_steps / secs, 1), "ids_match": ids == ids_graph}
         del g
+    # Decode with attention between qkv and o (w4a8_decoder_layer_attention: five launches per
+    # layer) over each layer's fp16 KV cache of capacity 640.  The 512 prompt positions of every
+    # cache hold seeded synthetic keys and values (the prefill runs no attention), and each token
+    # appends its own.  The attention length grows every token, so the launches are issued from
+    # the host (no graph).
+    seed = synth.WORKLOADS["e2e"]["seed"]
+    hkv, hd, cap = synth.ATTN_KV_HEADS, synth.ATTN_HEAD_DIM, synth.CONTEXT
+    prompt = int(x_pre.shape[0])
+    caches = []
+    for layer in range(n_layers):
+        kc, vc = w4.kv_cache(hkv, hd, cap)
+        kp = synth.rng(seed, 3_000_000 + 2 * layer).standard_normal((hkv, prompt, hd)).astype("float16")
+        vp = synth.rng(seed, 3_000_001 + 2 * layer).standard_normal((hkv, hd, prompt)).astype("float16")
+        kc[:, :prompt] = torch.from_numpy(kp).to(dev)
+        vc[:, :, :prompt] = torch.from_numpy(vp).to(dev)
+        caches.append((kc, vc))
+    attn_steps = min(decode_steps, cap - prompt)
+
+    def decode_attention_run():
+        x.copy_(x_start)
+        ids = []
+        torch.cuda.synchronize()
+        t_start = time.perf_counter()
+        for step in range(attn_steps):
+            for lw, (kc, vc) in zip(layers, caches):
+                w4.decoder_layer_attention(x, lw["qkv"], lw["o"], lw["gate_up"], lw["down"], E2E_SCALE, E2E_EPS,
+                                           kc, vc, synth.ATTN_HEADS, prompt + 1 + step, ws)
+            w4.norm_linear_argmax(x, head.packed, head.w_scales, eps=E2E_EPS, argmax=am)
+            ids.append(int(am.item()))                     # host sync every token
+        return time.perf_counter() - t_start, ids
+
+    decode_attention_run()                                 # warm-up (fills the caches' decode slots)
+    attn_s, attn_ids = decode_attention_run()
+    with_attention = {
+        "decode_tok_s_stream": round(attn_steps / attn_s, 1),
+        "decode_ms_per_token": round(attn_s / attn_steps * 1e3, 4),
+        "steps": attn_steps, "context": [prompt + 1, prompt + attn_steps],
+        "kernels_per_layer": "qkv GEMV (norm prologue), decode attention (8 x 256 query heads, one KV head), "
+                             "o, gate/up, down GEMVs",
+        "first_ids": attn_ids[:8],
+        "note": "prompt positions of the KV caches are seeded synthetic values; host-issued launches",
+    }
     device_errors = w4.take_device_errors()
 
     # The LM head alone (302 MB of weights and scales, more than the 256 MB memory-side cache,
@@ -503,6 +545,7 @@ def bench_e2e(w4, torch, synth, timer, decode_steps):
         "graph_ids_match_stream": ids_graph == ids_stream,
         "layers_kernel": "w4a8_decoder_stack: 26 layers in one launch of resident workgroups",
         "decode_by_layer_kernel": by_layer,
+        "decode_with_attention": with_attention,
         "device_errors": device_errors,
         "lm_head": {"K": h, "N": synth.LM_HEAD_SHAPE[1], "bytes": head_bytes,
                     "linear_us": round(head_linear_ms * 1e3, 2),

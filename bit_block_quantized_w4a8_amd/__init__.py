@@ -25,7 +25,7 @@ __all__ = [
     "decoder_layer_workspace", "decoder_layer", "reserve_scratch", "scratch_capacity", "linear_scratch_bytes",
     "decoder_layer_scratch_bytes", "norm_linear_argmax_scratch_bytes", "mx_linear_scratch_bytes",
     "decode_attention_scratch_bytes", "decoder_layer_workspace_offsets", "layer_kernel", "set_option",
-    "get_option", "take_device_errors", "decoder_stack", "OPTION_RESIDENT_LAYER", "LAYER_CHAIN", "LAYER_GEMM", "LAYER_GEMV4",
+    "get_option", "take_device_errors", "decoder_stack", "decoder_layer_attention", "OPTION_RESIDENT_LAYER", "LAYER_CHAIN", "LAYER_GEMM", "LAYER_GEMV4",
     "LAYER_RESIDENT",
 ]
 
@@ -107,6 +107,9 @@ def load_library() -> ctypes.CDLL:
         "w4a8_decode_attention_scratch_bytes": ([i64, i64, i64, i64, ctypes.POINTER(ctypes.c_size_t)], i32),
         "w4a8_decoder_stack": ([p, i64, i64, ctypes.POINTER(_CWeights), i64, ctypes.c_float, ctypes.c_float, p,
                                 ctypes.c_size_t, p], i32),
+        "w4a8_decoder_layer_attention": ([p, i64, ctypes.POINTER(_CWeights), ctypes.POINTER(_CWeights),
+                                          ctypes.POINTER(_CWeights), ctypes.POINTER(_CWeights), ctypes.c_float,
+                                          ctypes.c_float, p, p, i64, i64, i64, i64, i64, p, ctypes.c_size_t, p], i32),
         "w4a8_layer_kernel": ([i64, i64, ctypes.POINTER(_CWeights), ctypes.POINTER(_CWeights),
                                ctypes.POINTER(i32)], i32),
         "w4a8_set_option": ([i32, i32], i32),
@@ -512,4 +515,27 @@ def decoder_stack(x: torch.Tensor, layers: list, residual_scale: float, eps: flo
     _check("w4a8_decoder_stack", load_library().w4a8_decoder_stack(
         x.data_ptr(), m, h, table, len(layers), residual_scale, eps, workspace.data_ptr(),
         workspace.numel() * workspace.element_size(), _stream(x)))
+    return x
+
+
+def decoder_layer_attention(x: torch.Tensor, qkv: Weights, o: Weights, gate_up: Weights, down: Weights,
+                            residual_scale: float, eps: float, k_cache: torch.Tensor, v_cache: torch.Tensor,
+                            n_heads: int, length: int, workspace: torch.Tensor) -> torch.Tensor:
+    """One decode token through a decoder layer with attention between qkv and o, in place on x [1][H]."""
+    _need(x, "x", torch.float32, 2)
+    _need(k_cache, "k_cache", torch.float16, 3)
+    _need(v_cache, "v_cache", torch.float16, 3)
+    if not workspace.is_cuda or not workspace.is_contiguous():
+        raise ValueError("workspace must be a contiguous CUDA tensor")
+    m, h = x.shape
+    if m != 1:
+        raise ValueError("decoder_layer_attention takes one token row")
+    hkv, cap, d = k_cache.shape
+    if v_cache.shape != (hkv, d, cap):
+        raise ValueError(f"v_cache must be [{hkv}][{d}][{cap}]")
+    _ready(x)
+    _check("w4a8_decoder_layer_attention", load_library().w4a8_decoder_layer_attention(
+        x.data_ptr(), h, ctypes.byref(qkv.c), ctypes.byref(o.c), ctypes.byref(gate_up.c), ctypes.byref(down.c),
+        residual_scale, eps, k_cache.data_ptr(), v_cache.data_ptr(), n_heads, hkv, d, length, cap,
+        workspace.data_ptr(), workspace.numel() * workspace.element_size(), _stream(x)))
     return x

@@ -32,6 +32,16 @@
 //      when.  The final merge writes the fp16 output.  A merge keeps a running
 //      maximum (online softmax) and fetches eight partials per round, so its
 //      memory round trips grow with chunks / 8, not with chunks.
+//   5'. Up to kMaxLlChunks chunks (context 2048 at most), when the partials fit
+//      the library's attention exchange area: every chunk writes its partials
+//      as 64-bit words of 32 bits of data and a flag (agent-scope atomics, no
+//      store to wait for, no ticket), and every workgroup merges a share of
+//      the (head, 8 dimensions) items, one (item, chunk) pair per thread
+//      fetched in one round and combined through LDS in chunk order -- the
+//      arithmetic of the single-group merge above.  Each KV head has its own
+//      fixed region of words and epoch word; the flag is 1 + that epoch,
+//      which workgroup 0 of the head advances once it has read every chunk's
+//      words.  Every wait is bounded and raises the device error word.
 #include <algorithm>
 #include <cmath>
 
@@ -50,6 +60,8 @@ constexpr float kInvLo = 1.0f / 4096.0f;
 constexpr int kMaxGroups = 32;      // merge groups per KV head
 constexpr int kGroupChunks = 16;    // chunks per merge group, at least
 constexpr int kMergeUnroll = 8;     // partials fetched per merge round
+constexpr int kMaxLlChunks = 32;    // chunks the flagged-word merge serves
+constexpr int kLlSpin = 1 << 20;    // polls before a wait gives up
 
 typedef _Float16 h4 __attribute__((ext_vector_type(4)));
 typedef float f4 __attribute__((ext_vector_type(4)));
@@ -70,7 +82,20 @@ struct AttnArgs {
   int group_chunks;      // chunks per merge group
   int max_groups;        // merge groups per KV head at most (<= kMaxGroups): the ticket stride
   float scale2;          // log2(e) / sqrt(D)
+  // Flagged-word merge (nullable: the ticket merge above).
+  uint64_t* ll;          // [kAttnHeads][kAttnHeadWords] words; head g: [chunks][G][D + 2] (output dims, then max
+                         // and weight sum)
+  uint32_t* epochs;      // [Hkv]
+  uint32_t* error;       // device error word
 };
+
+__device__ __forceinline__ void ll_put(uint64_t* p, float v, uint32_t flag) {
+  __hip_atomic_store(p, (static_cast<uint64_t>(flag) << 32) | __float_as_uint(v), __ATOMIC_RELAXED,
+                     __HIP_MEMORY_SCOPE_AGENT);
+}
+__device__ __forceinline__ uint64_t ll_get(const uint64_t* p) {
+  return __hip_atomic_load(const_cast<uint64_t*>(p), __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+}
 
 __device__ __forceinline__ uint32_t pack2(_Float16 a, _Float16 b) {
   return static_cast<uint32_t>(__builtin_bit_cast(unsigned short, a)) |
@@ -90,12 +115,11 @@ __device__ __forceinline__ h4 half4_at(const uint4* run, int i) {
 __device__ __forceinline__ void fix_run(uint4* run, int valid, int at, uint32_t fresh) {
   uint32_t w[8] = {run[0].x, run[0].y, run[0].z, run[0].w, run[1].x, run[1].y, run[1].z, run[1].w};
 #pragma unroll
-  for (int i = 0; i < 16; ++i) {
-    const int sh = 16 * (i & 1);
-    uint32_t v = (w[i >> 1] >> sh) & 0xFFFFu;
-    v = i >= valid ? 0u : v;
-    v = i == at ? fresh : v;
-    w[i >> 1] = (w[i >> 1] & ~(0xFFFFu << sh)) | (v << sh);
+  for (int i = 0; i < 8; ++i) {  // word i holds positions 2 i (low half) and 2 i + 1
+    uint32_t v = w[i] & ((2 * i < valid ? 0x0000FFFFu : 0u) | (2 * i + 1 < valid ? 0xFFFF0000u : 0u));
+    v = 2 * i == at ? (v & 0xFFFF0000u) | fresh : v;
+    v = 2 * i + 1 == at ? (v & 0x0000FFFFu) | (fresh << 16) : v;
+    w[i] = v;
   }
   run[0] = make_uint4(w[0], w[1], w[2], w[3]);
   run[1] = make_uint4(w[4], w[5], w[6], w[7]);
@@ -146,7 +170,7 @@ __device__ __forceinline__ void merge_range(const float* st, const float* pp, in
   }
 }
 
-template <int D>
+template <int D, bool LL>
 __global__ __launch_bounds__(kThreads) void decode_attention_kernel(AttnArgs a) {
   constexpr int kSeg = D / 4;        // dimensions of a lane group's share of one key
   constexpr int kSteps = D / 16;     // score MFMAs per wave
@@ -158,6 +182,10 @@ __global__ __launch_bounds__(kThreads) void decode_attention_kernel(AttnArgs a) 
   __shared__ __align__(16) float s_raw[kRows * kSS];
   __shared__ __align__(16) _Float16 p_hl[kRows * kPS];
   __shared__ int last;
+  __shared__ uint32_t flag_s;
+  __shared__ __align__(16) uint16_t new_k[D], new_v[D];  // the newest token's key and value, fp16
+  // Flagged-word merge: one (item, chunk) pair per entry, 8 output dims, max, weight sum.
+  __shared__ float pairs[LL ? kThreads + kMaxLlChunks : 1][10];
 
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const int col = lane & 15, lg = lane >> 4;
@@ -165,6 +193,7 @@ __global__ __launch_bounds__(kThreads) void decode_attention_kernel(AttnArgs a) 
   const int G = a.group, L = a.length, cap = a.capacity;
   const int t0 = c * kChunk;
   const int newest = L - 1;
+  if (LL && tid == 0) flag_s = __hip_atomic_load(a.epochs + g, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) + 1u;
 
   // 1. Loads.  Key: this lane's position (column `col` of the wave's 16) and
   // its lane group's quarter of the dimensions.  Value: sixteen positions of
@@ -205,36 +234,45 @@ __global__ __launch_bounds__(kThreads) void decode_attention_kernel(AttnArgs a) 
     *reinterpret_cast<uint4*>(q_hl + h * kQS + d0) = make_uint4(hi[0], hi[1], hi[2], hi[3]);
     *reinterpret_cast<uint4*>(q_hl + (h + kMaxGroup) * kQS + d0) = make_uint4(lo[0], lo[1], lo[2], lo[3]);
   }
-  // The newest token: its key and value enter the cache as fp16 here and are
-  // used in that form; no other workgroup reads position L - 1.
-  if (tk == newest) {
-    const float4* src = reinterpret_cast<const float4*>(a.k_new + static_cast<int64_t>(g) * D + lg * kSeg);
+  // The newest token: its key and value enter the cache as fp16 and are used
+  // in that form; no other workgroup reads position L - 1.  The chunk's
+  // workgroup rounds them into LDS (four values per thread of its first wave)
+  // and writes them to the cache; after the barrier the lanes that hold
+  // position L - 1 take them from LDS.
+  const bool holds_newest = newest >= t0 && newest < t0 + kChunk;  // uniform per workgroup
+  if (holds_newest && tid < D / 4) {
+    const float4 kx = reinterpret_cast<const float4*>(a.k_new + static_cast<int64_t>(g) * D)[tid];
+    const float4 vx = reinterpret_cast<const float4*>(a.v_new + static_cast<int64_t>(g) * D)[tid];
+    const _Float16 k4[4] = {static_cast<_Float16>(kx.x), static_cast<_Float16>(kx.y), static_cast<_Float16>(kx.z),
+                            static_cast<_Float16>(kx.w)};
+    const _Float16 v4[4] = {static_cast<_Float16>(vx.x), static_cast<_Float16>(vx.y), static_cast<_Float16>(vx.z),
+                            static_cast<_Float16>(vx.w)};
+    const uint2 kp = make_uint2(pack2(k4[0], k4[1]), pack2(k4[2], k4[3]));
+    *reinterpret_cast<uint2*>(new_k + 4 * tid) = kp;
+    *reinterpret_cast<uint2*>(new_v + 4 * tid) = make_uint2(pack2(v4[0], v4[1]), pack2(v4[2], v4[3]));
+    *reinterpret_cast<uint2*>(a.k_cache + (static_cast<int64_t>(g) * cap + newest) * D + 4 * tid) = kp;
 #pragma unroll
-    for (int i = 0; i < kSeg / 8; ++i) {
-      const float4 x0 = src[2 * i], x1 = src[2 * i + 1];
-      kr[i] = make_uint4(pack2(static_cast<_Float16>(x0.x), static_cast<_Float16>(x0.y)),
-                         pack2(static_cast<_Float16>(x0.z), static_cast<_Float16>(x0.w)),
-                         pack2(static_cast<_Float16>(x1.x), static_cast<_Float16>(x1.y)),
-                         pack2(static_cast<_Float16>(x1.z), static_cast<_Float16>(x1.w)));
-      reinterpret_cast<uint4*>(krow)[i] = kr[i];
-    }
-  }
-  {
-    const int first = t0 + 16 * lg;   // position of element 0 of this lane's value runs
-    const int at = newest - first;
-#pragma unroll
-    for (int nt = 0; nt < kTiles; ++nt) {
-      const int d = wave * (D / 4) + 16 * nt + col;
-      uint32_t fresh = 0u;
-      if (at >= 0 && at < 16) {
-        const _Float16 v = static_cast<_Float16>(a.v_new[static_cast<int64_t>(g) * D + d]);
-        fresh = __builtin_bit_cast(unsigned short, v);
-        a.v_cache[(static_cast<int64_t>(g) * D + d) * cap + newest] = static_cast<uint16_t>(fresh);
-      }
-      fix_run(vr[nt], L - first, at, fresh);
-    }
+    for (int i = 0; i < 4; ++i)
+      a.v_cache[(static_cast<int64_t>(g) * D + 4 * tid + i) * cap + newest] = __builtin_bit_cast(unsigned short, v4[i]);
   }
   __syncthreads();
+  if (holds_newest) {
+    if (tk == newest) {
+#pragma unroll
+      for (int i = 0; i < kSeg / 8; ++i) kr[i] = *reinterpret_cast<const uint4*>(new_k + lg * kSeg + 8 * i);
+    }
+    const int first = t0 + 16 * lg;   // position of element 0 of this lane's value runs
+    const int at = newest - first;
+    // Only a run holding the newest position or reaching past it changes
+    // (valid length L - first of at most 16; 16 when the newest is its last).
+    if (L - first <= 16) {
+#pragma unroll
+      for (int nt = 0; nt < kTiles; ++nt) {
+        const int d = wave * (D / 4) + 16 * nt + col;
+        fix_run(vr[nt], L - first, at, (at >= 0 && at < 16) ? new_v[d] : 0u);
+      }
+    }
+  }
 
   // 2. Scores of the wave's 16 positions: row r of the result is head r's hi
   // part (r < 8) or head r - 8's lo part; lane l holds rows 4 * (l / 16) + j
@@ -255,6 +293,7 @@ __global__ __launch_bounds__(kThreads) void decode_attention_kernel(AttnArgs a) 
 
   // 3. Chunk softmax: thread -> head tid / 32, positions 2 * (tid % 32) + {0, 1};
   // the 32 threads of a head are one half of a wave.
+  float chunk_m = 0.f, chunk_l = 0.f;
   {
     const int h = tid >> 5, tt = 2 * (tid & 31);
     float s[2];
@@ -277,9 +316,14 @@ __global__ __launch_bounds__(kThreads) void decode_attention_kernel(AttnArgs a) 
       lo = pack2(static_cast<_Float16>((p0 - static_cast<float>(h0)) * kLo),
                  static_cast<_Float16>((p1 - static_cast<float>(h1)) * kLo));
       if ((tid & 31) == 0) {
-        float* st = a.stats + ((static_cast<int64_t>(g) * chunks + c) * G + h) * 2;
-        store_agent(st, m);
-        store_agent(st + 1, l);
+        if constexpr (LL) {
+          chunk_m = m;  // stored after the chunk's outputs (step 4)
+          chunk_l = l;
+        } else {
+          float* st = a.stats + ((static_cast<int64_t>(g) * chunks + c) * G + h) * 2;
+          store_agent(st, m);
+          store_agent(st + 1, l);
+        }
       }
     }
     *reinterpret_cast<uint32_t*>(p_hl + h * kPS + tt) = hi;
@@ -304,10 +348,122 @@ __global__ __launch_bounds__(kThreads) void decode_attention_kernel(AttnArgs a) 
       for (int j = 0; j < 4; ++j) {
         const float up = __shfl_down(acc[j], 32);
         const int h = 4 * lg + j;
-        if (lane < 32 && h < G)
-          store_agent(a.part + ((static_cast<int64_t>(g) * chunks + c) * G + h) * D + d, acc[j] + up * kInvLo);
+        if (lane < 32 && h < G) {
+          if constexpr (LL)
+            ll_put(a.ll + static_cast<int64_t>(g) * kAttnHeadWords + (static_cast<int64_t>(c) * G + h) * (D + 2) + d,
+                   acc[j] + up * kInvLo, flag_s);
+          else
+            store_agent(a.part + ((static_cast<int64_t>(g) * chunks + c) * G + h) * D + d, acc[j] + up * kInvLo);
+        }
       }
     }
+  }
+
+  if constexpr (LL) {
+    // The chunk's max and weight sum words go out after a barrier that every
+    // wave reaches once its output words are issued, so a reader that sees a
+    // chunk's max word (the one the merge polls first) finds its outputs
+    // almost always there too.
+    __syncthreads();
+    {
+      const int h = tid >> 5;
+      if ((tid & 31) == 0 && h < G) {
+        uint64_t* w = a.ll + static_cast<int64_t>(g) * kAttnHeadWords + (static_cast<int64_t>(c) * G + h) * (D + 2) + D;
+        ll_put(w, chunk_m, flag_s);
+        ll_put(w + 1, chunk_l, flag_s);
+      }
+    }
+    // 5'. Flagged-word merge.  Items (head h, dims 8 j .. 8 j + 7) i = c,
+    // c + chunks, ...; entry e of this workgroup is item c + chunks * (e /
+    // chunks) of chunk e % chunks.
+    const uint32_t flag = flag_s;
+    const int items = G * (D / 8);
+    const int per = (items + chunks - 1) / chunks;
+    const int mine = c < items ? (items - 1 - c) / chunks + 1 : 0;  // items this workgroup merges
+    const uint64_t* base = a.ll + static_cast<int64_t>(g) * kAttnHeadWords;
+    // Each thread polls the ten words of its entries (at most two: an entry
+    // tid and tid + kThreads), issuing every load of a round before testing
+    // any.  The chunks are few, so their polls are few.
+    bool ok = true;
+    const int n_entries = mine * chunks;
+    const int e0 = tid, e1 = tid + kThreads;
+    const uint64_t* w0 = base;
+    const uint64_t* w1 = base;
+    int d00 = 0, d01 = 0;
+    if (e0 < n_entries) {
+      const int it = c + chunks * (e0 / chunks);
+      w0 = base + (static_cast<int64_t>(e0 % chunks) * G + it / (D / 8)) * (D + 2);
+      d00 = (it % (D / 8)) * 8;
+    }
+    if (e1 < n_entries) {
+      const int it = c + chunks * (e1 / chunks);
+      w1 = base + (static_cast<int64_t>(e1 % chunks) * G + it / (D / 8)) * (D + 2);
+      d01 = (it % (D / 8)) * 8;
+    }
+    if (e0 < n_entries) {
+      uint64_t v[2][10];
+      for (int spin = 0;; ++spin) {
+#pragma unroll
+        for (int k = 0; k < 8; ++k) v[0][k] = ll_get(w0 + d00 + k);
+        v[0][8] = ll_get(w0 + D);
+        v[0][9] = ll_get(w0 + D + 1);
+        if (e1 < n_entries) {
+#pragma unroll
+          for (int k = 0; k < 8; ++k) v[1][k] = ll_get(w1 + d01 + k);
+          v[1][8] = ll_get(w1 + D);
+          v[1][9] = ll_get(w1 + D + 1);
+        }
+        bool ready = true;
+#pragma unroll
+        for (int k = 0; k < 10; ++k) ready &= static_cast<uint32_t>(v[0][k] >> 32) == flag;
+        if (e1 < n_entries) {
+#pragma unroll
+          for (int k = 0; k < 10; ++k) ready &= static_cast<uint32_t>(v[1][k] >> 32) == flag;
+        }
+        if (ready) break;
+        if (spin >= kLlSpin) {
+          ok = false;
+          break;
+        }
+        __builtin_amdgcn_s_sleep(1);
+      }
+#pragma unroll
+      for (int k = 0; k < 10; ++k) pairs[e0][k] = __uint_as_float(static_cast<uint32_t>(v[0][k]));
+      if (e1 < n_entries) {
+#pragma unroll
+        for (int k = 0; k < 10; ++k) pairs[e1][k] = __uint_as_float(static_cast<uint32_t>(v[1][k]));
+      }
+    }
+    if (!ok) __hip_atomic_store(a.error, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    __syncthreads();
+    // Workgroup 0 of the head has now read every chunk's words, so every
+    // workgroup of the head has read the epoch: advance it for the next call.
+    if (c == 0 && tid == 0) __hip_atomic_store(a.epochs + g, flag, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    if (tid < mine) {
+      const int it = c + chunks * tid;
+      const int h = it / (D / 8), d0 = (it % (D / 8)) * 8;
+      // Online-softmax merge in chunk order (the single-group merge's arithmetic).
+      float m = -INFINITY, l = 0.f, acc[8];
+#pragma unroll
+      for (int k = 0; k < 8; ++k) acc[k] = 0.f;
+      for (int cc = 0; cc < chunks; ++cc) {
+        const float* pv = pairs[tid * chunks + cc];
+        const float mn = fmaxf(m, pv[8]);
+        const float sc = exp2f(m - mn);
+        const float w = exp2f(pv[8] - mn);
+        l = l * sc + w * pv[9];
+#pragma unroll
+        for (int k = 0; k < 8; ++k) acc[k] = acc[k] * sc + w * pv[k];
+        m = mn;
+      }
+      uint32_t o[4];
+#pragma unroll
+      for (int i = 0; i < 4; ++i)
+        o[i] = pack2(static_cast<_Float16>(acc[2 * i] / l), static_cast<_Float16>(acc[2 * i + 1] / l));
+      *reinterpret_cast<uint4*>(a.out + (static_cast<int64_t>(g) * G + h) * D + d0) = make_uint4(o[0], o[1], o[2], o[3]);
+    }
+    (void)per;
+    return;
   }
 
   // 5. Merge.  The last workgroup of this chunk's merge group to finish
@@ -373,9 +529,16 @@ size_t attention_scratch_bytes(int n_kv_heads, int group, int head_dim, int leng
          sizeof(float);
 }
 
+bool attention_ll_fits(int n_kv_heads, int group, int head_dim, int length, const AttnExchange* ex) {
+  const int chunks = attention_chunks(length);
+  static_assert(kAttnHeadWords >= size_t{kMaxLlChunks} * kMaxGroup * (256 + 2), "attention exchange region");
+  return ex && ex->ll && chunks <= kMaxLlChunks && n_kv_heads <= ex->heads && group <= kMaxGroup &&
+         head_dim <= 256;
+}
+
 int launch_decode_attention(const float* q, const float* k_new, const float* v_new, uint16_t* k_cache,
                             uint16_t* v_cache, int n_heads, int n_kv_heads, int head_dim, int length, int capacity,
-                            uint16_t* out, Scratch* sc, hipStream_t stream) {
+                            uint16_t* out, Scratch* sc, const AttnExchange* ex, hipStream_t stream) {
   if (n_heads % n_kv_heads != 0 || n_heads / n_kv_heads > kMaxGroup || capacity % kChunk != 0 ||
       length < 1 || length > capacity || n_kv_heads < 1 || n_kv_heads >= (kMaxTickets - 2) / 2 ||
       sc->n_tickets < kMaxTickets)
@@ -405,11 +568,23 @@ int launch_decode_attention(const float* q, const float* k_new, const float* v_n
   a.capacity = capacity;
   a.scale2 = static_cast<float>(1.4426950408889634 / std::sqrt(static_cast<double>(head_dim)));
   const dim3 grid(chunks, n_kv_heads);
-  switch (head_dim) {
-    case 64: hipLaunchKernelGGL(decode_attention_kernel<64>, grid, dim3(kThreads), 0, stream, a); break;
-    case 128: hipLaunchKernelGGL(decode_attention_kernel<128>, grid, dim3(kThreads), 0, stream, a); break;
-    case 256: hipLaunchKernelGGL(decode_attention_kernel<256>, grid, dim3(kThreads), 0, stream, a); break;
-    default: return hip_fail(hipErrorInvalidValue, "decode attention: head_dim must be 64, 128 or 256");
+  if (attention_ll_fits(n_kv_heads, group, head_dim, length, ex)) {
+    a.ll = ex->ll;
+    a.epochs = ex->epochs;
+    a.error = ex->error;
+    switch (head_dim) {
+      case 64: hipLaunchKernelGGL((decode_attention_kernel<64, true>), grid, dim3(kThreads), 0, stream, a); break;
+      case 128: hipLaunchKernelGGL((decode_attention_kernel<128, true>), grid, dim3(kThreads), 0, stream, a); break;
+      case 256: hipLaunchKernelGGL((decode_attention_kernel<256, true>), grid, dim3(kThreads), 0, stream, a); break;
+      default: return hip_fail(hipErrorInvalidValue, "decode attention: head_dim must be 64, 128 or 256");
+    }
+  } else {
+    switch (head_dim) {
+      case 64: hipLaunchKernelGGL((decode_attention_kernel<64, false>), grid, dim3(kThreads), 0, stream, a); break;
+      case 128: hipLaunchKernelGGL((decode_attention_kernel<128, false>), grid, dim3(kThreads), 0, stream, a); break;
+      case 256: hipLaunchKernelGGL((decode_attention_kernel<256, false>), grid, dim3(kThreads), 0, stream, a); break;
+      default: return hip_fail(hipErrorInvalidValue, "decode attention: head_dim must be 64, 128 or 256");
+    }
   }
   W4A8_HIP(hipGetLastError());
   return W4A8_OK;

@@ -45,6 +45,8 @@ struct DeviceState {
   // all of that kernel's workgroups at once.
   uint32_t* exchange = nullptr;
   bool resident_ok = false;
+  // Exchange area of decode attention's flagged-word merge (zeroed at init).
+  AttnExchange attn;
   // Work areas replaced by w4a8_reserve_scratch.  They are never freed: a HIP
   // graph captured while one was current still reads and writes it.
   std::vector<void*> retired;
@@ -299,6 +301,16 @@ int w4a8_init(int device) {
   na.work_bytes = kNoallocBytes - kNoallocWorkOffset;
   W4A8_HIP(hipMalloc(&st.exchange, resident::kExchangeBytes));
   W4A8_HIP(hipMemset(st.exchange, 0, resident::kExchangeBytes));
+  {
+    const size_t bytes = kAttnHeads * kAttnHeadWords * sizeof(uint64_t) + kAttnHeads * sizeof(uint32_t);
+    void* p = nullptr;
+    W4A8_HIP(hipMalloc(&p, bytes));
+    W4A8_HIP(hipMemset(p, 0, bytes));
+    st.attn.ll = static_cast<uint64_t*>(p);
+    st.attn.epochs = reinterpret_cast<uint32_t*>(st.attn.ll + kAttnHeads * kAttnHeadWords);
+    st.attn.heads = kAttnHeads;
+    st.attn.error = st.exchange + resident::kErrorWord;
+  }
   int blocks = 0;
   W4A8_HIP(resident::co_resident_blocks(&blocks) == W4A8_OK ? hipSuccess : hipErrorUnknown);
   st.resident_ok = blocks >= resident::kG;
@@ -772,6 +784,80 @@ int w4a8_decoder_stack(float* x, int64_t M, int64_t H, const w4a8_weights* layer
 }
 
 
+int w4a8_decoder_layer_attention(float* x, int64_t H, const w4a8_weights* qkv, const w4a8_weights* o,
+                                 const w4a8_weights* gate_up, const w4a8_weights* down, float residual_scale,
+                                 float eps, uint16_t* k_cache, uint16_t* v_cache, int64_t n_heads, int64_t n_kv_heads,
+                                 int64_t head_dim, int64_t length, int64_t capacity, void* workspace,
+                                 size_t workspace_bytes, hipStream_t stream) {
+  W4A8_REQUIRE(x && aligned(x, 16), "x must be a 16-byte aligned pointer");
+  int rc = check_layer_shapes(1, H, qkv, gate_up);
+  if (rc != W4A8_OK) return rc;
+  if ((rc = check_weights(qkv, "qkv")) != W4A8_OK || (rc = check_weights(o, "o")) != W4A8_OK ||
+      (rc = check_weights(gate_up, "gate_up")) != W4A8_OK || (rc = check_weights(down, "down")) != W4A8_OK)
+    return rc;
+  W4A8_REQUIRE(o->K == H && o->N == H, "o must be H x H");
+  W4A8_REQUIRE(down->K == gate_up->N / 2 && down->N == H, "gate_up must be H x 2F and down F x H");
+  rc = check_attention(n_heads, n_kv_heads, head_dim, length);
+  if (rc != W4A8_OK) return rc;
+  W4A8_REQUIRE(k_cache && v_cache && aligned(k_cache, 16) && aligned(v_cache, 16), "caches must be 16-byte aligned");
+  W4A8_REQUIRE(capacity >= 64 && capacity % 64 == 0 && capacity <= (int64_t{1} << 24) && length <= capacity,
+               "capacity = %lld must be a multiple of 64 in [64, 2^24] and at least length = %lld",
+               static_cast<long long>(capacity), static_cast<long long>(length));
+  W4A8_REQUIRE(n_kv_heads * capacity * head_dim < (int64_t{1} << 38), "KV cache too large");
+  W4A8_REQUIRE(n_heads * head_dim == H, "n_heads * head_dim = %lld must equal H = %lld",
+               static_cast<long long>(n_heads * head_dim), static_cast<long long>(H));
+  W4A8_REQUIRE(qkv->N == (n_heads + 2 * n_kv_heads) * head_dim,
+               "qkv.N = %lld must hold the queries, one key and one value per KV head ((n_heads + 2 n_kv_heads) * "
+               "head_dim = %lld)",
+               static_cast<long long>(qkv->N), static_cast<long long>((n_heads + 2 * n_kv_heads) * head_dim));
+  W4A8_REQUIRE(layer_fused(1, H, qkv->N, gate_up->N), "the one-token GEMV launches do not support this shape");
+  const LayerWorkspace w = layer_workspace(1, static_cast<int>(H), static_cast<int>(qkv->N),
+                                           static_cast<int>(gate_up->N));
+  W4A8_REQUIRE(workspace && aligned(workspace, 256) && workspace_bytes >= w.bytes,
+               "workspace must be 256-byte aligned and hold %zu bytes", w.bytes);
+  Scratch* sc = nullptr;
+  rc = library_scratch(&sc);
+  if (rc != W4A8_OK) return rc;
+  const int Hq = static_cast<int>(n_heads), Hkv = static_cast<int>(n_kv_heads), D = static_cast<int>(head_dim);
+  rc = require_scratch(sc, attention_scratch_bytes(Hkv, Hq / Hkv, D, static_cast<int>(length)));
+  if (rc != W4A8_OK) return rc;
+  DeviceState* st = nullptr;
+  rc = current_state(&st);
+  if (rc != W4A8_OK) return rc;
+  char* base = static_cast<char*>(workspace);
+  float* q = reinterpret_cast<float*>(base + w.q);
+  uint16_t* a = reinterpret_cast<uint16_t*>(base + w.a);
+  float* ob = reinterpret_cast<float*>(base + w.o);
+  float* g = reinterpret_cast<float*>(base + w.g);
+  uint16_t* u = reinterpret_cast<uint16_t*>(base + w.u);
+  float* d = reinterpret_cast<float*>(base + w.d);
+  const int Hi = static_cast<int>(H), F = static_cast<int>(gate_up->N / 2);
+  // qkv with the normalisation in its prologue: the queries, keys and values in fp32.
+  GemvArgs qa{nullptr, qkv->packed_w, qkv->w_scales, 1, Hi, static_cast<int>(qkv->N), q, nullptr, nullptr, nullptr};
+  qa.xf = x;
+  qa.eps = eps;
+  qa.n16 = 0;
+  if ((rc = launch_gemv(qa, kGemvCast, sc, stream)) != W4A8_OK) return rc;
+  // Attention of the new token over the cache; its fp16 output is the o projection's input.
+  if ((rc = launch_decode_attention(q, q + Hq * D, q + (Hq + Hkv) * D, k_cache, v_cache, Hq, Hkv, D,
+                                    static_cast<int>(length), static_cast<int>(capacity), a, sc, &st->attn,
+                                    stream)) != W4A8_OK)
+    return rc;
+  GemvArgs oa{a, o->packed_w, o->w_scales, 1, Hi, Hi, ob, nullptr, nullptr, nullptr};
+  oa.resid = x;
+  oa.alpha = residual_scale;
+  if ((rc = launch_gemv(oa, kGemvResid, sc, stream)) != W4A8_OK) return rc;
+  GemvArgs ga{nullptr, gate_up->packed_w, gate_up->w_scales, 1, Hi, 2 * F, g, nullptr, nullptr, nullptr};
+  ga.xf = x;
+  ga.eps = eps;
+  ga.y16 = u;
+  if ((rc = launch_gemv(ga, kGemvGated, sc, stream)) != W4A8_OK) return rc;
+  GemvArgs da{u, down->packed_w, down->w_scales, 1, F, Hi, d, nullptr, nullptr, nullptr};
+  da.resid = x;
+  da.alpha = residual_scale;
+  return launch_gemv(da, kGemvResid, sc, stream);
+}
+
 int w4a8_norm_linear_argmax(const float* x, float eps, const uint8_t* packed_w, const uint16_t* w_scales,
                             int64_t M, int64_t K, int64_t N, float* logits, int32_t* argmax, hipStream_t stream) {
   W4A8_REQUIRE(x && aligned(x, 16), "x must be a 16-byte aligned pointer");
@@ -862,7 +948,10 @@ int w4a8_decode_attention(const float* q, const float* k_new, const float* v_new
   Scratch* sc = nullptr;
   rc = library_scratch(&sc);
   if (rc != W4A8_OK) return rc;
-  return launch_decode_attention(q, k_new, v_new, k_cache, v_cache, Hq, Hkv, D, Li, cap, out, sc, stream);
+  DeviceState* st = nullptr;
+  rc = current_state(&st);
+  if (rc != W4A8_OK) return rc;
+  return launch_decode_attention(q, k_new, v_new, k_cache, v_cache, Hq, Hkv, D, Li, cap, out, sc, &st->attn, stream);
 }
 
 int w4a8_gemv_max_m(void) { return gemv_max_m(); }

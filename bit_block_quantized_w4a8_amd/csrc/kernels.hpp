@@ -115,9 +115,26 @@ int launch_mx_linear(const uint16_t* x, const uint8_t* packed, const uint8_t* ws
 // Decode attention over an fp16 KV cache (attention.hip).
 int attention_chunks(int length);
 size_t attention_scratch_bytes(int n_kv_heads, int group, int head_dim, int length);
+// The library's exchange area of the flagged-word merge (device memory,
+// zeroed once): for each of `heads` KV heads a fixed region of
+// kAttnHeadWords 64-bit words of partials and an epoch word, and the device
+// error word.  A KV head's words always sit in its own region, whatever the
+// call's shape, so every word only ever carries flags of that head's epoch,
+// which rises with every call: a word left by an earlier call never shows the
+// current flag.
+struct AttnExchange {
+  uint64_t* ll = nullptr;
+  uint32_t* epochs = nullptr;
+  int heads = 0;
+  uint32_t* error = nullptr;
+};
+constexpr int kAttnHeads = 16;                     // KV heads the flagged-word merge serves
+constexpr size_t kAttnHeadWords = 32 * 8 * 258;     // 32 chunks x 8 query heads x (256 dims + 2)
+// Whether a call of this shape merges through the exchange area.
+bool attention_ll_fits(int n_kv_heads, int group, int head_dim, int length, const AttnExchange* ex);
 int launch_decode_attention(const float* q, const float* k_new, const float* v_new, uint16_t* k_cache,
                             uint16_t* v_cache, int n_heads, int n_kv_heads, int head_dim, int length, int capacity,
-                            uint16_t* out, Scratch* sc, hipStream_t stream);
+                            uint16_t* out, Scratch* sc, const AttnExchange* ex, hipStream_t stream);
 
 int gemv_max_m();
 // Kernel W4A8_PATH_AUTO picks for an M x K by K x N linear.

@@ -296,6 +296,30 @@ W4A8_API int w4a8_decoder_stack(float* x, int64_t M, int64_t H, const w4a8_weigh
                                 float residual_scale, float eps, void* workspace, size_t workspace_bytes,
                                 hipStream_t stream);
 
+/*
+ * One decode token through a decoder layer with attention between the qkv
+ * and o projections (the pages decode an LLM with an fp16 KV cache at context
+ * 640: ML Drift explainer on tech.dede.sh, section "Stage-aware optimization
+ * for large language models"):
+ *   n1 = fp16(x / rms(x)); q = L(n1; qkv) (fp32, qkv.N = (n_heads + 2 n_kv_heads)
+ *   head_dim values: the query heads, then one key and one value per KV head)
+ *   a  = w4a8_decode_attention(queries, key, value over the caches at `length`)
+ *   x += s * L(a; o); then the feed-forward half as in w4a8_decoder_layer.
+ * x fp32 [1][H] with H = n_heads * head_dim; caches, limits and errors as for
+ * w4a8_decode_attention (the call writes the new key and value at position
+ * length - 1).  Five launches: the qkv GEMV with the normalisation in its
+ * prologue, decode attention, and the o, gate/up and down GEMVs of the
+ * one-token layer.  The workspace (w4a8_decoder_layer_workspace for M = 1)
+ * receives q, a (the attention output), o, g, u and d.  The one-token GEMV
+ * launches must support the shape (as for W4A8_LAYER_GEMV4).
+ */
+W4A8_API int w4a8_decoder_layer_attention(float* x, int64_t H, const w4a8_weights* qkv, const w4a8_weights* o,
+                                          const w4a8_weights* gate_up, const w4a8_weights* down,
+                                          float residual_scale, float eps, uint16_t* k_cache, uint16_t* v_cache,
+                                          int64_t n_heads, int64_t n_kv_heads, int64_t head_dim, int64_t length,
+                                          int64_t capacity, void* workspace, size_t workspace_bytes,
+                                          hipStream_t stream);
+
 /* How w4a8_decoder_layer runs a layer of this shape on the current device. */
 #define W4A8_LAYER_CHAIN 0     /* separate linears with glue kernels (nine launches) */
 #define W4A8_LAYER_GEMM 1      /* prefill GEMMs with fused glue (six launches) */

@@ -14,7 +14,7 @@ def lib():
 
 def test_exports_every_declared_symbol(lib):
     names = w4.declared_functions()
-    assert len(names) == 33, names
+    assert len(names) == 34, names
     for name in names:
         assert hasattr(lib, name), name
 
@@ -222,3 +222,23 @@ def test_decoder_stack_validates(lib):
     t = table(2)
     t[4 * 1 + 1] = w4._CWeights(ALIGNED, ALIGNED, 2048, 1024)   # o not H x H
     assert call(t, 2) == w4.W4A8_EINVAL
+
+
+def test_decoder_layer_attention_validates(lib):
+    """Shape rules of the layer with attention: H = n_heads * head_dim, qkv.N = (n_heads + 2 n_kv_heads)
+    * head_dim, length <= capacity; a valid call without init is ENOINIT."""
+    def cw(k, n):
+        return ctypes.byref(w4._CWeights(ALIGNED, ALIGNED, k, n))
+
+    def call(h=2048, nq=2560, hq=8, hkv=1, d=256, length=513, cap=640, ws=1 << 30):
+        return lib.w4a8_decoder_layer_attention(P(ALIGNED), h, cw(h, nq), cw(h, h), cw(h, 16384), cw(8192, h),
+                                                ctypes.c_float(0.01), ctypes.c_float(1e-6), P(ALIGNED), P(ALIGNED),
+                                                hq, hkv, d, length, cap, P(ALIGNED), ws, None)
+
+    assert call() == w4.W4A8_ENOINIT
+    assert call(hq=4) == w4.W4A8_EINVAL            # 4 x 256 != 2048
+    assert call(nq=2304) == w4.W4A8_EINVAL         # no room for the value head
+    assert call(length=641) == w4.W4A8_EINVAL
+    assert call(cap=600) == w4.W4A8_EINVAL
+    assert call(d=96) == w4.W4A8_EINVAL
+    assert call(ws=64) == w4.W4A8_EINVAL

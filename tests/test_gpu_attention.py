@@ -157,3 +157,19 @@ def test_decode_attention_reads_qkv_row_slices():
                               kd, vd, 600).cpu().numpy()
     exact, mag = at.decode_attention_exact(q, k_new, v_new, k_past, v_past)
     check(got, exact, mag, "QKV row slices")
+
+
+def test_flagged_merge_regions_across_shapes():
+    """Calls of different shapes alternate on the flagged-word merge (at most 32 chunks, at
+    most 16 KV heads): each KV head keeps its own region of flagged words, so a word an
+    earlier call of another shape left behind never passes for the current call's.  (A
+    layout indexed by the call's shape failed exactly this: a three-head call after a
+    one-head call read head 1's words from the earlier call's head 0.)"""
+    shapes = [(8, 1, 256, 640, 640), (3, 3, 64, 77, 128), (8, 8, 128, 200, 256), (8, 1, 256, 64, 64),
+              (6, 3, 64, 100, 128), (16, 2, 256, 2048, 2112), (3, 3, 64, 77, 128), (8, 1, 256, 640, 640)]
+    for i, (hq, hkv, d, length, cap) in enumerate(shapes):
+        q, k_new, v_new, k_past, v_past = attention_inputs(500 + i, hq, hkv, d, length)
+        got = run(q, k_new, v_new, k_past, v_past, cap, 500 + i)
+        exact, mag = at.decode_attention_exact(q, k_new, v_new, k_past, v_past)
+        check(got, exact, mag, f"call {i}: Hq={hq} Hkv={hkv} D={d} L={length}")
+    assert w4.take_device_errors() == 0
