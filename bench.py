@@ -326,13 +326,14 @@ def bench_wide(w4, torch, synth, timer, iters):
         x = torch.from_numpy(synth.workload_inputs("wide", m)["wide"][0]).to(dev)
         out = torch.empty((m, n), dtype=torch.float32, device=dev)
         row = {}
-        for path, name in ((w4.PATH_GEMV, "gemv"), (w4.PATH_GEMM, "gemm")):
+        paths = ((w4.PATH_GEMV, "gemv"), (w4.PATH_GEMM, "gemm")) + (((w4.PATH_BATCH, "batch"),) if m <= 16 else ())
+        for path, name in paths:
             for i in range(3):
                 w4.linear(x, *reps[i % r], path=path, out=out)
             us = 1000.0 * back_to_back(torch, timer, lambda i: w4.linear(x, *reps[i % r], path=path, out=out), iters)
             b = algorithmic_bytes(m, k, n)
             row[name] = {"us": round(us, 2), "GB_s": round(b / us / 1e3, 1)}
-        row["auto"] = "gemv" if w4.auto_path(m, k, n) == w4.PATH_GEMV else "gemm"
+        row["auto"] = {w4.PATH_GEMV: "gemv", w4.PATH_GEMM: "gemm", w4.PATH_BATCH: "batch"}[w4.auto_path(m, k, n)]
         res[f"M={m}"] = row
     return {"K": k, "N": n, "replicas": r, "results": res}
 

@@ -19,7 +19,7 @@ import re
 import torch
 
 __all__ = [
-    "PATH_AUTO", "PATH_GEMV", "PATH_GEMM", "W4A8Error", "library_path", "load_library",
+    "PATH_AUTO", "PATH_GEMV", "PATH_GEMM", "PATH_BATCH", "W4A8Error", "library_path", "load_library",
     "declared_functions", "init", "pack_weights", "linear", "linear_argmax",
     "quantize_act", "block_sums", "gemv_max_m", "auto_path", "mx_pack_weights", "mx_quantize_act", "mx_linear", "kv_cache", "decode_attention", "Weights", "residual_norm_cast",
     "decoder_layer_workspace", "decoder_layer", "reserve_scratch", "scratch_capacity", "linear_scratch_bytes",
@@ -29,7 +29,7 @@ __all__ = [
     "LAYER_RESIDENT",
 ]
 
-PATH_AUTO, PATH_GEMV, PATH_GEMM = 0, 1, 2
+PATH_AUTO, PATH_GEMV, PATH_GEMM, PATH_BATCH = 0, 1, 2, 3
 LAYER_CHAIN, LAYER_GEMM, LAYER_GEMV4, LAYER_RESIDENT = 0, 1, 2, 3
 OPTION_RESIDENT_LAYER = 1
 W4A8_OK, W4A8_EINVAL, W4A8_EUNSUPPORTED, W4A8_EHIP, W4A8_ENOINIT = 0, -1, -2, -3, -4
@@ -401,7 +401,7 @@ def decode_attention(q: torch.Tensor, k_new: torch.Tensor, v_new: torch.Tensor, 
 
 
 def auto_path(m: int, k: int, n: int) -> int:
-    """PATH_GEMV or PATH_GEMM: the kernel PATH_AUTO runs for an m x k by k x n linear."""
+    """PATH_GEMV, PATH_GEMM or PATH_BATCH: the kernel PATH_AUTO runs for an m x k by k x n linear."""
     return int(load_library().w4a8_auto_path(m, k, n))
 
 

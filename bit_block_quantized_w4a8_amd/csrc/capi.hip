@@ -223,7 +223,7 @@ int layer_kernel(const DeviceState* st, int64_t M, int64_t H, int64_t n_qkv, int
 
 size_t linear_scratch(int64_t M, int64_t K, int64_t N, int path) {
   if (path == W4A8_PATH_AUTO) path = auto_path(M, K, N);
-  if (path == W4A8_PATH_GEMV) return 0;
+  if (path == W4A8_PATH_GEMV || path == W4A8_PATH_BATCH) return 0;
   return gemm_scratch_bytes(static_cast<int>(M), static_cast<int>(K), static_cast<int>(N));
 }
 
@@ -385,11 +385,26 @@ int w4a8_scratch_capacity(size_t* bytes) {
   return W4A8_OK;
 }
 
+namespace {
+// W4A8_EINVAL unless `path` names a kernel that can run an M x K by K x N product.
+int check_path(int path, int64_t M, int64_t K, int64_t N) {
+  W4A8_REQUIRE(path == W4A8_PATH_AUTO || path == W4A8_PATH_GEMV || path == W4A8_PATH_GEMM ||
+                   path == W4A8_PATH_BATCH,
+               "unknown path %d", path);
+  W4A8_REQUIRE(path != W4A8_PATH_BATCH || (M <= 16 && K % 256 == 0 && skinny_supported(static_cast<int>(M),
+                                                                                       static_cast<int>(K),
+                                                                                       static_cast<int>(N))),
+               "W4A8_PATH_BATCH takes M <= 16 and K a multiple of 256 (M = %lld, K = %lld)",
+               static_cast<long long>(M), static_cast<long long>(K));
+  return W4A8_OK;
+}
+}  // namespace
+
 int w4a8_linear_scratch_bytes(int64_t M, int64_t K, int64_t N, int path, size_t* bytes) {
   W4A8_REQUIRE(bytes, "null pointer");
-  const int rc = check_shape(M, K, N, int64_t{1} << 20);
+  int rc = check_shape(M, K, N, int64_t{1} << 20);
   if (rc != W4A8_OK) return rc;
-  W4A8_REQUIRE(path == W4A8_PATH_AUTO || path == W4A8_PATH_GEMV || path == W4A8_PATH_GEMM, "unknown path %d", path);
+  if ((rc = check_path(path, M, K, N)) != W4A8_OK) return rc;
   *bytes = linear_scratch(M, K, N, path);
   return W4A8_OK;
 }
@@ -455,10 +470,14 @@ int linear_on(const uint16_t* x, const uint8_t* packed_w, const uint16_t* w_scal
                out, nullptr, nullptr, nullptr};
     return launch_gemv(a, 0, sc, stream);
   }
+  if (path == W4A8_PATH_BATCH)
+    return launch_skinny(x, packed_w, w_scales, static_cast<int>(M), static_cast<int>(K), static_cast<int>(N), out,
+                         nullptr, stream);
   GemmArgs a{x, packed_w, w_scales, static_cast<int>(M), static_cast<int>(K), static_cast<int>(N), out,
              nullptr};
   return launch_gemm(a, 0, sc, stream);
 }
+
 }  // namespace
 
 int w4a8_linear_path(const uint16_t* x, const uint8_t* packed_w, const uint16_t* w_scales, int64_t M,
@@ -467,8 +486,7 @@ int w4a8_linear_path(const uint16_t* x, const uint8_t* packed_w, const uint16_t*
   if (rc != W4A8_OK) return rc;
   W4A8_REQUIRE(out, "null output pointer");
   W4A8_REQUIRE(aligned(out, 16), "out must be 16-byte aligned");
-  W4A8_REQUIRE(path == W4A8_PATH_AUTO || path == W4A8_PATH_GEMV || path == W4A8_PATH_GEMM,
-               "unknown path %d", path);
+  if ((rc = check_path(path, M, K, N)) != W4A8_OK) return rc;
   Scratch* sc = nullptr;
   rc = library_scratch(&sc);
   if (rc != W4A8_OK) return rc;
@@ -537,14 +555,16 @@ int w4a8_block_sums(const uint16_t* x, const uint8_t* packed_w, int64_t M, int64
                              int64_t{1} << 16);
   if (rc != W4A8_OK) return rc;
   W4A8_REQUIRE(sums && aligned(sums, 16), "sums must be a 16-byte aligned pointer");
-  W4A8_REQUIRE(path == W4A8_PATH_AUTO || path == W4A8_PATH_GEMV || path == W4A8_PATH_GEMM,
-               "unknown path %d", path);
+  if ((rc = check_path(path, M, K, N)) != W4A8_OK) return rc;
   Scratch* sc = nullptr;
   rc = library_scratch(&sc);
   if (rc != W4A8_OK) return rc;
   if (path == W4A8_PATH_AUTO) path = auto_path(M, K, N);
   rc = require_scratch(sc, linear_scratch(M, K, N, path));
   if (rc != W4A8_OK) return rc;
+  if (path == W4A8_PATH_BATCH)
+    return launch_skinny(x, packed_w, nullptr, static_cast<int>(M), static_cast<int>(K), static_cast<int>(N),
+                         nullptr, sums, stream);
   if (path == W4A8_PATH_GEMV) {
     GemvArgs a{x, packed_w, nullptr, static_cast<int>(M), static_cast<int>(K), static_cast<int>(N),
                nullptr, sums, nullptr, nullptr};

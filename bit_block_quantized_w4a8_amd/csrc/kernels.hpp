@@ -136,6 +136,13 @@ int launch_decode_attention(const float* q, const float* k_new, const float* v_n
                             uint16_t* v_cache, int n_heads, int n_kv_heads, int head_dim, int length, int capacity,
                             uint16_t* out, Scratch* sc, const AttnExchange* ex, hipStream_t stream);
 
+// Small-batch decode kernel (skinny.hip): M = 1 .. 16 rows on the int8 matrix
+// instruction, every weight read once; K a multiple of 256, N of 64.  `sums`
+// (int32 [M][N][K/32]) selects the block-sum export instead of `out`.
+bool skinny_supported(int M, int K, int N);
+int launch_skinny(const uint16_t* x, const uint8_t* packed_w, const uint16_t* w_scales, int M, int K, int N,
+                  float* out, int32_t* sums, hipStream_t stream);
+
 int gemv_max_m();
 // Kernel W4A8_PATH_AUTO picks for an M x K by K x N linear.
 int auto_path(int64_t M, int64_t K, int64_t N);

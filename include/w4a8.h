@@ -65,6 +65,8 @@ extern "C" {
 #define W4A8_PATH_AUTO 0  /* decode GEMV or prefill MFMA GEMM by shape: w4a8_auto_path */
 #define W4A8_PATH_GEMV 1  /* force the decode GEMV (any M; slow for large M) */
 #define W4A8_PATH_GEMM 2  /* force the quantise pre-pass + MFMA GEMM (any M) */
+#define W4A8_PATH_BATCH 3 /* force the small-batch kernel: M <= 16 rows on the int8 MFMA, every weight read
+                             once, activations quantised in the kernel (K a multiple of 256) */
 
 /*
  * Select `device`, check that it is gfx950 and allocate the library's scratch

@@ -45,7 +45,7 @@ def _linear(lib, x=ALIGNED, pw=ALIGNED, ws=ALIGNED, m=1, k=64, n=128, out=ALIGNE
     dict(m=0), dict(m=-3), dict(k=0), dict(k=48), dict(k=16), dict(n=0), dict(n=96), dict(n=32),
     dict(x=ALIGNED + 2), dict(x=ALIGNED + 8), dict(pw=ALIGNED + 8), dict(ws=ALIGNED + 2), dict(ws=ALIGNED + 8),
     dict(out=ALIGNED + 4),
-    dict(path=3), dict(path=-1),
+    dict(path=4), dict(path=-1), dict(path=3, m=17, k=256), dict(path=3, k=288), dict(path=3, k=64),
 ])
 def test_linear_rejects_bad_arguments(lib, kw):
     assert _linear(lib, **kw) == w4.W4A8_EINVAL
@@ -54,6 +54,7 @@ def test_linear_rejects_bad_arguments(lib, kw):
 
 def test_valid_arguments_need_init(lib):
     assert _linear(lib) == w4.W4A8_ENOINIT
+    assert _linear(lib, m=16, k=256, path=w4.PATH_BATCH) == w4.W4A8_ENOINIT
     assert b"w4a8_init" in lib.w4a8_last_error()
 
 
@@ -144,13 +145,15 @@ def test_scratch_sizes_on_the_host(lib):
     nb, m_pad = 2048 // 32, 512
     assert w4.linear_scratch_bytes(512, 2048, 16384) == nb * m_pad * 32 + nb * m_pad * 4
     assert w4.linear_scratch_bytes(512, 2048, 16384, w4.PATH_GEMM) == nb * m_pad * 32 + nb * m_pad * 4
+    assert w4.linear_scratch_bytes(16, 4096, 14336, w4.PATH_BATCH) == 0
     assert w4.norm_linear_argmax_scratch_bytes(1, 2048, 262144) == 0
     assert w4.norm_linear_argmax_scratch_bytes(2, 256, 4096) == 2 * 256 * 2
     assert w4.mx_linear_scratch_bytes(512, 2048, 2560) == 512 * 2048 + 512 * 64
     assert w4.decode_attention_scratch_bytes(8, 1, 256, 640) > 0
 
 
-@pytest.mark.parametrize("args", [(0, 64, 64, 0), (1, 48, 64, 0), (1, 64, 96, 0), (1, 64, 64, 7)])
+@pytest.mark.parametrize("args", [(0, 64, 64, 0), (1, 48, 64, 0), (1, 64, 96, 0), (1, 64, 64, 7),
+                                  (17, 256, 64, 3), (1, 288, 64, 3)])
 def test_scratch_queries_reject_bad_shapes(lib, args):
     n = ctypes.c_size_t(0)
     assert lib.w4a8_linear_scratch_bytes(*args, ctypes.byref(n)) == w4.W4A8_EINVAL
