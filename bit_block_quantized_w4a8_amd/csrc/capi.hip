@@ -169,14 +169,22 @@ int gemv_max_m() {
 // quantises all M rows of x it reads and forms M dot products per weight
 // load) while the GEMM's barely moves at small M, so the crossover falls with
 // the size of the weight matrix: measured on MI355X with cold weights, the GEMV
-// is faster through M = 4 for 2048 x 2560, 2048 x 16384 and 8192 x 2048, but
-// only through M = 2 for 4096 x 14336 (2^25.8 values).  W4A8_GEMV_MAX_M in the
-// environment replaces the rule by a plain M threshold.
+// is the fastest through M = 4 for 2048 x 2560, 2048 x 16384 and 8192 x 2048,
+// but only through M = 2 for 4096 x 14336 (2^25.8 values).  Above that and up
+// to 16 rows the small-batch kernel beats both (4096 x 14336: 11.5 - 11.9 us
+// at M = 3 - 8 and 14.2 us at M = 16, against the GEMM's 16.6 us), except
+// where few 64-column workgroups each stream a long K (8192 x 2048: 32
+// workgroups, two rounds), which stays on the GEMM.  W4A8_GEMV_MAX_M in the
+// environment replaces the rule by a plain M threshold between GEMV and GEMM.
 int auto_path(int64_t M, int64_t K, int64_t N) {
   const int lim = gemv_max_m();
   if (g_gemv_max_m_forced) return M <= lim ? W4A8_PATH_GEMV : W4A8_PATH_GEMM;
   const bool big = K * N > (int64_t{1} << 25);
-  return M <= (big ? (lim < 2 ? lim : 2) : lim) ? W4A8_PATH_GEMV : W4A8_PATH_GEMM;
+  if (M <= (big ? (lim < 2 ? lim : 2) : lim)) return W4A8_PATH_GEMV;
+  if (M <= 16 && skinny_supported(static_cast<int>(M), static_cast<int>(K), static_cast<int>(N)) &&
+      (N >= 8192 || K <= 4096))
+    return W4A8_PATH_BATCH;
+  return W4A8_PATH_GEMM;
 }
 
 namespace {

@@ -62,7 +62,7 @@ extern "C" {
 #define W4A8_ENOINIT      -4  /* w4a8_init has not succeeded on the current device */
 
 /* Kernel selection for w4a8_linear_path / w4a8_block_sums. */
-#define W4A8_PATH_AUTO 0  /* decode GEMV or prefill MFMA GEMM by shape: w4a8_auto_path */
+#define W4A8_PATH_AUTO 0  /* decode GEMV, small-batch kernel or prefill MFMA GEMM by shape: w4a8_auto_path */
 #define W4A8_PATH_GEMV 1  /* force the decode GEMV (any M; slow for large M) */
 #define W4A8_PATH_GEMM 2  /* force the quantise pre-pass + MFMA GEMM (any M) */
 #define W4A8_PATH_BATCH 3 /* force the small-batch kernel: M <= 16 rows on the int8 MFMA, every weight read
@@ -122,8 +122,10 @@ W4A8_API int w4a8_pack_weights(const int8_t* q, const uint16_t* s, int64_t K, in
  *   x         fp16 [M][K], 16-byte aligned
  *   packed_w, w_scales as produced by w4a8_pack_weights, both 16-byte aligned
  * Stage choice (w4a8_auto_path): few rows run the decode GEMV, which quantises
- * the activations inside the kernel; more rows run a quantise pre-pass into
- * library scratch followed by the int8-MFMA prefill GEMM.
+ * the activations inside the kernel; up to 16 rows the small-batch kernel,
+ * which also quantises in the kernel and forms the block sums on the int8
+ * matrix instruction; more rows run a quantise pre-pass into library scratch
+ * followed by the int8-MFMA prefill GEMM.
  */
 W4A8_API int w4a8_linear(const uint16_t* x, const uint8_t* packed_w, const uint16_t* w_scales,
                 int64_t M, int64_t K, int64_t N, float* out, hipStream_t stream);
@@ -367,12 +369,16 @@ W4A8_API int w4a8_gemv_max_m(void);
 
 /*
  * Kernel that W4A8_PATH_AUTO runs for an M x K by K x N linear
- * (W4A8_PATH_GEMV or W4A8_PATH_GEMM).  The pages run one kernel per inference
- * stage (ML Drift explainer on tech.dede.sh, section "Stage-aware optimization
- * for large language models"); the row thresholds are measured on MI355X: the
- * decode GEMV for M <= 2, and up to M = w4a8_gemv_max_m() for weight matrices
- * of at most 2^25 values; the prefill GEMM otherwise.  The environment variable W4A8_GEMV_MAX_M replaces the
- * rule by the plain threshold M <= W4A8_GEMV_MAX_M.  Host-only; no error cases.
+ * (W4A8_PATH_GEMV, W4A8_PATH_BATCH or W4A8_PATH_GEMM).  The pages run one
+ * kernel per inference stage (ML Drift explainer on tech.dede.sh, section
+ * "Stage-aware optimization for large language models"); the row thresholds
+ * are measured on MI355X: the decode GEMV for M <= 2, and up to
+ * M = w4a8_gemv_max_m() for weight matrices of at most 2^25 values; then up
+ * to M = 16 the small-batch kernel where it runs (K a multiple of 256, N of
+ * 64) and either N >= 8192 or K <= 4096; the prefill GEMM otherwise.  The
+ * environment variable W4A8_GEMV_MAX_M replaces the rule by the plain
+ * threshold M <= W4A8_GEMV_MAX_M between GEMV and GEMM.  Host-only; no error
+ * cases.
  */
 W4A8_API int w4a8_auto_path(int64_t M, int64_t K, int64_t N);
 

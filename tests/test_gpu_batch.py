@@ -140,6 +140,21 @@ def test_repeat_runs_are_bit_identical():
     assert np.array_equal(a.view(np.int32), b.view(np.int32))
 
 
+def test_every_step_waits_for_both_quantiser_waves():
+    """Repeated calls at shapes whose MFMAs start as soon as a step's activations are in
+    LDS: every call must match the oracle (a step may not start on one quantiser wave's
+    half of the rows)."""
+    for m, k, n in [(16, 2048, 128), (16, 1024, 64), (11, 2048, 192)]:
+        x, qw, sw = synth.linear_inputs(m + k + n, m, k, n, outliers=True)
+        packed, ws = w4.pack_weights(dev(qw), dev(sw))
+        xd = dev(x)
+        qx, _ = oracle.quantize_activations(x)
+        ref = oracle.block_sums(qx, qw)
+        for rep in range(20):
+            got = host(w4.block_sums(xd, packed, path=BATCH)).astype(np.int64)
+            assert np.array_equal(got, ref), f"M={m} K={k} N={n} call {rep}"
+
+
 def test_rejected_shapes_raise():
     x, qw, sw = synth.linear_inputs(6, 17, 256, 64)
     packed, ws = w4.pack_weights(dev(qw), dev(sw))
