@@ -170,21 +170,23 @@ int gemv_max_m() {
 // load) while the GEMM's barely moves at small M, so the crossover falls with
 // the size of the weight matrix: measured on MI355X with cold weights, the GEMV
 // is the fastest through M = 4 for 2048 x 2560, 2048 x 16384 and 8192 x 2048,
-// but only through M = 2 for 4096 x 14336 (2^25.8 values).  Above that and up
-// to 16 rows the small-batch kernel beats both (4096 x 14336: 11.5 - 11.9 us
-// at M = 3 - 8 and 14.2 us at M = 16, against the GEMM's 16.6 us), except
-// where few 64-column workgroups each stream a long K (8192 x 2048: 32
-// workgroups, two rounds), which stays on the GEMM.  W4A8_GEMV_MAX_M in the
-// environment replaces the rule by a plain M threshold between GEMV and GEMM.
+// but only through M = 2 for 4096 x 14336 (2^25.8 values).  From M = 2 on
+// such large matrices, and above the GEMV's rows elsewhere, up to 16 rows the
+// small-batch kernel beats both (4096 x 14336: 11.7 us at M = 2, against the
+// GEMV's 12.8; 11.7 - 11.9 us at M = 3 - 8 and 14.8 us at M = 16, against the
+// GEMM's 16.6 - 17.6 us), except where few 64-column workgroups each stream a
+// long K (8192 x 2048: 32 workgroups, two rounds), which stays on the GEMM.
+// W4A8_GEMV_MAX_M in the environment replaces the rule by a plain M threshold
+// between GEMV and GEMM.
 int auto_path(int64_t M, int64_t K, int64_t N) {
   const int lim = gemv_max_m();
   if (g_gemv_max_m_forced) return M <= lim ? W4A8_PATH_GEMV : W4A8_PATH_GEMM;
   const bool big = K * N > (int64_t{1} << 25);
+  const bool batch = M <= 16 && skinny_supported(static_cast<int>(M), static_cast<int>(K), static_cast<int>(N)) &&
+                     (N >= 8192 || K <= 4096);
+  if (big && M >= 2 && batch) return W4A8_PATH_BATCH;
   if (M <= (big ? (lim < 2 ? lim : 2) : lim)) return W4A8_PATH_GEMV;
-  if (M <= 16 && skinny_supported(static_cast<int>(M), static_cast<int>(K), static_cast<int>(N)) &&
-      (N >= 8192 || K <= 4096))
-    return W4A8_PATH_BATCH;
-  return W4A8_PATH_GEMM;
+  return batch ? W4A8_PATH_BATCH : W4A8_PATH_GEMM;
 }
 
 namespace {

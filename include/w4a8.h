@@ -372,10 +372,11 @@ W4A8_API int w4a8_gemv_max_m(void);
  * (W4A8_PATH_GEMV, W4A8_PATH_BATCH or W4A8_PATH_GEMM).  The pages run one
  * kernel per inference stage (ML Drift explainer on tech.dede.sh, section
  * "Stage-aware optimization for large language models"); the row thresholds
- * are measured on MI355X: the decode GEMV for M <= 2, and up to
- * M = w4a8_gemv_max_m() for weight matrices of at most 2^25 values; then up
- * to M = 16 the small-batch kernel where it runs (K a multiple of 256, N of
- * 64) and either N >= 8192 or K <= 4096; the prefill GEMM otherwise.  The
+ * are measured on MI355X: the decode GEMV for M = 1, for M = 2 too where
+ * the small-batch kernel does not run, and up to M = w4a8_gemv_max_m() for
+ * weight matrices of at most 2^25 values; then up to M = 16 the small-batch
+ * kernel where it runs (K a multiple of 256, N of 64) and either N >= 8192 or
+ * K <= 4096; the prefill GEMM otherwise.  The
  * environment variable W4A8_GEMV_MAX_M replaces the rule by the plain
  * threshold M <= W4A8_GEMV_MAX_M between GEMV and GEMM.  Host-only; no error
  * cases.

@@ -24,14 +24,15 @@ def test_gemv_threshold(lib):
 
 
 def test_auto_path_rule():
-    """Host-side stage rule: GEMV through M = 2 always, through M = 4 for weight matrices of at
-    most 2^25 values; then the small-batch kernel through M = 16 where it runs and either
-    N >= 8192 or K <= 4096; the GEMM above (the environment override is not set under pytest)."""
+    """Host-side stage rule: GEMV at M = 1, at M = 2 too where the small-batch kernel does not
+    run, and through M = 4 for weight matrices of at most 2^25 values; then the small-batch kernel
+    through M = 16 where it runs and either N >= 8192 or K <= 4096; the GEMM above (the
+    environment override is not set under pytest)."""
     gemv, gemm, batch = w4.PATH_GEMV, w4.PATH_GEMM, w4.PATH_BATCH
     for k, n in [(2048, 2560), (2048, 16384)]:
         assert [w4.auto_path(m, k, n) for m in (1, 2, 3, 4, 5, 16, 17, 512)] == [gemv] * 4 + [batch] * 2 + [gemm] * 2
     assert [w4.auto_path(m, 8192, 2048) for m in (1, 4, 5, 16, 512)] == [gemv, gemv, gemm, gemm, gemm]
-    assert [w4.auto_path(m, 4096, 14336) for m in (1, 2, 3, 4, 8, 16, 17)] == [gemv] * 2 + [batch] * 4 + [gemm]
+    assert [w4.auto_path(m, 4096, 14336) for m in (1, 2, 3, 4, 8, 16, 17)] == [gemv] + [batch] * 5 + [gemm]
     # outside the small-batch kernel's shapes (K not a multiple of 256) the GEMM takes over
     assert [w4.auto_path(m, 4128, 14336) for m in (2, 3, 16)] == [gemv, gemm, gemm]
 
