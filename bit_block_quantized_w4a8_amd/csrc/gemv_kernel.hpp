@@ -221,15 +221,26 @@ __global__ __launch_bounds__(T) void gemv_kernel(GemvArgs a, uint32_t* __restric
       for (int j = 0; j < XQ; ++j) xv[j] = load_x16<MR>(x, K, kb0, nbc, min(j * T + tid, tasks - 1));
     }
     __builtin_amdgcn_sched_barrier(0);  // keep the activation loads ahead of the weights
+    // With 8 or more loads per lane, the weight loads go in two halves: the
+    // first before the quantisation, the second after the barrier that
+    // publishes the codes.  A CU accepts loads only as fast as the memory
+    // system drains them, so a wave that issued all of its loads first would
+    // reach the barrier late and hold every other wave's dot products back
+    // until then; with the split, the dot products of the first half run while
+    // the second half streams in (gate_up 2048 x 16384: 5.81 -> 5.42 us).  With
+    // 2 or 4 loads per lane the split lost (qkv 3.33 -> 3.47 us, o 2.99 ->
+    // 3.23 us).
+    constexpr int RH = R >= 8 ? R / 2 : R;
     uint4 w[R];
     uint32_t s[R];
-#pragma unroll
-    for (int r = 0; r < R; ++r) {
+    auto load_weights = [&](int r) __attribute__((always_inline)) {
       const int bl = min(slot + r * S, nbc - 1);
       const int64_t g = static_cast<int64_t>(kb0 + bl) * N + n;
       w[r] = *reinterpret_cast<const uint4*>(pw + g * kPackedBytes);
       s[r] = MODE == kGemvSums ? 0u : ws[g];  // the block-sum export reads no scales
-    }
+    };
+#pragma unroll
+    for (int r = 0; r < RH; ++r) load_weights(r);
     __builtin_amdgcn_sched_barrier(0);
 
     // 2. Quantise into LDS.
@@ -342,6 +353,9 @@ __global__ __launch_bounds__(T) void gemv_kernel(GemvArgs a, uint32_t* __restric
     // wave reads its own codes back without a workgroup barrier.
     if constexpr (kWaveQuant) __builtin_amdgcn_wave_barrier();
     else __syncthreads();
+#pragma unroll
+    for (int r = RH; r < R; ++r) load_weights(r);
+    __builtin_amdgcn_sched_barrier(0);
 
     // 3. Integer block dots and the fp32 epilogue.
 #pragma unroll
