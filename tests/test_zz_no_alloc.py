@@ -59,8 +59,10 @@ def test_noalloc_matches_linear_on_consecutive_calls():
               (8, 8192, 2048),     # smaller: split-K GEMM, tickets in the static scratch
               (1, 2048, 16384),    # decode GEMV (no scratch)
               (512, 8192, 2048),   # larger again (staging 4.7 MB)
-              (40, 2048, 2048)]    # smaller again
+              (40, 2048, 2048),    # smaller again
+              (12, 2048, 16384)]   # small-batch kernel (no scratch)
     assert w4.auto_path(8, 8192, 2048) == w4.PATH_GEMM and w4.auto_path(1, 2048, 16384) == w4.PATH_GEMV
+    assert w4.auto_path(12, 2048, 16384) == w4.PATH_BATCH
     for i, (m, k, n) in enumerate(shapes):
         assert w4.linear_scratch_bytes(m, k, n) <= size.value
         run_case(100 + i, m, k, n)
