@@ -97,6 +97,27 @@ __device__ __forceinline__ uint64_t ll_get(const uint64_t* p) {
   return __hip_atomic_load(const_cast<uint64_t*>(p), __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
 }
 
+// Max or sum over each 32-lane half of a wave, the result in all its lanes:
+// DPP within quads (lane ^ 1, lane ^ 2), within 8-lane and 16-lane rows
+// (mirrors), then the two 16-lane rows of the half (v_permlane16_swap).  The
+// pairing is that of a lane ^ 1, 2, 4, 8, 16 butterfly, so every lane forms the
+// same sums in the same order; no LDS traffic.
+template <bool kMax>
+__device__ __forceinline__ float half_wave_reduce(float v) {
+  auto op = [](float x, float y) { return kMax ? fmaxf(x, y) : x + y; };
+  v = op(v, __int_as_float(__builtin_amdgcn_mov_dpp(__float_as_int(v), 0xB1, 0xF, 0xF, true)));   // quad_perm [1,0,3,2]
+  v = op(v, __int_as_float(__builtin_amdgcn_mov_dpp(__float_as_int(v), 0x4E, 0xF, 0xF, true)));   // quad_perm [2,3,0,1]
+  v = op(v, __int_as_float(__builtin_amdgcn_mov_dpp(__float_as_int(v), 0x141, 0xF, 0xF, true)));  // row_half_mirror
+  v = op(v, __int_as_float(__builtin_amdgcn_mov_dpp(__float_as_int(v), 0x140, 0xF, 0xF, true)));  // row_mirror
+  const auto r = __builtin_amdgcn_permlane16_swap(__float_as_uint(v), __float_as_uint(v), false, false);
+  return op(__uint_as_float(r[0]), __uint_as_float(r[1]));
+}
+
+// Lanes 0 .. 31 receive lanes 32 .. 63 of v (one v_permlane32_swap).
+__device__ __forceinline__ float upper_half(float v) {
+  return __uint_as_float(__builtin_amdgcn_permlane32_swap(__float_as_uint(v), __float_as_uint(v), false, false)[1]);
+}
+
 __device__ __forceinline__ uint32_t pack2(_Float16 a, _Float16 b) {
   return static_cast<uint32_t>(__builtin_bit_cast(unsigned short, a)) |
          (static_cast<uint32_t>(__builtin_bit_cast(unsigned short, b)) << 16);
@@ -195,6 +216,17 @@ __global__ __launch_bounds__(kThreads) void decode_attention_kernel(AttnArgs a) 
   const int newest = L - 1;
   if (LL && tid == 0) flag_s = __hip_atomic_load(a.epochs + g, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) + 1u;
 
+  // The newest token's key and value (fp32) first: a wave's loads complete in
+  // order, and the chunk that holds position L - 1 needs them before its
+  // scores, so behind the chunk's cache loads they would hold that chunk, and
+  // every merge waiting for it, back.
+  const bool holds_newest = newest >= t0 && newest < t0 + kChunk;  // uniform per workgroup
+  float4 kx = {0.f, 0.f, 0.f, 0.f}, vx = {0.f, 0.f, 0.f, 0.f};
+  if (holds_newest && tid < D / 4) {
+    kx = reinterpret_cast<const float4*>(a.k_new + static_cast<int64_t>(g) * D)[tid];
+    vx = reinterpret_cast<const float4*>(a.v_new + static_cast<int64_t>(g) * D)[tid];
+  }
+
   // 1. Loads.  Key: this lane's position (column `col` of the wave's 16) and
   // its lane group's quarter of the dimensions.  Value: sixteen positions of
   // each of the wave's output dimensions.  Every address lies below the
@@ -239,22 +271,28 @@ __global__ __launch_bounds__(kThreads) void decode_attention_kernel(AttnArgs a) 
   // workgroup rounds them into LDS (four values per thread of its first wave)
   // and writes them to the cache; after the barrier the lanes that hold
   // position L - 1 take them from LDS.
-  const bool holds_newest = newest >= t0 && newest < t0 + kChunk;  // uniform per workgroup
+  // The cache stores themselves wait until the chunk's outputs are out
+  // (write_newest): every workgroup barrier before then would wait for them.
+  uint2 kp = {0u, 0u}, vp = {0u, 0u};
   if (holds_newest && tid < D / 4) {
-    const float4 kx = reinterpret_cast<const float4*>(a.k_new + static_cast<int64_t>(g) * D)[tid];
-    const float4 vx = reinterpret_cast<const float4*>(a.v_new + static_cast<int64_t>(g) * D)[tid];
     const _Float16 k4[4] = {static_cast<_Float16>(kx.x), static_cast<_Float16>(kx.y), static_cast<_Float16>(kx.z),
                             static_cast<_Float16>(kx.w)};
     const _Float16 v4[4] = {static_cast<_Float16>(vx.x), static_cast<_Float16>(vx.y), static_cast<_Float16>(vx.z),
                             static_cast<_Float16>(vx.w)};
-    const uint2 kp = make_uint2(pack2(k4[0], k4[1]), pack2(k4[2], k4[3]));
+    kp = make_uint2(pack2(k4[0], k4[1]), pack2(k4[2], k4[3]));
+    vp = make_uint2(pack2(v4[0], v4[1]), pack2(v4[2], v4[3]));
     *reinterpret_cast<uint2*>(new_k + 4 * tid) = kp;
-    *reinterpret_cast<uint2*>(new_v + 4 * tid) = make_uint2(pack2(v4[0], v4[1]), pack2(v4[2], v4[3]));
-    *reinterpret_cast<uint2*>(a.k_cache + (static_cast<int64_t>(g) * cap + newest) * D + 4 * tid) = kp;
-#pragma unroll
-    for (int i = 0; i < 4; ++i)
-      a.v_cache[(static_cast<int64_t>(g) * D + 4 * tid + i) * cap + newest] = __builtin_bit_cast(unsigned short, v4[i]);
+    *reinterpret_cast<uint2*>(new_v + 4 * tid) = vp;
   }
+  auto write_newest = [&]() __attribute__((always_inline)) {
+    if (holds_newest && tid < D / 4) {
+      *reinterpret_cast<uint2*>(a.k_cache + (static_cast<int64_t>(g) * cap + newest) * D + 4 * tid) = kp;
+      const uint32_t vh[4] = {vp.x & 0xFFFFu, vp.x >> 16, vp.y & 0xFFFFu, vp.y >> 16};
+#pragma unroll
+      for (int i = 0; i < 4; ++i)
+        a.v_cache[(static_cast<int64_t>(g) * D + 4 * tid + i) * cap + newest] = static_cast<uint16_t>(vh[i]);
+    }
+  };
   __syncthreads();
   if (holds_newest) {
     if (tk == newest) {
@@ -293,7 +331,6 @@ __global__ __launch_bounds__(kThreads) void decode_attention_kernel(AttnArgs a) 
 
   // 3. Chunk softmax: thread -> head tid / 32, positions 2 * (tid % 32) + {0, 1};
   // the 32 threads of a head are one half of a wave.
-  float chunk_m = 0.f, chunk_l = 0.f;
   {
     const int h = tid >> 5, tt = 2 * (tid & 31);
     float s[2];
@@ -302,13 +339,9 @@ __global__ __launch_bounds__(kThreads) void decode_attention_kernel(AttnArgs a) 
       const float v = (s_raw[h * kSS + tt + e] + s_raw[(h + kMaxGroup) * kSS + tt + e] * kInvLo) * a.scale2;
       s[e] = t0 + tt + e < L ? v : -INFINITY;
     }
-    float m = fmaxf(s[0], s[1]);
-#pragma unroll
-    for (int o = 1; o < 32; o <<= 1) m = fmaxf(m, __shfl_xor(m, o));
+    const float m = half_wave_reduce<true>(fmaxf(s[0], s[1]));
     const float p0 = exp2f(s[0] - m), p1 = exp2f(s[1] - m);
-    float l = p0 + p1;
-#pragma unroll
-    for (int o = 1; o < 32; o <<= 1) l += __shfl_xor(l, o);
+    const float l = half_wave_reduce<false>(p0 + p1);
     uint32_t hi = 0u, lo = 0u;
     if (h < G) {
       const _Float16 h0 = static_cast<_Float16>(p0), h1 = static_cast<_Float16>(p1);
@@ -317,8 +350,10 @@ __global__ __launch_bounds__(kThreads) void decode_attention_kernel(AttnArgs a) 
                  static_cast<_Float16>((p1 - static_cast<float>(h1)) * kLo));
       if ((tid & 31) == 0) {
         if constexpr (LL) {
-          chunk_m = m;  // stored after the chunk's outputs (step 4)
-          chunk_l = l;
+          // the max and weight sum words follow the head's D output words
+          uint64_t* w = a.ll + static_cast<int64_t>(g) * kAttnHeadWords + (static_cast<int64_t>(c) * G + h) * (D + 2) + D;
+          ll_put(w, m, flag_s);
+          ll_put(w + 1, l, flag_s);
         } else {
           float* st = a.stats + ((static_cast<int64_t>(g) * chunks + c) * G + h) * 2;
           store_agent(st, m);
@@ -334,46 +369,45 @@ __global__ __launch_bounds__(kThreads) void decode_attention_kernel(AttnArgs a) 
   // 4. Chunk output of the wave's D / 4 dimensions: the contraction index of
   // step `ks` is position 16 * lg + 4 * ks + j, matching the value runs.  Rows
   // 0 .. 7 of the result sit in lanes 0 .. 31 and their lo rows 32 lanes up.
+  // Every tile's MFMAs come before the first store: stores count in the
+  // same wait counter as loads, so a tile's wait for its value loads would
+  // otherwise also wait for the previous tiles' stores to be acknowledged.
   {
     h4 pa[4];
 #pragma unroll
     for (int ks = 0; ks < 4; ++ks) pa[ks] = *reinterpret_cast<const h4*>(p_hl + col * kPS + 16 * lg + 4 * ks);
+    f4 acc[kTiles];
 #pragma unroll
     for (int nt = 0; nt < kTiles; ++nt) {
-      f4 acc = {0.f, 0.f, 0.f, 0.f};
+      acc[nt] = f4{0.f, 0.f, 0.f, 0.f};
 #pragma unroll
-      for (int ks = 0; ks < 4; ++ks) acc = __builtin_amdgcn_mfma_f32_16x16x16f16(pa[ks], half4_at(vr[nt], ks), acc, 0, 0, 0);
+      for (int ks = 0; ks < 4; ++ks)
+        acc[nt] = __builtin_amdgcn_mfma_f32_16x16x16f16(pa[ks], half4_at(vr[nt], ks), acc[nt], 0, 0, 0);
+    }
+    const uint32_t flag = LL ? flag_s : 0u;
+#pragma unroll
+    for (int nt = 0; nt < kTiles; ++nt) {
       const int d = wave * (D / 4) + 16 * nt + col;
 #pragma unroll
       for (int j = 0; j < 4; ++j) {
-        const float up = __shfl_down(acc[j], 32);
+        const float up = upper_half(acc[nt][j]);
         const int h = 4 * lg + j;
         if (lane < 32 && h < G) {
           if constexpr (LL)
             ll_put(a.ll + static_cast<int64_t>(g) * kAttnHeadWords + (static_cast<int64_t>(c) * G + h) * (D + 2) + d,
-                   acc[j] + up * kInvLo, flag_s);
+                   acc[nt][j] + up * kInvLo, flag);
           else
-            store_agent(a.part + ((static_cast<int64_t>(g) * chunks + c) * G + h) * D + d, acc[j] + up * kInvLo);
+            store_agent(a.part + ((static_cast<int64_t>(g) * chunks + c) * G + h) * D + d, acc[nt][j] + up * kInvLo);
         }
       }
     }
   }
 
+  write_newest();
   if constexpr (LL) {
-    // The chunk's max and weight sum words go out after a barrier that every
-    // wave reaches once its output words are issued, so a reader that sees a
-    // chunk's max word (the one the merge polls first) finds its outputs
-    // almost always there too.
-    __syncthreads();
-    {
-      const int h = tid >> 5;
-      if ((tid & 31) == 0 && h < G) {
-        uint64_t* w = a.ll + static_cast<int64_t>(g) * kAttnHeadWords + (static_cast<int64_t>(c) * G + h) * (D + 2) + D;
-        ll_put(w, chunk_m, flag_s);
-        ll_put(w + 1, chunk_l, flag_s);
-      }
-    }
-    // 5'. Flagged-word merge.  Items (head h, dims 8 j .. 8 j + 7) i = c,
+    // 5'. Flagged-word merge (no barrier before it: a workgroup barrier's
+    // fence would wait for this workgroup's word stores to be acknowledged,
+    // and a reader checks every word's flag anyway).  Items (head h, dims 8 j .. 8 j + 7) i = c,
     // c + chunks, ...; entry e of this workgroup is item c + chunks * (e /
     // chunks) of chunk e % chunks.
     const uint32_t flag = flag_s;
@@ -439,28 +473,24 @@ __global__ __launch_bounds__(kThreads) void decode_attention_kernel(AttnArgs a) 
     // Workgroup 0 of the head has now read every chunk's words, so every
     // workgroup of the head has read the epoch: advance it for the next call.
     if (c == 0 && tid == 0) __hip_atomic_store(a.epochs + g, flag, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-    if (tid < mine) {
-      const int it = c + chunks * tid;
-      const int h = it / (D / 8), d0 = (it % (D / 8)) * 8;
-      // Online-softmax merge in chunk order (the single-group merge's arithmetic).
-      float m = -INFINITY, l = 0.f, acc[8];
-#pragma unroll
-      for (int k = 0; k < 8; ++k) acc[k] = 0.f;
+    // Online-softmax merge in chunk order (the single-group merge's
+    // arithmetic), one output dimension per thread: the thread of (item i,
+    // dimension k) runs the item's max and weight-sum chain itself.
+    for (int p = tid; p < 8 * mine; p += kThreads) {
+      const int i = p >> 3, k = p & 7;
+      const int it = c + chunks * i;
+      const int h = it / (D / 8), d = (it % (D / 8)) * 8 + k;
+      float m = -INFINITY, l = 0.f, acc = 0.f;
       for (int cc = 0; cc < chunks; ++cc) {
-        const float* pv = pairs[tid * chunks + cc];
+        const float* pv = pairs[i * chunks + cc];
         const float mn = fmaxf(m, pv[8]);
         const float sc = exp2f(m - mn);
         const float w = exp2f(pv[8] - mn);
         l = l * sc + w * pv[9];
-#pragma unroll
-        for (int k = 0; k < 8; ++k) acc[k] = acc[k] * sc + w * pv[k];
+        acc = acc * sc + w * pv[k];
         m = mn;
       }
-      uint32_t o[4];
-#pragma unroll
-      for (int i = 0; i < 4; ++i)
-        o[i] = pack2(static_cast<_Float16>(acc[2 * i] / l), static_cast<_Float16>(acc[2 * i + 1] / l));
-      *reinterpret_cast<uint4*>(a.out + (static_cast<int64_t>(g) * G + h) * D + d0) = make_uint4(o[0], o[1], o[2], o[3]);
+      a.out[(static_cast<int64_t>(g) * G + h) * D + d] = __builtin_bit_cast(unsigned short, static_cast<_Float16>(acc / l));
     }
     (void)per;
     return;
