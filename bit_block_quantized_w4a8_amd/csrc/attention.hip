@@ -35,10 +35,13 @@
 //   5'. Up to kMaxLlChunks chunks (context 2048 at most), when the partials fit
 //      the library's attention exchange area: every chunk writes its partials
 //      as 64-bit words of 32 bits of data and a flag (agent-scope atomics, no
-//      store to wait for, no ticket), and every workgroup merges a share of
-//      the (head, 8 dimensions) items, one (item, chunk) pair per thread
-//      fetched in one round and combined through LDS in chunk order -- the
-//      arithmetic of the single-group merge above.  Each KV head has its own
+//      store to wait for, no ticket), and every workgroup merges a run of
+//      consecutive outputs (head * D + dimension), one output per thread
+//      (a few for short contexts), in chunk order.  A wave's polls read
+//      consecutive words, so a poll round costs a few cache lines per
+//      instruction.  With many chunks the workgroup's threads split the
+//      chunks into two or four ranges merged side by side and combined in
+//      order through LDS.  Each KV head has its own
 //      fixed region of words and epoch word; the flag is 1 + that epoch,
 //      which workgroup 0 of the head advances once it has read every chunk's
 //      words.  Every wait is bounded and raises the device error word.
@@ -62,6 +65,34 @@ constexpr int kGroupChunks = 16;    // chunks per merge group, at least
 constexpr int kMergeUnroll = 8;     // partials fetched per merge round
 constexpr int kMaxLlChunks = 32;    // chunks the flagged-word merge serves
 constexpr int kLlSpin = 1 << 20;    // polls before a wait gives up
+constexpr int kLlSlots = 16;        // (output, chunk) pairs a thread of the flagged-word merge holds
+
+// The flagged-word merge's split of a KV head's `outputs` (G * D, a multiple
+// of 64) over its chunks' workgroups: the first `workers` workgroups (the
+// largest divisor of outputs / 64 not above the chunk count) merge `per`
+// consecutive outputs each, `per` a multiple of 64.  A workgroup's threads
+// form `split` ranges of `cs` consecutive chunks (4 with per <= 64, 2 with
+// per <= 128), each range's kThreads / split threads covering the
+// workgroup's outputs, `reps` outputs per thread (kThreads / split apart).
+// Whether a thread has its r-th output is uniform over its wave.  A thread
+// holds at most reps * cs words.
+struct LlPlan {
+  int workers, per, split, reps, cs;
+  int tlog;  // log2(kThreads / split)
+};
+LlPlan ll_plan(int outputs, int chunks) {
+  LlPlan p;
+  const int blocks = outputs / 64;
+  p.workers = 1;
+  for (int d = 1; d <= std::min(blocks, chunks); ++d)
+    if (blocks % d == 0) p.workers = d;
+  p.per = outputs / p.workers;
+  p.split = p.per <= 64 ? 4 : p.per <= 128 ? 2 : 1;
+  p.tlog = p.split == 4 ? 6 : p.split == 2 ? 7 : 8;
+  p.reps = (p.per + (1 << p.tlog) - 1) >> p.tlog;
+  p.cs = (chunks + p.split - 1) / p.split;
+  return p;
+}
 
 typedef _Float16 h4 __attribute__((ext_vector_type(4)));
 typedef float f4 __attribute__((ext_vector_type(4)));
@@ -87,6 +118,7 @@ struct AttnArgs {
                          // and weight sum)
   uint32_t* epochs;      // [Hkv]
   uint32_t* error;       // device error word
+  LlPlan llp;            // the flagged-word merge's split (ll_plan)
 };
 
 __device__ __forceinline__ void ll_put(uint64_t* p, float v, uint32_t flag) {
@@ -205,8 +237,8 @@ __global__ __launch_bounds__(kThreads) void decode_attention_kernel(AttnArgs a) 
   __shared__ int last;
   __shared__ uint32_t flag_s;
   __shared__ __align__(16) uint16_t new_k[D], new_v[D];  // the newest token's key and value, fp16
-  // Flagged-word merge: one (item, chunk) pair per entry, 8 output dims, max, weight sum.
-  __shared__ float pairs[LL ? kThreads + kMaxLlChunks : 1][10];
+  // Flagged-word merge: (max, weight sum, output) of each chunk range's merge.
+  __shared__ float comb[LL ? 3 * kThreads : 1];
 
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const int col = lane & 15, lg = lane >> 4;
@@ -294,22 +326,9 @@ __global__ __launch_bounds__(kThreads) void decode_attention_kernel(AttnArgs a) 
     }
   };
   __syncthreads();
-  if (holds_newest) {
-    if (tk == newest) {
+  if (holds_newest && tk == newest) {
 #pragma unroll
-      for (int i = 0; i < kSeg / 8; ++i) kr[i] = *reinterpret_cast<const uint4*>(new_k + lg * kSeg + 8 * i);
-    }
-    const int first = t0 + 16 * lg;   // position of element 0 of this lane's value runs
-    const int at = newest - first;
-    // Only a run holding the newest position or reaching past it changes
-    // (valid length L - first of at most 16; 16 when the newest is its last).
-    if (L - first <= 16) {
-#pragma unroll
-      for (int nt = 0; nt < kTiles; ++nt) {
-        const int d = wave * (D / 4) + 16 * nt + col;
-        fix_run(vr[nt], L - first, at, (at >= 0 && at < 16) ? new_v[d] : 0u);
-      }
-    }
+    for (int i = 0; i < kSeg / 8; ++i) kr[i] = *reinterpret_cast<const uint4*>(new_k + lg * kSeg + 8 * i);
   }
 
   // 2. Scores of the wave's 16 positions: row r of the result is head r's hi
@@ -366,6 +385,22 @@ __global__ __launch_bounds__(kThreads) void decode_attention_kernel(AttnArgs a) 
   }
   __syncthreads();
 
+  // The value runs change only here, where they are first used, so the
+  // scores never wait for the value loads.  Only a run holding the newest
+  // position or reaching past it changes (valid length L - first of at most
+  // 16; 16 when the newest is its last).
+  if (holds_newest) {
+    const int first = t0 + 16 * lg;  // position of element 0 of this lane's value runs
+    const int at = newest - first;
+    if (L - first <= 16) {
+#pragma unroll
+      for (int nt = 0; nt < kTiles; ++nt) {
+        const int d = wave * (D / 4) + 16 * nt + col;
+        fix_run(vr[nt], L - first, at, (at >= 0 && at < 16) ? new_v[d] : 0u);
+      }
+    }
+  }
+
   // 4. Chunk output of the wave's D / 4 dimensions: the contraction index of
   // step `ks` is position 16 * lg + 4 * ks + j, matching the value runs.  Rows
   // 0 .. 7 of the result sit in lanes 0 .. 31 and their lo rows 32 lanes up.
@@ -407,92 +442,122 @@ __global__ __launch_bounds__(kThreads) void decode_attention_kernel(AttnArgs a) 
   if constexpr (LL) {
     // 5'. Flagged-word merge (no barrier before it: a workgroup barrier's
     // fence would wait for this workgroup's word stores to be acknowledged,
-    // and a reader checks every word's flag anyway).  Items (head h, dims 8 j .. 8 j + 7) i = c,
-    // c + chunks, ...; entry e of this workgroup is item c + chunks * (e /
-    // chunks) of chunk e % chunks.
+    // and a reader checks every word's flag anyway).  Thread (range sub,
+    // index st) merges outputs f0, f0 + T, ... over the range's chunks.
     const uint32_t flag = flag_s;
-    const int items = G * (D / 8);
-    const int per = (items + chunks - 1) / chunks;
-    const int mine = c < items ? (items - 1 - c) / chunks + 1 : 0;  // items this workgroup merges
-    const uint64_t* base = a.ll + static_cast<int64_t>(g) * kAttnHeadWords;
-    // Each thread polls the ten words of its entries (at most two: an entry
-    // tid and tid + kThreads), issuing every load of a round before testing
-    // any.  The chunks are few, so their polls are few.
+    const LlPlan pl = a.llp;
+    if (c >= pl.workers) return;  // no outputs here (uniform)
+    const int T = 1 << pl.tlog;   // threads per chunk range
+    const int sub = __builtin_amdgcn_readfirstlane(tid >> pl.tlog);  // uniform per wave (T >= 64)
+    const int st = tid & (T - 1);
+    const int cb = sub * pl.cs;
+    const int nc = max(0, min(chunks - cb, pl.cs));  // the range's chunks
+    // Outputs c * per + st + T * r for r < nr; per and T are multiples of 64,
+    // so nr is the same for the whole wave.
+    const int st0 = __builtin_amdgcn_readfirstlane(st & ~63);
+    const int nr = st0 < pl.per ? min(pl.reps, (pl.per - st0 + T - 1) >> pl.tlog) : 0;
+    const int nslots = nr * nc;  // (output, chunk) pairs, output-major: at most kLlSlots
+    const int f0 = c * pl.per + st;
+    // Word offsets in a chunk's block of G * (D + 2): output f0, and its
+    // head's max (the weight sum follows).  With several outputs per thread
+    // T is a multiple of D, so output f0 + T * r lies r * r_words further.
+    const uint32_t o_off = static_cast<uint32_t>(f0 / D * (D + 2) + f0 % D);
+    const uint32_t s_off = static_cast<uint32_t>(f0 / D * (D + 2) + D);
+    const int r_words = T >= D ? T / D * (D + 2) : 0;
+    const int cstride = G * (D + 2);
+    const uint64_t* hb = a.ll + static_cast<int64_t>(g) * kAttnHeadWords + static_cast<int64_t>(cb) * cstride;
+    // Each pair's output word and its chunk's max and weight-sum words, every
+    // load of a round issued before any is tested: lanes of a wave read
+    // consecutive output words, and the max and sum words of a head.
+    uint64_t w[kLlSlots][3];
     bool ok = true;
-    const int n_entries = mine * chunks;
-    const int e0 = tid, e1 = tid + kThreads;
-    const uint64_t* w0 = base;
-    const uint64_t* w1 = base;
-    int d00 = 0, d01 = 0;
-    if (e0 < n_entries) {
-      const int it = c + chunks * (e0 / chunks);
-      w0 = base + (static_cast<int64_t>(e0 % chunks) * G + it / (D / 8)) * (D + 2);
-      d00 = (it % (D / 8)) * 8;
-    }
-    if (e1 < n_entries) {
-      const int it = c + chunks * (e1 / chunks);
-      w1 = base + (static_cast<int64_t>(e1 % chunks) * G + it / (D / 8)) * (D + 2);
-      d01 = (it % (D / 8)) * 8;
-    }
-    if (e0 < n_entries) {
-      uint64_t v[2][10];
-      for (int spin = 0;; ++spin) {
+    for (int spin = 0;; ++spin) {
+      int r = 0, k = 0;
 #pragma unroll
-        for (int k = 0; k < 8; ++k) v[0][k] = ll_get(w0 + d00 + k);
-        v[0][8] = ll_get(w0 + D);
-        v[0][9] = ll_get(w0 + D + 1);
-        if (e1 < n_entries) {
-#pragma unroll
-          for (int k = 0; k < 8; ++k) v[1][k] = ll_get(w1 + d01 + k);
-          v[1][8] = ll_get(w1 + D);
-          v[1][9] = ll_get(w1 + D + 1);
+      for (int j = 0; j < kLlSlots; ++j) {
+        if (j < nslots) {
+          const uint64_t* blk = hb + k * cstride + r * r_words;
+          w[j][0] = ll_get(blk + o_off);
+          w[j][1] = ll_get(blk + s_off);
+          w[j][2] = ll_get(blk + s_off + 1);
         }
-        bool ready = true;
-#pragma unroll
-        for (int k = 0; k < 10; ++k) ready &= static_cast<uint32_t>(v[0][k] >> 32) == flag;
-        if (e1 < n_entries) {
-#pragma unroll
-          for (int k = 0; k < 10; ++k) ready &= static_cast<uint32_t>(v[1][k] >> 32) == flag;
+        if (++k == nc) {
+          k = 0;
+          ++r;
         }
-        if (ready) break;
-        if (spin >= kLlSpin) {
-          ok = false;
-          break;
-        }
-        __builtin_amdgcn_s_sleep(1);
       }
+      uint32_t stale = 0u;
 #pragma unroll
-      for (int k = 0; k < 10; ++k) pairs[e0][k] = __uint_as_float(static_cast<uint32_t>(v[0][k]));
-      if (e1 < n_entries) {
-#pragma unroll
-        for (int k = 0; k < 10; ++k) pairs[e1][k] = __uint_as_float(static_cast<uint32_t>(v[1][k]));
+      for (int j = 0; j < kLlSlots; ++j) {
+        if (j < nslots)
+          stale |= (static_cast<uint32_t>(w[j][0] >> 32) ^ flag) | (static_cast<uint32_t>(w[j][1] >> 32) ^ flag) |
+                   (static_cast<uint32_t>(w[j][2] >> 32) ^ flag);
       }
+      if (stale == 0u) break;
+      if (spin >= kLlSpin) {
+        ok = false;
+        break;
+      }
+      __builtin_amdgcn_s_sleep(1);
     }
     if (!ok) __hip_atomic_store(a.error, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-    __syncthreads();
-    // Workgroup 0 of the head has now read every chunk's words, so every
-    // workgroup of the head has read the epoch: advance it for the next call.
-    if (c == 0 && tid == 0) __hip_atomic_store(a.epochs + g, flag, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-    // Online-softmax merge in chunk order (the single-group merge's
-    // arithmetic), one output dimension per thread: the thread of (item i,
-    // dimension k) runs the item's max and weight-sum chain itself.
-    for (int p = tid; p < 8 * mine; p += kThreads) {
-      const int i = p >> 3, k = p & 7;
-      const int it = c + chunks * i;
-      const int h = it / (D / 8), d = (it % (D / 8)) * 8 + k;
+    // Online-softmax merge of the range's chunks in chunk order, one output
+    // at a time.
+    {
+      uint16_t* out = a.out + static_cast<int64_t>(g) * G * D;
       float m = -INFINITY, l = 0.f, acc = 0.f;
-      for (int cc = 0; cc < chunks; ++cc) {
-        const float* pv = pairs[i * chunks + cc];
-        const float mn = fmaxf(m, pv[8]);
-        const float sc = exp2f(m - mn);
-        const float w = exp2f(pv[8] - mn);
-        l = l * sc + w * pv[9];
-        acc = acc * sc + w * pv[k];
-        m = mn;
+      int r = 0, k = 0;
+#pragma unroll
+      for (int j = 0; j < kLlSlots; ++j) {
+        if (j < nslots) {
+          const float pm = __uint_as_float(static_cast<uint32_t>(w[j][1]));
+          const float mn = fmaxf(m, pm);  // every chunk's max is finite
+          const float sc = exp2f(m - mn);  // 0 on the first chunk (m = -inf)
+          const float wt = exp2f(pm - mn);
+          l = l * sc + wt * __uint_as_float(static_cast<uint32_t>(w[j][2]));
+          acc = acc * sc + wt * __uint_as_float(static_cast<uint32_t>(w[j][0]));
+          m = mn;
+          if (k == nc - 1) {
+            if (pl.split == 1) {
+              out[f0 + T * r] = __builtin_bit_cast(unsigned short, static_cast<_Float16>(acc / l));
+            } else {  // one output per thread (reps = 1)
+              comb[tid] = m;
+              comb[kThreads + tid] = l;
+              comb[2 * kThreads + tid] = acc;
+            }
+            m = -INFINITY;
+            l = 0.f;
+            acc = 0.f;
+          }
+        }
+        if (++k == nc) {
+          k = 0;
+          ++r;
+        }
       }
-      a.out[(static_cast<int64_t>(g) * G + h) * D + d] = __builtin_bit_cast(unsigned short, static_cast<_Float16>(acc / l));
     }
-    (void)per;
+    if (pl.split > 1) {
+      // Combine the ranges' results in range (chunk) order.
+      __syncthreads();
+      if (sub == 0 && nr > 0) {
+        float m = comb[st], l = comb[kThreads + st], acc = comb[2 * kThreads + st];
+        for (int s2 = 1; s2 < pl.split && s2 * pl.cs < chunks; ++s2) {
+          const int t = s2 * T + st;
+          const float mn = fmaxf(m, comb[t]);
+          const float sc = exp2f(m - mn);
+          const float wt = exp2f(comb[t] - mn);
+          l = l * sc + wt * comb[kThreads + t];
+          acc = acc * sc + wt * comb[2 * kThreads + t];
+          m = mn;
+        }
+        a.out[static_cast<int64_t>(g) * G * D + f0] = __builtin_bit_cast(unsigned short, static_cast<_Float16>(acc / l));
+      }
+    }
+    // Workgroup 0 of the head has now read every chunk's words (thread 0 alone
+    // with one chunk range; every range before the barrier above otherwise),
+    // so every workgroup of the head has read the epoch: advance it for the
+    // next call.
+    if (c == 0 && tid == 0) __hip_atomic_store(a.epochs + g, flag, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
     return;
   }
 
@@ -562,8 +627,10 @@ size_t attention_scratch_bytes(int n_kv_heads, int group, int head_dim, int leng
 bool attention_ll_fits(int n_kv_heads, int group, int head_dim, int length, const AttnExchange* ex) {
   const int chunks = attention_chunks(length);
   static_assert(kAttnHeadWords >= size_t{kMaxLlChunks} * kMaxGroup * (256 + 2), "attention exchange region");
-  return ex && ex->ll && chunks <= kMaxLlChunks && n_kv_heads <= ex->heads && group <= kMaxGroup &&
-         head_dim <= 256;
+  if (!(ex && ex->ll && chunks <= kMaxLlChunks && n_kv_heads <= ex->heads && group <= kMaxGroup && head_dim <= 256))
+    return false;
+  const LlPlan p = ll_plan(group * head_dim, chunks);
+  return p.reps * p.cs <= kLlSlots;
 }
 
 int launch_decode_attention(const float* q, const float* k_new, const float* v_new, uint16_t* k_cache,
@@ -600,6 +667,7 @@ int launch_decode_attention(const float* q, const float* k_new, const float* v_n
   const dim3 grid(chunks, n_kv_heads);
   if (attention_ll_fits(n_kv_heads, group, head_dim, length, ex)) {
     a.ll = ex->ll;
+    a.llp = ll_plan(group * head_dim, chunks);
     a.epochs = ex->epochs;
     a.error = ex->error;
     switch (head_dim) {
