@@ -121,12 +121,33 @@ struct AttnArgs {
   LlPlan llp;            // the flagged-word merge's split (ll_plan)
 };
 
-__device__ __forceinline__ void ll_put(uint64_t* p, float v, uint32_t flag) {
-  __hip_atomic_store(p, (static_cast<uint64_t>(flag) << 32) | __float_as_uint(v), __ATOMIC_RELAXED,
-                     __HIP_MEMORY_SCOPE_AGENT);
+// A KV head's flagged words are reached through a buffer resource: a
+// uniform base and size in scalar registers, a 32-bit byte offset per lane
+// and one per access (a scalar or a constant), so an access costs one
+// instruction and no 64-bit address arithmetic.  Offsets at or past the
+// region's end drop a store (the way lanes with nothing to write skip it).
+// Every access is one aligned 64-bit load or store with the device-coherent
+// cache policy (sc1), what a relaxed agent-scope atomic compiles to here.
+typedef unsigned int u32x2 __attribute__((ext_vector_type(2)));
+constexpr int kCoherent = 16;               // cache policy bits: sc1
+constexpr uint32_t kDropOffset = 0x80000000u;  // past every region's end
+__device__ __forceinline__ __amdgpu_buffer_rsrc_t head_words(uint64_t* ll, int g) {
+  // The base is uniform; readfirstlane keeps it (and the resource) in
+  // scalar registers wherever it is used.
+  const uint64_t p = reinterpret_cast<uint64_t>(ll + static_cast<int64_t>(g) * kAttnHeadWords);
+  // (readfirstlane returns int: go through uint32_t, or the low half would be
+  // sign-extended into the high one.)
+  const uint64_t lo = static_cast<uint32_t>(__builtin_amdgcn_readfirstlane(static_cast<uint32_t>(p)));
+  const uint64_t hi = static_cast<uint32_t>(__builtin_amdgcn_readfirstlane(static_cast<uint32_t>(p >> 32)));
+  return __builtin_amdgcn_make_buffer_rsrc(reinterpret_cast<void*>(hi << 32 | lo), 0,
+                                           static_cast<int>(kAttnHeadWords * sizeof(uint64_t)), 0x00020000);
 }
-__device__ __forceinline__ uint64_t ll_get(const uint64_t* p) {
-  return __hip_atomic_load(const_cast<uint64_t*>(p), __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+__device__ __forceinline__ void ll_put(__amdgpu_buffer_rsrc_t r, uint32_t lane_off, uint32_t off, float v,
+                                       uint32_t flag) {
+  __builtin_amdgcn_raw_buffer_store_b64(u32x2{__float_as_uint(v), flag}, r, lane_off, off, kCoherent);
+}
+__device__ __forceinline__ u32x2 ll_get(__amdgpu_buffer_rsrc_t r, uint32_t lane_off, uint32_t off) {
+  return __builtin_amdgcn_raw_buffer_load_b64(r, lane_off, off, kCoherent);
 }
 
 // Max or sum over each 32-lane half of a wave, the result in all its lanes:
@@ -223,8 +244,14 @@ __device__ __forceinline__ void merge_range(const float* st, const float* pp, in
   }
 }
 
-template <int D, bool LL>
+// kLlReps = 0: the ticket merge; 1, 2, 4 or 8: the flagged-word merge with up
+// to that many outputs per thread (the power of two at or above the plan's
+// reps) and up to kLlSlots / kLlReps chunks per range.
+template <int D, int kLlReps>
 __global__ __launch_bounds__(kThreads) void decode_attention_kernel(AttnArgs a) {
+  constexpr bool LL = kLlReps > 0;
+  constexpr int kReps = LL ? kLlReps : 1;
+  constexpr int kRange = kLlSlots / kReps;  // chunk slots per output
   constexpr int kSeg = D / 4;        // dimensions of a lane group's share of one key
   constexpr int kSteps = D / 16;     // score MFMAs per wave
   constexpr int kTiles = D / 64;     // 16-dimension output tiles per wave
@@ -370,9 +397,10 @@ __global__ __launch_bounds__(kThreads) void decode_attention_kernel(AttnArgs a) 
       if ((tid & 31) == 0) {
         if constexpr (LL) {
           // the max and weight sum words follow the head's D output words
-          uint64_t* w = a.ll + static_cast<int64_t>(g) * kAttnHeadWords + (static_cast<int64_t>(c) * G + h) * (D + 2) + D;
-          ll_put(w, m, flag_s);
-          ll_put(w + 1, l, flag_s);
+          const __amdgpu_buffer_rsrc_t rw = head_words(a.ll, g);
+          const uint32_t wo = static_cast<uint32_t>(((c * G + h) * (D + 2) + D) * 8);
+          ll_put(rw, wo, 0, m, flag_s);
+          ll_put(rw, wo, 8, l, flag_s);
         } else {
           float* st = a.stats + ((static_cast<int64_t>(g) * chunks + c) * G + h) * 2;
           store_agent(st, m);
@@ -419,19 +447,31 @@ __global__ __launch_bounds__(kThreads) void decode_attention_kernel(AttnArgs a) 
       for (int ks = 0; ks < 4; ++ks)
         acc[nt] = __builtin_amdgcn_mfma_f32_16x16x16f16(pa[ks], half4_at(vr[nt], ks), acc[nt], 0, 0, 0);
     }
-    const uint32_t flag = LL ? flag_s : 0u;
+    if constexpr (LL) {
+      // Word (head 4 lg + j, dimension wave * D / 4 + 16 nt + col) of this
+      // chunk's block: a lane offset plus a constant per (nt, j); lanes of
+      // the lo rows and of heads past G get an offset that drops the store.
+      const uint32_t flag = flag_s;
+      const __amdgpu_buffer_rsrc_t rw = head_words(a.ll, g);
+      const uint32_t base = static_cast<uint32_t>(((c * G + 4 * lg) * (D + 2) + wave * (D / 4) + col) * 8);
+      uint32_t lo[4];
 #pragma unroll
-    for (int nt = 0; nt < kTiles; ++nt) {
-      const int d = wave * (D / 4) + 16 * nt + col;
+      for (int j = 0; j < 4; ++j) lo[j] = lane < 32 && 4 * lg + j < G ? base : kDropOffset;
 #pragma unroll
-      for (int j = 0; j < 4; ++j) {
-        const float up = upper_half(acc[nt][j]);
-        const int h = 4 * lg + j;
-        if (lane < 32 && h < G) {
-          if constexpr (LL)
-            ll_put(a.ll + static_cast<int64_t>(g) * kAttnHeadWords + (static_cast<int64_t>(c) * G + h) * (D + 2) + d,
-                   acc[nt][j] + up * kInvLo, flag);
-          else
+      for (int nt = 0; nt < kTiles; ++nt) {
+#pragma unroll
+        for (int j = 0; j < 4; ++j)
+          ll_put(rw, lo[j], (j * (D + 2) + 16 * nt) * 8, acc[nt][j] + upper_half(acc[nt][j]) * kInvLo, flag);
+      }
+    } else {
+#pragma unroll
+      for (int nt = 0; nt < kTiles; ++nt) {
+        const int d = wave * (D / 4) + 16 * nt + col;
+#pragma unroll
+        for (int j = 0; j < 4; ++j) {
+          const float up = upper_half(acc[nt][j]);
+          const int h = 4 * lg + j;
+          if (lane < 32 && h < G)
             store_agent(a.part + ((static_cast<int64_t>(g) * chunks + c) * G + h) * D + d, acc[nt][j] + up * kInvLo);
         }
       }
@@ -455,43 +495,45 @@ __global__ __launch_bounds__(kThreads) void decode_attention_kernel(AttnArgs a) 
     // Outputs c * per + st + T * r for r < nr; per and T are multiples of 64,
     // so nr is the same for the whole wave.
     const int st0 = __builtin_amdgcn_readfirstlane(st & ~63);
-    const int nr = st0 < pl.per ? min(pl.reps, (pl.per - st0 + T - 1) >> pl.tlog) : 0;
-    const int nslots = nr * nc;  // (output, chunk) pairs, output-major: at most kLlSlots
+    const int nr = st0 < pl.per ? min(pl.reps, (pl.per - st0 + T - 1) >> pl.tlog) : 0;  // at most kReps
     const int f0 = c * pl.per + st;
     // Word offsets in a chunk's block of G * (D + 2): output f0, and its
     // head's max (the weight sum follows).  With several outputs per thread
     // T is a multiple of D, so output f0 + T * r lies r * r_words further.
-    const uint32_t o_off = static_cast<uint32_t>(f0 / D * (D + 2) + f0 % D);
-    const uint32_t s_off = static_cast<uint32_t>(f0 / D * (D + 2) + D);
-    const int r_words = T >= D ? T / D * (D + 2) : 0;
-    const int cstride = G * (D + 2);
-    const uint64_t* hb = a.ll + static_cast<int64_t>(g) * kAttnHeadWords + static_cast<int64_t>(cb) * cstride;
-    // Each pair's output word and its chunk's max and weight-sum words, every
-    // load of a round issued before any is tested: lanes of a wave read
-    // consecutive output words, and the max and sum words of a head.
-    uint64_t w[kLlSlots][3];
+    const uint32_t o_b = static_cast<uint32_t>((f0 / D * (D + 2) + f0 % D) * 8);
+    const uint32_t s_b = static_cast<uint32_t>((f0 / D * (D + 2) + D) * 8);
+    const int r_bytes = T >= D ? T / D * (D + 2) * 8 : 0;
+    const int c_bytes = G * (D + 2) * 8;
+    const int b0 = cb * c_bytes;
+    const __amdgpu_buffer_rsrc_t rw = head_words(a.ll, g);
+    // Each (output r, chunk k) pair's output word and its chunk's max and
+    // weight-sum words, every load of a round issued before any is tested:
+    // lanes of a wave read consecutive output words, and the max and sum
+    // words of a head.  Slot (r, k) is compile-time; r < nr and k < nc are
+    // uniform, and so is each load's block offset.
+    u32x2 w[kReps][kRange][3];
     bool ok = true;
     for (int spin = 0;; ++spin) {
-      int r = 0, k = 0;
+      asm volatile("" ::: "memory");  // every round loads afresh
 #pragma unroll
-      for (int j = 0; j < kLlSlots; ++j) {
-        if (j < nslots) {
-          const uint64_t* blk = hb + k * cstride + r * r_words;
-          w[j][0] = ll_get(blk + o_off);
-          w[j][1] = ll_get(blk + s_off);
-          w[j][2] = ll_get(blk + s_off + 1);
-        }
-        if (++k == nc) {
-          k = 0;
-          ++r;
+      for (int r = 0; r < kReps; ++r) {
+#pragma unroll
+        for (int k = 0; k < kRange; ++k) {
+          if (r < nr && k < nc) {
+            const uint32_t blk = __builtin_amdgcn_readfirstlane(b0 + k * c_bytes + r * r_bytes);
+            w[r][k][0] = ll_get(rw, o_b, blk);
+            w[r][k][1] = ll_get(rw, s_b, blk);
+            w[r][k][2] = ll_get(rw, s_b, blk + 8);
+          }
         }
       }
       uint32_t stale = 0u;
 #pragma unroll
-      for (int j = 0; j < kLlSlots; ++j) {
-        if (j < nslots)
-          stale |= (static_cast<uint32_t>(w[j][0] >> 32) ^ flag) | (static_cast<uint32_t>(w[j][1] >> 32) ^ flag) |
-                   (static_cast<uint32_t>(w[j][2] >> 32) ^ flag);
+      for (int r = 0; r < kReps; ++r) {
+#pragma unroll
+        for (int k = 0; k < kRange; ++k) {
+          if (r < nr && k < nc) stale |= (w[r][k][0].y ^ flag) | (w[r][k][1].y ^ flag) | (w[r][k][2].y ^ flag);
+        }
       }
       if (stale == 0u) break;
       if (spin >= kLlSpin) {
@@ -503,38 +545,37 @@ __global__ __launch_bounds__(kThreads) void decode_attention_kernel(AttnArgs a) 
     if (!ok) __hip_atomic_store(a.error, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
     // Online-softmax merge of the range's chunks in chunk order, one output
     // at a time.
-    {
-      uint16_t* out = a.out + static_cast<int64_t>(g) * G * D;
-      float m = -INFINITY, l = 0.f, acc = 0.f;
-      int r = 0, k = 0;
+    float m = -INFINITY, l = 0.f, acc = 0.f;
 #pragma unroll
-      for (int j = 0; j < kLlSlots; ++j) {
-        if (j < nslots) {
-          const float pm = __uint_as_float(static_cast<uint32_t>(w[j][1]));
-          const float mn = fmaxf(m, pm);  // every chunk's max is finite
-          const float sc = exp2f(m - mn);  // 0 on the first chunk (m = -inf)
-          const float wt = exp2f(pm - mn);
-          l = l * sc + wt * __uint_as_float(static_cast<uint32_t>(w[j][2]));
-          acc = acc * sc + wt * __uint_as_float(static_cast<uint32_t>(w[j][0]));
-          m = mn;
-          if (k == nc - 1) {
-            if (pl.split == 1) {
-              out[f0 + T * r] = __builtin_bit_cast(unsigned short, static_cast<_Float16>(acc / l));
-            } else {  // one output per thread (reps = 1)
-              comb[tid] = m;
-              comb[kThreads + tid] = l;
-              comb[2 * kThreads + tid] = acc;
-            }
-            m = -INFINITY;
-            l = 0.f;
-            acc = 0.f;
+    for (int r = 0; r < kReps; ++r) {
+      if (r < nr) {
+        m = -INFINITY;
+        l = 0.f;
+        acc = 0.f;
+#pragma unroll
+        for (int k = 0; k < kRange; ++k) {
+          if (k < nc) {
+            const float pm = __uint_as_float(w[r][k][1].x);
+            const float mn = fmaxf(m, pm);  // every chunk's max is finite
+            // 2^x on the hardware's exponential: results below 2^-126 become
+            // 0, a change far below the fp16 output's rounding (the largest
+            // chunk weight is 1).  0 on the first chunk (m = -inf).
+            const float sc = __builtin_amdgcn_exp2f(m - mn);
+            const float wt = __builtin_amdgcn_exp2f(pm - mn);
+            l = l * sc + wt * __uint_as_float(w[r][k][2].x);
+            acc = acc * sc + wt * __uint_as_float(w[r][k][0].x);
+            m = mn;
           }
         }
-        if (++k == nc) {
-          k = 0;
-          ++r;
-        }
+        if (pl.split == 1)
+          a.out[static_cast<int64_t>(g) * G * D + f0 + T * r] =
+              __builtin_bit_cast(unsigned short, static_cast<_Float16>(acc / l));
       }
+    }
+    if (pl.split > 1 && nr > 0) {  // one output per thread (reps = 1)
+      comb[tid] = m;
+      comb[kThreads + tid] = l;
+      comb[2 * kThreads + tid] = acc;
     }
     if (pl.split > 1) {
       // Combine the ranges' results in range (chunk) order.
@@ -630,7 +671,18 @@ bool attention_ll_fits(int n_kv_heads, int group, int head_dim, int length, cons
   if (!(ex && ex->ll && chunks <= kMaxLlChunks && n_kv_heads <= ex->heads && group <= kMaxGroup && head_dim <= 256))
     return false;
   const LlPlan p = ll_plan(group * head_dim, chunks);
-  return p.reps * p.cs <= kLlSlots;
+  const int reps = p.reps <= 1 ? 1 : p.reps <= 2 ? 2 : p.reps <= 4 ? 4 : 8;
+  return p.reps <= 8 && p.cs <= kLlSlots / reps;
+}
+
+template <int D>
+void launch_ll(int reps, dim3 grid, const AttnArgs& a, hipStream_t stream) {
+  switch (reps) {
+    case 1: hipLaunchKernelGGL((decode_attention_kernel<D, 1>), grid, dim3(kThreads), 0, stream, a); break;
+    case 2: hipLaunchKernelGGL((decode_attention_kernel<D, 2>), grid, dim3(kThreads), 0, stream, a); break;
+    case 4: hipLaunchKernelGGL((decode_attention_kernel<D, 4>), grid, dim3(kThreads), 0, stream, a); break;
+    default: hipLaunchKernelGGL((decode_attention_kernel<D, 8>), grid, dim3(kThreads), 0, stream, a); break;
+  }
 }
 
 int launch_decode_attention(const float* q, const float* k_new, const float* v_new, uint16_t* k_cache,
@@ -668,19 +720,20 @@ int launch_decode_attention(const float* q, const float* k_new, const float* v_n
   if (attention_ll_fits(n_kv_heads, group, head_dim, length, ex)) {
     a.ll = ex->ll;
     a.llp = ll_plan(group * head_dim, chunks);
+    const int reps = a.llp.reps <= 1 ? 1 : a.llp.reps <= 2 ? 2 : a.llp.reps <= 4 ? 4 : 8;
     a.epochs = ex->epochs;
     a.error = ex->error;
     switch (head_dim) {
-      case 64: hipLaunchKernelGGL((decode_attention_kernel<64, true>), grid, dim3(kThreads), 0, stream, a); break;
-      case 128: hipLaunchKernelGGL((decode_attention_kernel<128, true>), grid, dim3(kThreads), 0, stream, a); break;
-      case 256: hipLaunchKernelGGL((decode_attention_kernel<256, true>), grid, dim3(kThreads), 0, stream, a); break;
+      case 64: launch_ll<64>(reps, grid, a, stream); break;
+      case 128: launch_ll<128>(reps, grid, a, stream); break;
+      case 256: launch_ll<256>(reps, grid, a, stream); break;
       default: return hip_fail(hipErrorInvalidValue, "decode attention: head_dim must be 64, 128 or 256");
     }
   } else {
     switch (head_dim) {
-      case 64: hipLaunchKernelGGL((decode_attention_kernel<64, false>), grid, dim3(kThreads), 0, stream, a); break;
-      case 128: hipLaunchKernelGGL((decode_attention_kernel<128, false>), grid, dim3(kThreads), 0, stream, a); break;
-      case 256: hipLaunchKernelGGL((decode_attention_kernel<256, false>), grid, dim3(kThreads), 0, stream, a); break;
+      case 64: hipLaunchKernelGGL((decode_attention_kernel<64, 0>), grid, dim3(kThreads), 0, stream, a); break;
+      case 128: hipLaunchKernelGGL((decode_attention_kernel<128, 0>), grid, dim3(kThreads), 0, stream, a); break;
+      case 256: hipLaunchKernelGGL((decode_attention_kernel<256, 0>), grid, dim3(kThreads), 0, stream, a); break;
       default: return hip_fail(hipErrorInvalidValue, "decode attention: head_dim must be 64, 128 or 256");
     }
   }
