@@ -487,6 +487,11 @@ __global__ __launch_bounds__(kThreads) void decode_attention_kernel(AttnArgs a) 
     const uint32_t flag = flag_s;
     const LlPlan pl = a.llp;
     if (c >= pl.workers) return;  // no outputs here (uniform)
+    // This workgroup's own word stores acknowledged first: a poll issued
+    // behind them would wait for them anyway, and one issued a little later
+    // finds the other chunks' words in one round more often (measured with
+    // per-phase timestamps: 0.5 us less per call at 640 positions).
+    __builtin_amdgcn_s_waitcnt(0);
     const int T = 1 << pl.tlog;   // threads per chunk range
     const int sub = __builtin_amdgcn_readfirstlane(tid >> pl.tlog);  // uniform per wave (T >= 64)
     const int st = tid & (T - 1);
