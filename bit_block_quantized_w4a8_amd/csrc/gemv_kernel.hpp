@@ -353,13 +353,9 @@ __global__ __launch_bounds__(T) void gemv_kernel(GemvArgs a, uint32_t* __restric
     // wave reads its own codes back without a workgroup barrier.
     if constexpr (kWaveQuant) __builtin_amdgcn_wave_barrier();
     else __syncthreads();
-#pragma unroll
-    for (int r = RH; r < R; ++r) load_weights(r);
-    __builtin_amdgcn_sched_barrier(0);
-
-    // 3. Integer block dots and the fp32 epilogue.
-#pragma unroll
-    for (int r = 0; r < R; ++r) {
+    // 3. Integer block dots and the fp32 epilogue, block slot r at a time
+    // (the accumulation order is r = 0, 1, ..).
+    auto dot_block = [&](int r) __attribute__((always_inline)) {
       const int bl = slot + r * S;
       if (bl < nbc) {
         const uint32_t l0 = low_nibbles_x16(w[r].x), l1 = low_nibbles_x16(w[r].y);
@@ -393,6 +389,26 @@ __global__ __launch_bounds__(T) void gemv_kernel(GemvArgs a, uint32_t* __restric
           }
         }
       }
+    };
+    if constexpr (RH < R) {
+      // Each second-half load is followed by the dot products of a
+      // first-half block, whose data has long arrived: a wave held at a load
+      // (the CU accepts loads only as fast as the memory system drains them)
+      // does the first half's arithmetic between its issues instead of after
+      // its last one, and only the second half is left once the last data
+      // arrives.
+#pragma unroll
+      for (int r = RH; r < R; ++r) {
+        load_weights(r);
+        __builtin_amdgcn_sched_barrier(0);
+        dot_block(r - RH);
+        __builtin_amdgcn_sched_barrier(0);
+      }
+#pragma unroll
+      for (int r = R - RH; r < R; ++r) dot_block(r);
+    } else {
+#pragma unroll
+      for (int r = 0; r < R; ++r) dot_block(r);
     }
     // The next chunk overwrites the LDS codes (with per-wave quantisation each
     // wave rewrites only the blocks it reads itself).
