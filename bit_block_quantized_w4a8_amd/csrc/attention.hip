@@ -273,18 +273,32 @@ __global__ __launch_bounds__(kThreads) void decode_attention_kernel(AttnArgs a) 
   const int G = a.group, L = a.length, cap = a.capacity;
   const int t0 = c * kChunk;
   const int newest = L - 1;
-  if (LL && tid == 0) flag_s = __hip_atomic_load(a.epochs + g, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) + 1u;
+  // The loads below are unconditional (addresses clamped in range, unused
+  // values dropped later) and all issued before any is waited for: a load
+  // inside a branch gets its use (and the wait for it) pulled into the
+  // branch, which would hold the wave's later loads back.
+  const uint32_t epoch = LL ? __hip_atomic_load(a.epochs + g, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) : 0u;
 
-  // The newest token's key and value (fp32) first: a wave's loads complete in
-  // order, and the chunk that holds position L - 1 needs them before its
-  // scores, so behind the chunk's cache loads they would hold that chunk, and
-  // every merge waiting for it, back.
-  const bool holds_newest = newest >= t0 && newest < t0 + kChunk;  // uniform per workgroup
-  float4 kx = {0.f, 0.f, 0.f, 0.f}, vx = {0.f, 0.f, 0.f, 0.f};
-  if (holds_newest && tid < D / 4) {
-    kx = reinterpret_cast<const float4*>(a.k_new + static_cast<int64_t>(g) * D)[tid];
-    vx = reinterpret_cast<const float4*>(a.v_new + static_cast<int64_t>(g) * D)[tid];
+  // The group's queries (item tid: head h, dimensions d0 .. d0 + 7) first,
+  // then the newest token's key and value (fp32): a wave's loads complete in
+  // order, so the queries' conversion runs while the cache tiles are in
+  // flight, and the chunk that holds position L - 1 has its new key and value
+  // before its scores (behind the cache loads they would hold that chunk,
+  // and every merge waiting for it, back).
+  static_assert(kMaxGroup * (D / 8) <= kThreads, "one query item per thread");
+  const int qh = tid / (D / 8), qd0 = (tid % (D / 8)) * 8;
+  const bool q_item = tid < kMaxGroup * (D / 8);
+  float4 qx0, qx1;
+  {
+    const float4* src =
+        reinterpret_cast<const float4*>(a.q + (static_cast<int64_t>(g) * G + min(qh, G - 1)) * D + (q_item ? qd0 : 0));
+    qx0 = src[0];
+    qx1 = src[1];
   }
+  const bool holds_newest = newest >= t0 && newest < t0 + kChunk;  // uniform per workgroup
+  const float4 kx = reinterpret_cast<const float4*>(a.k_new + static_cast<int64_t>(g) * D)[tid % (D / 4)];
+  const float4 vx = reinterpret_cast<const float4*>(a.v_new + static_cast<int64_t>(g) * D)[tid % (D / 4)];
+  __builtin_amdgcn_sched_barrier(0);  // these ahead of the cache tiles
 
   // 1. Loads.  Key: this lane's position (column `col` of the wave's 16) and
   // its lane group's quarter of the dimensions.  Value: sixteen positions of
@@ -304,16 +318,15 @@ __global__ __launch_bounds__(kThreads) void decode_attention_kernel(AttnArgs a) 
     vr[nt][0] = vrow[0];
     vr[nt][1] = vrow[1];
   }
+  // Every load is issued before any of them is waited for.
+  __builtin_amdgcn_sched_barrier(0);
+  if (LL && tid == 0) flag_s = epoch + 1u;
   // Queries of the group -> hi / lo rows of the A operand.
-  for (int it = tid; it < kMaxGroup * (D / 8); it += kThreads) {
-    const int h = it / (D / 8), d0 = (it % (D / 8)) * 8;
-    float v[8] = {0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f};
-    if (h < G) {
-      const float4* src = reinterpret_cast<const float4*>(a.q + (static_cast<int64_t>(g) * G + h) * D + d0);
-      const float4 x0 = src[0], x1 = src[1];
-      v[0] = x0.x; v[1] = x0.y; v[2] = x0.z; v[3] = x0.w;
-      v[4] = x1.x; v[5] = x1.y; v[6] = x1.z; v[7] = x1.w;
-    }
+  if (q_item) {
+    const int h = qh, d0 = qd0;
+    const bool live = h < G;  // heads past the group get zero rows
+    const float v[8] = {live ? qx0.x : 0.f, live ? qx0.y : 0.f, live ? qx0.z : 0.f, live ? qx0.w : 0.f,
+                        live ? qx1.x : 0.f, live ? qx1.y : 0.f, live ? qx1.z : 0.f, live ? qx1.w : 0.f};
     uint32_t hi[4], lo[4];
 #pragma unroll
     for (int i = 0; i < 4; ++i) {
