@@ -81,6 +81,8 @@ CASES = [
     (8, 1, 256, 64, 64),
     (8, 1, 256, 1, 64),
     (8, 1, 256, 65, 128),
+    (8, 1, 256, 300, 320),        # flagged-word merge with two outputs per thread (5 chunks, 4 merging)
+    (8, 1, 256, 1024, 1024),      # flagged-word merge over two chunk ranges per output (16 chunks)
     (4, 2, 128, 300, 320),
     (6, 3, 64, 100, 128),
     (3, 3, 64, 77, 128),
