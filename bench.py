@@ -474,7 +474,7 @@ def bench_e2e(w4, torch, synth, timer, decode_steps):
             w4.set_option(w4.OPTION_RESIDENT_LAYER, 1)
         by_layer[name] = {"decode_tok_s_graph": round(decode_steps / secs, 1), "ids_match": ids == ids_graph}
         del g
-    # Decode with attention between qkv and o (w4a8_decoder_layer_attention: five launches per
+    # Decode with attention between qkv and o (w4a8_decoder_layer_attention: three launches per
     # layer) over each layer's fp16 KV cache of capacity 640.  The 512 prompt positions of every
     # cache hold seeded synthetic keys and values (the prefill runs no attention), and each token
     # appends its own.  The attention length grows every token, so the launches are issued from
@@ -512,7 +512,7 @@ def bench_e2e(w4, torch, synth, timer, decode_steps):
         "decode_ms_per_token": round(attn_s / attn_steps * 1e3, 4),
         "steps": attn_steps, "context": [prompt + 1, prompt + attn_steps],
         "kernels_per_layer": "qkv GEMV (norm prologue), decode attention (8 x 256 query heads, one KV head), "
-                             "o, gate/up, down GEMVs",
+                             "o + gate/up + down in one launch of resident workgroups",
         "first_ids": attn_ids[:8],
         "note": "prompt positions of the KV caches are seeded synthetic values; host-issued launches",
     }

@@ -873,6 +873,28 @@ int w4a8_decoder_layer_attention(float* x, int64_t H, const w4a8_weights* qkv, c
                                     static_cast<int>(length), static_cast<int>(capacity), a, sc, &st->attn,
                                     stream)) != W4A8_OK)
     return rc;
+  if (layer_kernel(st, 1, H, qkv->N, gate_up->N) == W4A8_LAYER_RESIDENT) {
+    // o, gate/up and down in one launch of resident workgroups, from the
+    // attention output on (the same values as the three GEMV launches below,
+    // bit for bit).
+    resident::StackArgs ra{};
+    ra.x = x;
+    ra.n_qkv = static_cast<int>(qkv->N);
+    ra.n_layers = 1;
+    ra.alpha = residual_scale;
+    ra.eps = eps;
+    ra.q = q;
+    ra.a = a;
+    ra.o = ob;
+    ra.g = g;
+    ra.u = u;
+    ra.d = d;
+    ra.exchange = st->exchange;
+    ra.o_in = a;
+    ra.w[0] = {qkv->packed_w, qkv->w_scales, o->packed_w, o->w_scales,
+               gate_up->packed_w, gate_up->w_scales, down->packed_w, down->w_scales};
+    return resident::launch_stack(ra, stream);
+  }
   GemvArgs oa{a, o->packed_w, o->w_scales, 1, Hi, Hi, ob, nullptr, nullptr, nullptr};
   oa.resid = x;
   oa.alpha = residual_scale;

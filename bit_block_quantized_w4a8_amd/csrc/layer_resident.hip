@@ -203,6 +203,7 @@ __device__ __forceinline__ void loader_role(const StackArgs& a, Lds& s, int lt, 
   };
   bool ok = true;
   uint32_t flag = 0;
+  const bool tail = a.o_in != nullptr;  // one layer from o on: no qkv input to form
   for (int l = 0; l < a.n_layers; ++l) {
     if (l > 0) {  // this layer's input: the previous layer's output stream
       uint32_t d[8];
@@ -210,20 +211,25 @@ __device__ __forceinline__ void loader_role(const StackArgs& a, Lds& s, int lt, 
 #pragma unroll
       for (int k = 0; k < 8; ++k) xv[k] = __uint_as_float(d[k]);
     }
-    partial_squares();
+    if (!tail) partial_squares();
     if (lt == tile) {
 #pragma unroll
       for (int k = 0; k < 8; ++k) s.x_res[k] = xv[k];
     }
     __syncthreads();  // 1
     flag = s.flag + static_cast<uint32_t>(l);
-    normalise_into(s.q_a, s.s_a);
+    if (!tail) normalise_into(s.q_a, s.s_a);
     __syncthreads();  // 2
     __syncthreads();  // 3: qkv partial sums
-    // o input: the query slice from every qkv tile.
+    // o input: the query slice from every qkv tile, or the given fp16 row.
     {
       uint32_t d[4];
-      ok &= ll_wait<4>(ll_a + 4 * lt, flag, ok ? kSpinLimit : 1, d);
+      if (tail) {
+        const uint4 t4 = *reinterpret_cast<const uint4*>(a.o_in + 8 * lt);
+        d[0] = t4.x, d[1] = t4.y, d[2] = t4.z, d[3] = t4.w;
+      } else {
+        ok &= ll_wait<4>(ll_a + 4 * lt, flag, ok ? kSpinLimit : 1, d);
+      }
       float v[8];
 #pragma unroll
       for (int k = 0; k < 4; ++k) {
@@ -485,9 +491,12 @@ __global__ __launch_bounds__(kThreads) void decode_stack_kernel(StackArgs a) {
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int w = blockIdx.x;
   const int tile = tile_of(w, kG);  // tile of o, gate/up and down (256 tiles each)
+  // A launch that starts at o (a.o_in) holds no qkv tiles.
+  const bool tail = a.o_in != nullptr;
   if (wave >= 8) loader_role(a, s, tid - kComputeThreads, lane, wave - 8, tile);
+  else if (wave < 4 && tail) compute_role<true, false>(a, s, tid, lane, wave, w, tile);
   else if (wave < 4) compute_role<true, true>(a, s, tid, lane, wave, w, tile);
-  else if (kG + w < a.n_qkv / 8) compute_role<false, true>(a, s, tid, lane, wave, w, tile);
+  else if (!tail && kG + w < a.n_qkv / 8) compute_role<false, true>(a, s, tid, lane, wave, w, tile);
   else compute_role<false, false>(a, s, tid, lane, wave, w, tile);
 }
 
@@ -508,6 +517,7 @@ int co_resident_blocks(int* blocks) {
 
 int launch_stack(const StackArgs& a, hipStream_t stream) {
   if (a.n_layers < 1 || a.n_layers > kMaxStack) return hip_fail(hipErrorInvalidValue, "resident stack: layer count");
+  if (a.o_in && a.n_layers != 1) return hip_fail(hipErrorInvalidValue, "resident stack: a launch from o runs one layer");
   hipLaunchKernelGGL(decode_stack_kernel, dim3(kG), dim3(kThreads), 0, stream, a);
   W4A8_HIP(hipGetLastError());
   return W4A8_OK;

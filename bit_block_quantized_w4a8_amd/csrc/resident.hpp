@@ -58,6 +58,10 @@ struct StackArgs {
   uint16_t* u;
   float* d;
   uint32_t* exchange;  // kExchangeBytes
+  // Null: the layers start at qkv.  Otherwise one layer that starts at o, whose
+  // fp16 [kH] input this is (the attention output between qkv and o); the
+  // launch then runs no qkv phase and writes neither q nor a.
+  const uint16_t* o_in;
   LayerWeights w[kMaxStack];
 };
 

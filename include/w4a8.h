@@ -311,9 +311,11 @@ W4A8_API int w4a8_decoder_stack(float* x, int64_t M, int64_t H, const w4a8_weigh
  *   x += s * L(a; o); then the feed-forward half as in w4a8_decoder_layer.
  * x fp32 [1][H] with H = n_heads * head_dim; caches, limits and errors as for
  * w4a8_decode_attention (the call writes the new key and value at position
- * length - 1).  Five launches: the qkv GEMV with the normalisation in its
- * prologue, decode attention, and the o, gate/up and down GEMVs of the
- * one-token layer.  The workspace (w4a8_decoder_layer_workspace for M = 1)
+ * length - 1).  Three launches: the qkv GEMV with the normalisation in its
+ * prologue, decode attention, and o, gate/up and down in one launch of
+ * resident workgroups where w4a8_layer_kernel gives W4A8_LAYER_RESIDENT for
+ * the shape (otherwise as three one-token GEMVs; the same values either
+ * way).  The workspace (w4a8_decoder_layer_workspace for M = 1)
  * receives q, a (the attention output), o, g, u and d.  The one-token GEMV
  * launches must support the shape (as for W4A8_LAYER_GEMV4).
  */
@@ -335,7 +337,9 @@ W4A8_API int w4a8_layer_kernel(int64_t M, int64_t H, const w4a8_weights* qkv, co
 /*
  * Library options (process-wide):
  *   W4A8_OPTION_RESIDENT_LAYER  1 (default): the one-token layer runs in one
- *                               launch where it can; 0: as four launches.
+ *                               launch where it can (and the attention layer's
+ *                               o, gate/up and down in one); 0: as four
+ *                               launches (three).
  * W4A8_EINVAL for an unknown option or value.  Not for calls in flight.
  */
 #define W4A8_OPTION_RESIDENT_LAYER 1

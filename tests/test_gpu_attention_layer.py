@@ -97,3 +97,44 @@ def test_decode_layer_with_attention_teacher_forced():
         assert np.array_equal(host(x), oracle.residual_add(x_mid, d, SCALE))
         print(f"step {step} (length {length}): every launch checked", flush=True)
     assert w4.take_device_errors() == 0
+
+
+def test_attention_layer_from_o_in_one_launch_equals_three_gemvs():
+    """With the resident layer available, w4a8_decoder_layer_attention runs o, gate/up and down
+    as one launch of resident workgroups that starts from the attention output; it must leave
+    the residual stream and every intermediate bit for bit as the three one-token GEMV
+    launches do, over consecutive decode steps (each step's cache writes feed the next)."""
+    h, hq, hkv, d = 2048, 8, 1, 256
+    n_qkv, f, cap = (hq + 2 * hkv) * d, 8192, 640
+    weights = {p: w4.Weights.pack(dev(synth.int4_values(synth.rng(71, i), n, k)),
+                                  dev(synth.weight_scales(synth.rng(71, 10 + i), n, k)))
+               for i, (p, (k, n)) in enumerate({"qkv": (h, n_qkv), "o": (h, h), "gate_up": (h, 2 * f),
+                                                 "down": (f, h)}.items())}
+    assert w4.layer_kernel(1, h, weights["qkv"], weights["gate_up"]) == w4.LAYER_RESIDENT
+    g = np.random.default_rng(72)
+    x0 = g.standard_normal((1, h)).astype(np.float32)
+    kp = g.standard_normal((hkv, cap, d)).astype(np.float16)
+    vp = g.standard_normal((hkv, d, cap)).astype(np.float16)
+    results = {}
+    for resident in (1, 0):
+        w4.set_option(w4.OPTION_RESIDENT_LAYER, resident)
+        try:
+            x = dev(x0.copy())
+            kc, vc = dev(kp.copy()), dev(vp.copy())
+            ws = torch.zeros(w4.decoder_layer_workspace(1, h, weights["qkv"], weights["gate_up"]),
+                             dtype=torch.uint8, device=DEV)
+            steps = []
+            for step in range(3):
+                w4.decoder_layer_attention(x, weights["qkv"], weights["o"], weights["gate_up"], weights["down"],
+                                           0.01, 1e-6, kc, vc, hq, 600 + step, ws)
+                steps.append((host(x).copy(), host(ws).copy()))
+            results[resident] = (steps, host(kc), host(vc))
+        finally:
+            w4.set_option(w4.OPTION_RESIDENT_LAYER, 1)
+    (one, k1, v1), (three, k3, v3) = results[1], results[0]
+    for step, ((x1, ws1), (x3, ws3)) in enumerate(zip(one, three)):
+        assert np.array_equal(x1.view(np.uint32), x3.view(np.uint32)), f"step {step}: residual stream"
+        assert np.array_equal(ws1, ws3), f"step {step}: workspace intermediates"
+    assert np.array_equal(k1.view(np.uint16), k3.view(np.uint16)) and np.array_equal(v1.view(np.uint16),
+                                                                                       v3.view(np.uint16))
+    assert w4.take_device_errors() == 0
